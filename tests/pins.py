@@ -1,0 +1,337 @@
+"""Pins for the oracle: each check raises AssertionError when the oracle (as
+currently bound in the ``oracle`` package) violates a property the pages or
+the mathematics fix.  ``test_oracle_pins.py`` runs them; the mutation tests
+plant mistakes in the oracle and assert that some check fails."""
+
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+import oracle
+from oracle import brute
+from helpers import model_np, spec_of, tiny_cfg
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiny(gemm64=True, **kw):
+    cfg = tiny_cfg(**kw)
+    spec = spec_of(cfg, gemm64=gemm64)
+    layers, head = model_np(cfg, gain_std=0.2)
+    return cfg, spec, layers, head
+
+
+def _lists(W):
+    return {k: (v.tolist()) for k, v in W.items()}
+
+
+def check_brute_layer():
+    """P7: dense layer and a sparse refresh against pure-Python loops."""
+    cfg, spec, layers, _ = _tiny()
+    rng = np.random.default_rng(5)
+    L, d = spec.seq_len, spec.d_model
+    W = layers[0]
+    x0 = rng.standard_normal((L, d))
+    out, K, V = oracle.layer_dense(x0, W, spec)
+    Kb, Vb = [None] * L, [None] * L
+    ob = brute.layer_rows(x0.tolist(), Kb, Vb, list(range(L)), _lists(W), spec)
+    for i in range(L):
+        assert np.max(np.abs(out[i] - np.array(ob[i]))) < 1e-12
+        assert np.max(np.abs(K[i] - np.array(Kb[i]))) < 1e-12
+        assert np.max(np.abs(V[i] - np.array(Vb[i]))) < 1e-12
+    # sparse refresh of rows {1, 4} after rows 1, 3, 4 changed
+    x1 = x0.copy()
+    x1[[1, 3, 4]] += 0.3 * rng.standard_normal((3, d))
+    H = out.copy()
+    oracle.sparse_layer(x1, K, V, H, [1, 4], W, spec)
+    ob2 = brute.layer_rows(x1.tolist(), Kb, Vb, [1, 4], _lists(W), spec)
+    for i in range(L):
+        exp = np.array(ob2[i]) if i in (1, 4) else out[i]
+        assert np.max(np.abs(H[i] - exp)) < 1e-12
+        assert np.max(np.abs(K[i] - np.array(Kb[i]))) < 1e-12
+
+
+def check_brute_decisions():
+    """P7: proxy, drift, selection, LM statistics and commit against brute force."""
+    cfg, spec, layers, head = _tiny()
+    rng = np.random.default_rng(6)
+    L, d = spec.seq_len, spec.d_model
+    W = layers[1]
+    x = rng.standard_normal((L, d))
+    xp = x + 0.2 * rng.standard_normal((L, d))
+    C = oracle.proxy(x, W["attn_norm"], W["w_proxy"])
+    P = oracle.proxy(xp, W["attn_norm"], W["w_proxy"])
+    for i in range(L):
+        cb = brute.proxy(x[i].tolist(), W["attn_norm"].tolist(), W["w_proxy"].tolist())
+        assert np.max(np.abs(C[i] - np.array(cb))) < 1e-12
+    s = oracle.drift(C, P)
+    for i in range(L):
+        assert abs(s[i] - brute.drift(C[i].tolist(), P[i].tolist())) < 1e-12
+    # selection with ties (zeros and repeated values)
+    for trial in range(200):
+        L2 = int(rng.integers(1, 40))
+        vals = rng.choice([0.0, 0.25, 0.5, 1e-9], size=L2) * (rng.random(L2) < 0.8)
+        vals = np.where(rng.random(L2) < 0.3, rng.random(L2), vals)
+        forced = rng.random(L2) < 0.2
+        k = int(rng.integers(0, L2 + 2))
+        got = oracle.select(vals, forced, k).tolist()
+        assert got == brute.select(vals.tolist(), forced.tolist(), k), (vals, forced, k)
+    # LM-head statistics
+    st = oracle.lm_stats(x, head["final_norm"], head["lm_head"], spec)
+    for i in range(L):
+        b = brute.lm_stats(x[i].tolist(), head["final_norm"].tolist(), head["lm_head"].tolist(),
+                           spec.rms_eps)
+        assert st["argmax"][i] == b["argmax"]
+        assert abs(st["m"][i] - b["m"]) < 1e-12
+        assert abs(st["conf"][i] - b["conf"]) < 1e-12
+        assert abs(st["entropy"][i] - b["entropy"]) < 1e-12
+    # commit with ties
+    for trial in range(200):
+        n = int(rng.integers(1, 9))
+        rows = np.arange(10, 10 + n)
+        conf = rng.choice([0.1, 0.5, 0.95, 0.9], size=n)
+        am = rng.integers(0, 50, size=n)
+        ent = rng.random(n)
+        committed = np.zeros(40, bool)
+        committed[rows[rng.random(n) < 0.4]] = True
+        a = oracle.commit(rows, conf, am, ent, committed, 0.9)
+        b = brute.commit(rows.tolist(), conf.tolist(), am.tolist(), ent.tolist(),
+                         committed.tolist(), 0.9)
+        assert list(a[0]) == list(b[0]) and list(a[1]) == list(b[1]) and a[2] == b[2]
+
+
+def check_all_rows_equals_dense():
+    """P1: I = all rows reproduces the dense layer from an arbitrary (stale) cache."""
+    cfg, spec, layers, _ = _tiny()
+    rng = np.random.default_rng(7)
+    L, d = spec.seq_len, spec.d_model
+    x = rng.standard_normal((L, d))
+    out, Kd, Vd = oracle.layer_dense(x, layers[0], spec)
+    K = rng.standard_normal(Kd.shape)
+    V = rng.standard_normal(Vd.shape)
+    H = rng.standard_normal(out.shape)
+    oracle.sparse_layer(x, K, V, H, np.arange(L), layers[0], spec)
+    assert np.max(np.abs(H - out)) < 1e-12
+    assert np.max(np.abs(K - Kd)) < 1e-12 and np.max(np.abs(V - Vd)) < 1e-12
+
+
+def check_empty_set_noop():
+    """P2: I = {} leaves K, V and the layer output bitwise unchanged."""
+    cfg, spec, layers, _ = _tiny()
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((spec.seq_len, spec.d_model))
+    out, K, V = oracle.layer_dense(x, layers[0], spec)
+    K0, V0, H0 = K.copy(), V.copy(), out.copy()
+    oracle.sparse_layer(x + 1.0, K, V, out, np.array([], np.int64), layers[0], spec)
+    assert np.array_equal(K, K0) and np.array_equal(V, V0) and np.array_equal(out, H0)
+
+
+def check_fixed_point():
+    """P3: a cache built from the current inputs is a fixed point: refreshing
+    any rows reproduces the cached outputs, and every drift is exactly 0."""
+    cfg, spec, layers, _ = _tiny()
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((spec.seq_len, spec.d_model))
+    W = layers[0]
+    out, K, V = oracle.layer_dense(x, W, spec)
+    P = oracle.proxy(x, W["attn_norm"], W["w_proxy"])
+    H = out.copy()
+    I, s, _ = oracle.decode.layer_refresh(x, K, V, H, P, W, spec, 3, None)
+    assert np.all(s == 0.0)
+    assert I.tolist() == [0, 1, 2]
+    assert np.max(np.abs(H - out)) < 1e-12
+
+
+def check_drift_closed_forms():
+    """P4: s(x, x) = 0 exactly; s(x, a x) = 0 for a > 0; s(x, -x) = 2;
+    orthogonal -> 1; zero-vector conventions."""
+    rng = np.random.default_rng(10)
+    c = rng.standard_normal((64, 17))
+    assert np.all(oracle.drift(c, c) == 0.0)
+    assert np.max(np.abs(oracle.drift(c, 3.7 * c))) < 1e-15
+    assert np.max(np.abs(oracle.drift(c, -c) - 2.0)) < 1e-14
+    e = np.eye(17)
+    assert np.max(np.abs(oracle.drift(e[:5], e[5:10]) - 1.0)) < 1e-15
+    z = np.zeros((1, 17))
+    assert oracle.drift(z, z)[0] == 0.0
+    assert oracle.drift(z, c[:1])[0] == 1.0 and oracle.drift(c[:1], z)[0] == 1.0
+    # small rotation by angle t: 1 - cos t
+    for t in (1e-6, 1e-3, 0.3, 2.0):
+        a = np.zeros((1, 17)); b = np.zeros((1, 17))
+        a[0, 0] = 1.0
+        b[0, 0], b[0, 1] = math.cos(t), math.sin(t)
+        want = 2.0 * math.sin(t / 2) ** 2
+        assert abs(oracle.drift(a, 5.0 * b)[0] - want) <= 1e-15 * max(1.0, want) + 1e-14 * want
+
+
+def _golden_entropy():
+    out = {}
+    with open(os.path.join(GOLDEN, "entropy_uniform.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                v, h = line.split()
+                out[int(v)] = float(h)
+    return out
+
+
+def check_entropy_closed_forms():
+    """P5: uniform logits give entropy ln V and confidence 1/V; a one-hot
+    logit vector gives entropy 0 and confidence 1; 0 <= H <= ln V."""
+    gold = _golden_entropy()
+    for V, lnv in gold.items():
+        d = 8
+        spec = oracle.Spec(n_layers=1, d_model=d, n_q_heads=1, n_kv_heads=1, head_dim=8,
+                           d_ffn=8, vocab=V, seq_len=2, block_len=2, proxy_rank=2)
+        h = np.random.default_rng(V).standard_normal((2, d)).astype(np.float32)
+        st = oracle.lm_stats(h, np.ones(d, np.float32), np.zeros((d, V), np.float32), spec)
+        assert np.max(np.abs(st["entropy"] - lnv)) < 1e-12 * lnv
+        assert np.max(np.abs(st["conf"] - 1.0 / V)) < 1e-15
+        assert np.all(st["argmax"] == 0)
+    spec = oracle.Spec(n_layers=1, d_model=8, n_q_heads=1, n_kv_heads=1, head_dim=8, d_ffn=8,
+                       vocab=1024, seq_len=1, block_len=1, proxy_rank=2)
+    w = np.zeros((8, 1024), np.float32)
+    w[0, 517] = 1e4
+    h = np.zeros((1, 8), np.float32)
+    h[0, 0] = 1.0
+    st = oracle.lm_stats(h, np.ones(8, np.float32), w, spec)
+    assert st["entropy"][0] == 0.0 and st["conf"][0] == 1.0 and st["argmax"][0] == 517
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((8, 1024)).astype(np.float32)
+    st = oracle.lm_stats(rng.standard_normal((16, 8)), np.ones(8), w, spec)
+    assert np.all(st["entropy"] >= 0.0) and np.all(st["entropy"] <= gold[1024] + 1e-12)
+
+
+def check_proxy_basis():
+    """P6: the SVD factor recovers a planted spectrum; Eckart-Young; W_r^T W_r =
+    Sigma_r^2; at full rank the proxy cosine equals the value-state cosine."""
+    from sparse_kv_cache_value_amd import configs, inputs
+    cfg = configs.C1
+    wv, wr_planted, sigma = inputs.planted_value_projection(cfg, 0)
+    wv = wv.double().numpy()
+    r = cfg.proxy_rank
+    wr, s = oracle.proxy_basis(wv, r)
+    assert np.max(np.abs(s[:r] - sigma.numpy())) < 1e-5 * s[0]
+    # same subspace, same weights: W_r W_r^T is basis-independent
+    g1 = wr @ wr.T
+    g2 = wr_planted.double().numpy() @ wr_planted.double().numpy().T
+    assert np.max(np.abs(g1 - g2)) < 1e-5 * np.max(np.abs(g2))
+    # Eckart-Young and the Gram identity on a plain Gaussian matrix
+    rng = np.random.default_rng(12)
+    w = rng.standard_normal((40, 24))
+    for rr in (1, 5, 24):
+        f, s = oracle.proxy_basis(w, rr)
+        u, _, vt = np.linalg.svd(w, full_matrices=False)
+        approx = f @ vt[:rr]
+        assert abs(np.sum((w - approx) ** 2) - np.sum(s[rr:] ** 2)) < 1e-10 * np.sum(w * w)
+        assert np.max(np.abs(f.T @ f - np.diag(s[:rr] ** 2))) < 1e-10 * s[0] ** 2
+    # full rank: cosine drift on the proxy equals drift of the value states
+    f, _ = oracle.proxy_basis(w, 24)
+    x = rng.standard_normal((30, 40))
+    y = x + 0.1 * rng.standard_normal((30, 40))
+    g = 1.0 + 0.1 * rng.standard_normal(40)
+    s_proxy = oracle.drift(oracle.proxy(x, g, f), oracle.proxy(y, g, f))
+    s_full = oracle.drift((x * g) @ w, (y * g) @ w)
+    assert np.max(np.abs(s_proxy - s_full)) < 1e-13
+
+
+def check_gqa_is_repeated_mha():
+    """P9: grouped-query attention equals multi-head attention with each KV head
+    repeated Hq/Hkv times; Hkv = Hq is plain MHA."""
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((5, 8, 4))
+    K = rng.standard_normal((9, 2, 4))
+    V = rng.standard_normal((9, 2, 4))
+    a = oracle.attention(q, K, V, np.float64)
+    b = oracle.attention(q, np.repeat(K, 4, axis=1), np.repeat(V, 4, axis=1), np.float64)
+    assert np.max(np.abs(a - b)) < 1e-15
+    # explicit softmax-weighted sum for one head
+    h, g = 5, 1
+    sc = q[:, h] @ K[:, g].T / 2.0
+    p = np.exp(sc - sc.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    assert np.max(np.abs(a[:, h] - p @ V[:, g])) < 1e-14
+
+
+def check_permutation_equivariance():
+    """P10: permuting rows together with their positions permutes the outputs."""
+    cfg, spec, layers, _ = _tiny()
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((spec.seq_len, spec.d_model))
+    perm = rng.permutation(spec.seq_len)
+    out, K, V = oracle.layer_dense(x, layers[0], spec)
+    out2, K2, V2 = oracle.layer_dense(x[perm], layers[0], spec, pos=perm)
+    assert np.max(np.abs(out2 - out[perm])) < 1e-12
+    assert np.max(np.abs(K2 - K[perm])) < 1e-12
+
+
+def check_selection_structure():
+    """P11: |I| = min(max(k, |F|), L); F is inside I; I ascending; k = L gives all."""
+    rng = np.random.default_rng(15)
+    for _ in range(300):
+        L = int(rng.integers(1, 60))
+        s = rng.random(L) * (rng.random(L) < 0.5)
+        F = rng.random(L) < 0.15
+        k = int(rng.integers(0, L + 3))
+        I = oracle.select(s, F, k)
+        assert len(I) == min(max(k, int(F.sum())), L)
+        assert set(np.nonzero(F)[0]).issubset(set(I.tolist()))
+        assert np.all(np.diff(I) > 0)
+        # every picked non-forced row outranks every unpicked one
+        picked = [i for i in I if not F[i]]
+        unpicked = [i for i in range(L) if not F[i] and i not in set(I.tolist())]
+        for a in picked:
+            for b in unpicked:
+                assert (s[a], -a) > (s[b], -b)
+        assert oracle.select(s, F, L).tolist() == list(range(L))
+
+
+def check_budget_table():
+    """P13: rho(l) literal table equals the split-Gaussian reading, mean 0.16,
+    and its rounded budgets match the fixture."""
+    from sparse_kv_cache_value_amd import configs
+    tab = oracle.budget.split_gaussian(32)
+    assert np.max(np.abs(np.array(tab) - np.array(configs.RHO_SPLIT_GAUSSIAN_32))) < 1e-15
+    assert abs(sum(tab) / 32 - 0.16) < 1e-12
+    with open(os.path.join(GOLDEN, "rho_k_table_32x1024.txt")) as f:
+        ks = [int(t) for line in f if not line.startswith("#") for t in line.split()]
+    assert [oracle.budget_k(r, 1024) for r in tab] == ks
+    assert max(range(32), key=lambda l: tab[l]) in (15, 16)
+
+
+def check_decode_structure():
+    """P12: under random init (confidence far below 0.9) every step commits
+    exactly one token (the fallback), commits never revert, the history grows
+    in commit order and the block advances once full."""
+    from sparse_kv_cache_value_amd import configs, inputs
+    from helpers import policy_of
+    cfg = configs.C1.with_(seq_len=40, prompt_len=30, block_len=4, n_layers=1,
+                           rho=(0.25,))
+    spec = spec_of(cfg)
+    layers, head = model_np(cfg)
+    tok, com = inputs.prompt_tokens(cfg)
+    st = oracle.decode.SeqState(spec, tok.numpy()[0], com.numpy()[0])
+    pol = policy_of(cfg)
+    assert st.block_start == 28
+    seen = []
+    for t in range(10):
+        before = st.committed.copy()
+        info = oracle.decode.step(st, layers, head, spec, pol)
+        assert info["full"] == (t == 0)
+        assert len(info["pos"]) == 1
+        assert np.all(st.committed[before])
+        assert float(np.max(info["stats"]["conf"])) < 0.9
+        seen += info["pos"]
+        assert st.history == seen
+    assert st.done()
+
+
+ALL_CHECKS = [
+    check_brute_layer, check_brute_decisions, check_all_rows_equals_dense,
+    check_empty_set_noop, check_fixed_point, check_drift_closed_forms,
+    check_entropy_closed_forms, check_proxy_basis, check_gqa_is_repeated_mha,
+    check_permutation_equivariance, check_selection_structure, check_budget_table,
+    check_decode_structure,
+]

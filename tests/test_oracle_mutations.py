@@ -1,0 +1,164 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at least
+one pin catches each of them.  This shows that the pins constrain the oracle
+beyond restating its own formulas."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.model as om
+import pins
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(om, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(checks):
+    failed = []
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            failed.append(c.__name__)
+    return failed
+
+
+def m_rope_sign(monkeypatch):
+    orig = om.rope
+
+    def bad(x, pos, theta, wd=np.float32):
+        return orig(x, -np.asarray(pos), theta, wd)
+    _patch(monkeypatch, "rope", bad)
+
+
+def m_drift_unnormalised(monkeypatch):
+    def bad(C, P):
+        d = np.asarray(C, np.float64) - np.asarray(P, np.float64)
+        return 0.5 * np.sum(d * d, axis=-1)
+    _patch(monkeypatch, "drift", bad)
+
+
+def m_drift_abs_cos(monkeypatch):
+    def bad(C, P):
+        C = np.asarray(C, np.float64); P = np.asarray(P, np.float64)
+        nc = np.linalg.norm(C, axis=-1); npp = np.linalg.norm(P, axis=-1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            c = np.abs(np.sum(C * P, -1)) / (nc * npp)
+        return np.where((nc == 0) & (npp == 0), 0.0, np.where((nc == 0) | (npp == 0), 1.0, 1.0 - c))
+    _patch(monkeypatch, "drift", bad)
+
+
+def m_select_high_index_ties(monkeypatch):
+    def bad(s, forced, k):
+        s = np.asarray(s, np.float64); L = len(s)
+        forced = np.zeros(L, bool) if forced is None else np.asarray(forced, bool)
+        F = [i for i in range(L) if forced[i]]
+        keff = min(max(k, len(F)), L)
+        rest = sorted((i for i in range(L) if not forced[i]), key=lambda i: (-s[i], -i))
+        return np.array(sorted(F + rest[: keff - len(F)]), np.int64)
+    _patch(monkeypatch, "select", bad)
+
+
+def m_scatter_after_attention(monkeypatch):
+    def bad(x, K, V, H_out, idx, W, spec):
+        idx = np.asarray(idx, np.int64)
+        if idx.size == 0:
+            return
+        x = np.asarray(x, spec.wd)
+        xr = x[idx]
+        a = om._act(om.rmsnorm(xr, W["attn_norm"], spec.rms_eps, spec.wd), spec)
+        q, k, v = om._qkv(a, W, idx, spec)
+        H_out[idx] = om._attn_out_ffn(xr, q, K, V, W, spec)
+        K[idx] = k
+        V[idx] = v
+    _patch(monkeypatch, "sparse_layer", bad)
+    monkeypatch.setattr(oracle.decode, "sparse_layer", bad)
+
+
+def m_entropy_sign(monkeypatch):
+    orig = om.lm_stats
+
+    def bad(h, g_f, w_lm, spec):
+        st = orig(h, g_f, w_lm, spec)
+        st["entropy"] = np.log(st["S"]) + st["T"] / st["S"]
+        return st
+    _patch(monkeypatch, "lm_stats", bad)
+
+
+def m_drop_ffn_residual(monkeypatch):
+    def bad(x_rows, q, K, V, W, spec):
+        n = x_rows.shape[0]
+        o = om._act(om.attention(q, K, V, spec.wd).reshape(n, -1), spec)
+        h1 = (np.asarray(x_rows, spec.wd) + om._mm(o, W["w_o"], spec)).astype(spec.wd)
+        nrm = om._act(om.rmsnorm(h1, W["ffn_norm"], spec.rms_eps, spec.wd), spec)
+        act = om._silu(om._mm(nrm, W["w_gate"], spec)) * om._mm(nrm, W["w_up"], spec)
+        return om._act(om._mm(act.astype(spec.wd), W["w_down"], spec), spec)
+    _patch(monkeypatch, "_attn_out_ffn", bad)
+
+
+def m_gqa_modulo(monkeypatch):
+    def bad(q, K, V, wd=np.float32):
+        q = np.asarray(q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
+        n, hq, dh = q.shape
+        hkv = K.shape[1]
+        out = np.empty((n, hq, dh))
+        for h in range(hq):
+            g = h % hkv
+            s = q[:, h] @ K[:, g].T / math.sqrt(dh)
+            p = np.exp(s - s.max(1, keepdims=True)); p /= p.sum(1, keepdims=True)
+            out[:, h] = p @ V[:, g]
+        return out.astype(wd)
+    _patch(monkeypatch, "attention", bad)
+
+
+def m_proxy_drops_gain(monkeypatch):
+    def bad(x, g1, w_r):
+        return np.asarray(x, np.float64) @ np.asarray(w_r, np.float64)
+    _patch(monkeypatch, "proxy", bad)
+    monkeypatch.setattr(oracle.decode, "proxy", bad)
+
+
+def m_commit_last_on_ties(monkeypatch):
+    def bad(rows, conf, argmax, entropy, committed, threshold):
+        cand = [j for j in range(len(rows)) if not committed[rows[j]]]
+        pick = [j for j in cand if conf[j] >= threshold]
+        if not pick and cand:
+            pick = [sorted(cand, key=lambda j: (-conf[j], -rows[j]))[0]]
+        pick.sort(key=lambda j: rows[j])
+        return ([int(rows[j]) for j in pick], [int(argmax[j]) for j in pick],
+                max((float(entropy[j]) for j in pick), default=0.0))
+    _patch(monkeypatch, "commit", bad)
+
+
+def m_budget_truncates(monkeypatch):
+    _patch(monkeypatch, "budget_k", lambda rho, L: int(math.floor(rho * L)))
+
+
+def m_key_uses_query_weights(monkeypatch):
+    def bad(a, W, pos, spec):
+        n = a.shape[0]
+        H, G, dh = spec.n_q_heads, spec.n_kv_heads, spec.head_dim
+        q = om._mm(a, W["w_q"], spec).reshape(n, H, dh)
+        k = om._mm(a, W["w_q"], spec)[:, : G * dh].reshape(n, G, dh)
+        v = om._mm(a, W["w_v"], spec).reshape(n, G, dh)
+        q = om._act(om.rope(q, pos, spec.rope_theta, spec.wd), spec)
+        k = om._act(om.rope(k, pos, spec.rope_theta, spec.wd), spec)
+        return q, k, om._act(v, spec)
+    _patch(monkeypatch, "_qkv", bad)
+
+
+MUTATIONS = [m_rope_sign, m_drift_unnormalised, m_drift_abs_cos, m_select_high_index_ties,
+             m_scatter_after_attention, m_entropy_sign, m_drop_ffn_residual, m_gqa_modulo,
+             m_proxy_drops_gain, m_commit_last_on_ties, m_budget_truncates,
+             m_key_uses_query_weights]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
+def test_mutation_is_caught(monkeypatch, mutation):
+    mutation(monkeypatch)
+    assert _fails(pins.ALL_CHECKS), f"no pin catches {mutation.__name__}"
