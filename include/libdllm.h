@@ -1,0 +1,224 @@
+/*
+ * libdllm -- one denoising step of a bidirectional diffusion LLM under
+ * approximate KV caching, on one MI355X (gfx950).
+ *
+ * The step has four parts, each an entry point below:
+ *   1. a cheap per-token drift score      (dllm_drift_score, dllm_commit's entropy gate)
+ *   2. a per-layer budgeted selection      (dllm_select)
+ *   3. a sparse forward on the selection   (dllm_sparse_layer)
+ *   4. LM-head statistics and the commit   (dllm_lm_head, dllm_commit)
+ * and dllm_step runs all of them for every layer.
+ *
+ * Sources (four summary pages):
+ *   SPA-Cache -- "Singular proxy for adaptive caching in diffusion language
+ *     models": step 1 (value proxy from the truncated SVD of W_V, cosine
+ *     against the cached proxy, lowest similarity refreshed), step 2 (per-layer
+ *     update ratio rho(l), piecewise Gaussian), step 3 (sparse execution on I).
+ *   EntropyCache summary, section 2: the maximum entropy of the tokens decoded
+ *     in a step decides whether the next step runs a full pass; otherwise the
+ *     current mask block and the k most recently decoded tokens are recomputed.
+ *   Polestar, section 1 / TSPD-CE, problem statement: parallel decoding commits
+ *     every masked token whose confidence clears a static threshold.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE memory unless the name ends in _h (host memory).
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the null stream).  Only dllm_step with a non-NULL result pointer, and
+ *     dllm_step in DLLM_MODE_AUTO, wait on the stream.
+ *   - Matrices are row-major; weight matrices are [in][out] (y = x W).
+ *   - Activations, weights, the hidden-state cache and the K/V cache use the
+ *     model dtype (DLLM_FP32 or DLLM_BF16); norm gains and the proxy basis are
+ *     fp32; proxies and drift scores are fp64; token ids and indices int32.
+ *   - Every function validates its arguments before enqueuing anything and
+ *     returns a dllm_status; on failure dllm_last_error() describes it.  A HIP
+ *     failure returns DLLM_E_HIP.  After a failure inside a step the state
+ *     contents are unspecified.
+ *   - One model serves one stream at a time (its workspace is shared).
+ */
+#ifndef LIBDLLM_H
+#define LIBDLLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dllm_model dllm_model; /* opaque; owned by the library */
+typedef int32_t dllm_status;
+
+enum {
+  DLLM_OK = 0,
+  DLLM_E_ARG = -1,         /* NULL or out-of-range argument */
+  DLLM_E_SHAPE = -2,       /* dimensions the library cannot handle */
+  DLLM_E_STATE = -3,       /* call order violated (e.g. layer weights missing) */
+  DLLM_E_NOMEM = -4,       /* device allocation failed */
+  DLLM_E_HIP = -5,         /* a HIP runtime call failed */
+  DLLM_E_UNSUPPORTED = -6  /* feature not built */
+};
+enum { DLLM_FP32 = 0, DLLM_BF16 = 1 };
+enum { DLLM_MODE_AUTO = 0, DLLM_MODE_FULL = 1, DLLM_MODE_SPARSE = 2 };
+enum { DLLM_FORCED_NONE = 0, DLLM_FORCED_BLOCK = 1, DLLM_FORCED_BLOCK_RECENT = 2 };
+
+/* Model and sequence dimensions.  Limits checked by dllm_create:
+ * head_dim even and <= 256; n_q_heads a multiple of n_kv_heads;
+ * seq_len <= 8192; block_len <= 64; proxy_rank <= 128; for DLLM_BF16 the
+ * widths d_model, d_ffn, n_q_heads*head_dim, n_kv_heads*head_dim and vocab
+ * must be multiples of 32 and d_model, d_ffn multiples of 64. */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  int32_t max_batch, seq_len, block_len, proxy_rank, dtype;
+  float rms_eps;    /* RMSNorm epsilon (1e-5) */
+  float rope_theta; /* rotary base (1e4) */
+} dllm_dims;
+
+/* One layer's weights (device pointers, model dtype unless noted).  The layer
+ * is h' = x + Attn(RMSNorm(x) * attn_norm) W_o,
+ *       out = h' + (SiLU(n W_gate) * (n W_up)) W_down,  n = RMSNorm(h') * ffn_norm,
+ * attention bidirectional (no mask) with rotate-half RoPE on q and k. */
+typedef struct {
+  const float *attn_norm; /* [d_model] fp32 */
+  const void *w_q;        /* [d_model][n_q_heads*head_dim] */
+  const void *w_k;        /* [d_model][n_kv_heads*head_dim] */
+  const void *w_v;        /* [d_model][n_kv_heads*head_dim] */
+  const void *w_o;        /* [n_q_heads*head_dim][d_model] */
+  const float *ffn_norm;  /* [d_model] fp32 */
+  const void *w_gate;     /* [d_model][d_ffn] */
+  const void *w_up;       /* [d_model][d_ffn] */
+  const void *w_down;     /* [d_ffn][d_model] */
+  /* SPA-Cache step 1: W_r = U_r S_r, the top-r left singular vectors of W_v
+   * scaled by their singular values, [d_model][proxy_rank] fp32. */
+  const float *w_proxy;
+} dllm_layer_weights;
+
+/* Caller-owned decode state (e.g. torch tensors); B = batch <= max_batch,
+ * L = seq_len, N = n_layers, r = proxy_rank.  Everything a step reads or
+ * writes lives here, so a copy of these buffers is a checkpoint. */
+typedef struct {
+  void *hidden;         /* [N+1][B][L][d_model]: slot 0 = embeddings, slot l+1 = layer l output */
+  void *k_cache;        /* [N][B][n_kv_heads][L][head_dim] (post-RoPE keys) */
+  void *v_cache;        /* [N][B][n_kv_heads][L][head_dim] */
+  double *proxy_cur;    /* [N][B][L][r]  current proxy C of each row's layer input */
+  double *proxy_ref;    /* [N][B][L][r]  proxy P at the row's last refresh */
+  double *score;        /* [N][B][L]     drift of C against P (0 for refreshed rows) */
+  int32_t *tokens;      /* [B][L]  token ids (masked rows hold the mask id) */
+  uint8_t *committed;   /* [B][L]  1 = prompt or committed token */
+  int32_t *history;     /* [B][L]  decode history: committed positions in commit order */
+  int32_t *n_history;   /* [B] */
+  int32_t *n_new;       /* [B]  commits made by the last commit (the tail of history) */
+  int32_t *block_start; /* [B]  first row of the current block (>= L when done) */
+  uint8_t *full_next;   /* [B]  entropy gate: 1 = the next step runs a full pass */
+  double *max_entropy;  /* [B]  max entropy (nats) over the last commit's tokens */
+  int32_t batch;
+} dllm_state;
+
+typedef struct {
+  int32_t mode;          /* DLLM_MODE_*; AUTO reads state.full_next (one host wait) */
+  int32_t forced_rule;   /* DLLM_FORCED_* */
+  int32_t recent_k;      /* EntropyCache k: recent decoded tokens always refreshed */
+  double tau;            /* entropy gate threshold in nats (+inf: never full) */
+  double conf_threshold; /* commit threshold on the top-1 probability */
+  const double *rho_h;   /* [n_layers] host: per-layer update ratio rho(l) */
+} dllm_step_params;
+
+typedef struct {
+  int32_t n_full;        /* sequences that ran a full pass in this step */
+  int32_t n_committed;   /* tokens committed in this step (all sequences) */
+  int32_t n_active;      /* sequences that still hold masked rows */
+  double max_entropy;    /* max over sequences of state.max_entropy */
+} dllm_step_result;
+
+/* Text of the last error on the calling thread ("" if none). */
+const char *dllm_last_error(void);
+
+/* Allocate a model for `dims` on the current HIP device, with workspace for
+ * max_batch sequences of seq_len rows.  *out is set on success. */
+dllm_status dllm_create(const dllm_dims *dims, dllm_model **out);
+
+/* Free a model and its workspace (waits for the device). NULL is a no-op. */
+dllm_status dllm_destroy(dllm_model *m);
+
+/* Copy layer `layer`'s weights into library-owned, repacked buffers (the
+ * caller may free its copies once the stream has passed this call). */
+dllm_status dllm_init_layer(dllm_model *m, int32_t layer, const dllm_layer_weights *w,
+                            void *stream);
+
+/* Copy the embedding table [vocab][d_model], the final norm gain [d_model]
+ * (fp32) and the LM head [d_model][vocab]. */
+dllm_status dllm_init_head(dllm_model *m, const void *embed, const float *final_norm,
+                           const void *lm_head, void *stream);
+
+/* Layer-0 input for listed rows: hidden[0][b][i] = embed[tokens[b][i]].
+ * Rows: rows[b][0..n_rows[b]) (layout [B][L]); rows == NULL means every row.
+ * A token id outside [0, vocab) yields a zero row. */
+dllm_status dllm_embed(dllm_model *m, const dllm_state *s, const int32_t *rows,
+                       const int32_t *n_rows, void *stream);
+
+/* SPA-Cache step 1 at `layer` for the rows whose layer input changed (rows as
+ * in dllm_embed; NULL = every row): C = (x * attn_norm) W_r in fp64 from
+ * x = hidden[layer][b][i], stored to proxy_cur, and
+ * score = 1 - cos(C, P) = 0.5 |C/|C| - P/|P||^2 (both zero: 0; one zero: 1)
+ * with P = proxy_ref.  Rows not listed keep their stored score.
+ * max_rows (host) bounds sum(n_rows); 0 means batch*seq_len. */
+dllm_status dllm_drift_score(dllm_model *m, int32_t layer, dllm_state *s, const int32_t *rows,
+                             const int32_t *n_rows, int32_t max_rows, void *stream);
+
+/* SPA-Cache step 2 / EntropyCache step 3: index set I of `layer` per sequence.
+ * k = floor(rho * seq_len + 1/2); rows with forced[b][i] != 0 (forced may be
+ * NULL) are always selected; the other max(k, |F|) - |F| rows are those with
+ * the largest score[layer][b][i], ties to the lower index.  Sequences with
+ * full[b] != 0 (full may be NULL) select every row.  Writes idx[b][0..n_sel[b])
+ * in ascending order ([B][L] layout) and n_sel[b]. */
+dllm_status dllm_select(dllm_model *m, int32_t layer, const dllm_state *s, const uint8_t *forced,
+                        const uint8_t *full, double rho, int32_t *idx, int32_t *n_sel,
+                        void *stream);
+
+/* SPA-Cache step 3 at `layer` on rows I = idx/n_sel (as from dllm_select):
+ * gather rows of hidden[layer], RMSNorm, QKV projection, RoPE, scatter the new
+ * keys/values into k_cache/v_cache (before attention), bidirectional attention
+ * of the selected queries over all seq_len cached rows, output projection and
+ * residual, FFN on the selected rows only, then hidden[layer+1][b][i] <- output
+ * for i in I (other rows keep their cached output), proxy_ref <- proxy_cur and
+ * score <- 0 for i in I.  max_rows bounds sum(n_sel) (0: batch*seq_len). */
+dllm_status dllm_sparse_layer(dllm_model *m, int32_t layer, dllm_state *s, const int32_t *idx,
+                              const int32_t *n_sel, int32_t max_rows, void *stream);
+
+/* LM-head statistics of the current block's rows (rows block_start[b] + j,
+ * j < block_len): z = (RMSNorm(hidden[N][b][row]) * final_norm) W_lm with the
+ * norm in fp64 and z accumulated in fp32.  stats_out[b][j][0..3] (fp64) =
+ * max z, argmax (lowest id on ties), S = sum exp(z - max), T = sum exp(z - max)(z - max);
+ * confidence = 1/S, entropy = ln S - T/S.  logits_out ([B][block_len][vocab]
+ * fp32) is optional (NULL: not written).  Rows past the end are zero. */
+dllm_status dllm_lm_head(dllm_model *m, const dllm_state *s, double *stats_out,
+                         float *logits_out, void *stream);
+
+/* Static-threshold commit over the current block plus the entropy gate:
+ * computes the LM-head statistics, commits every masked block row with
+ * confidence >= conf_threshold (if none, the single most confident masked row,
+ * lowest position on ties), writes tokens/committed, appends the commits to
+ * history in ascending position order, sets n_new, max_entropy (max entropy
+ * of the committed rows, 0 if none) and full_next = (max_entropy > tau), and
+ * advances block_start past fully committed blocks. */
+dllm_status dllm_commit(dllm_model *m, dllm_state *s, double conf_threshold, double tau,
+                        void *stream);
+
+/* Forced rows for the next step, forced[b][i] in {0,1} ([B][L]):
+ * DLLM_FORCED_BLOCK marks the current block, DLLM_FORCED_BLOCK_RECENT also the
+ * last recent_k entries of history, DLLM_FORCED_NONE marks nothing. */
+dllm_status dllm_forced_set(dllm_model *m, const dllm_state *s, int32_t rule, int32_t recent_k,
+                            uint8_t *forced, void *stream);
+
+/* One denoising step for every sequence: embed the rows whose token changed
+ * (every row in a full pass), then per layer drift score, selection (every
+ * row in a full pass) and sparse layer, then commit.  Mode FULL or SPARSE
+ * applies to every sequence; AUTO runs a full pass for the sequences whose
+ * full_next is set (the caller sets it before the first step, whose caches are
+ * empty).  If res_h is non-NULL the call waits for the stream and fills it. */
+dllm_status dllm_step(dllm_model *m, dllm_state *s, const dllm_step_params *p,
+                      dllm_step_result *res_h, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDLLM_H */

@@ -1,0 +1,588 @@
+// libdllm C-ABI: argument validation, weight repacking, workspace and the
+// per-step orchestration of the kernels (see include/libdllm.h).
+#include "../../include/libdllm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace dllm;
+
+namespace {
+
+thread_local std::string g_err;
+
+dllm_status fail(dllm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIPCHK(expr)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess) return fail(DLLM_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define CHK(expr)                   \
+  do {                              \
+    dllm_status s_ = (expr);        \
+    if (s_ != DLLM_OK) return s_;   \
+  } while (0)
+
+struct LayerW {
+  float* attn_norm = nullptr;
+  float* ffn_norm = nullptr;
+  void* w_qkv = nullptr;   // packed [d][nq + 2 nv]
+  void* w_o = nullptr;     // packed [nq][d]
+  void* w_gu = nullptr;    // packed [d][2F], gate/up interleaved by 32 columns
+  void* w_down = nullptr;  // packed [F][d]
+  double* w_proxy = nullptr;  // diag(attn_norm) W_r, fp64 [d][r]
+  bool ready = false;
+};
+
+}  // namespace
+
+struct dllm_model {
+  dllm_dims d{};
+  int device = 0;
+  bool bf16 = false;
+  int n_cu = 256;
+  size_t esize = 4;
+  std::vector<LayerW> layers;
+  void* embed = nullptr;
+  float* final_norm = nullptr;
+  void* lm_head = nullptr;
+  bool head_ready = false;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  // workspace
+  int M_cap = 0;   // max_batch * seq_len
+  int M_pad = 0;   // rows allocated in activation buffers
+  void* A1 = nullptr;
+  void* q = nullptr;
+  void* attn_o = nullptr;
+  void* A2 = nullptr;
+  void* act = nullptr;
+  float* hprime = nullptr;
+  float* part = nullptr;
+  size_t part_floats = 0;
+  double* ppart = nullptr;
+  size_t ppart_doubles = 0;
+  float* attn_part = nullptr;
+  int32_t* idx[2] = {nullptr, nullptr};
+  int32_t* nsel[2] = {nullptr, nullptr};
+  int32_t* idx0 = nullptr;
+  int32_t* n0 = nullptr;
+  uint8_t* forced = nullptr;
+  uint8_t* step_full = nullptr;
+  void* A_lm = nullptr;
+  float* logits = nullptr;
+  double* lm_part = nullptr;
+  double* lm_stats = nullptr;
+  int32_t* lm_rows = nullptr;
+  int lm_slabs = 0;
+  void* res_dev = nullptr;
+  void* res_host = nullptr;   // pinned, 32 bytes
+  uint8_t* full_host = nullptr;  // pinned, max_batch
+  std::vector<void*> allocs;
+
+  dllm_status alloc(void** p, size_t bytes) {
+    if (bytes == 0) bytes = 16;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+      *p = nullptr;
+      return fail(DLLM_E_NOMEM, "hipMalloc(%zu bytes): %s", bytes, hipGetErrorString(e));
+    }
+    allocs.push_back(*p);
+    e = hipMemset(*p, 0, bytes);
+    if (e != hipSuccess) return fail(DLLM_E_HIP, "hipMemset: %s", hipGetErrorString(e));
+    return DLLM_OK;
+  }
+  template <typename T>
+  dllm_status alloc_t(T** p, size_t count) {
+    void* v = nullptr;
+    dllm_status s = alloc(&v, count * sizeof(T));
+    *p = (T*)v;
+    return s;
+  }
+};
+
+namespace {
+
+inline hipStream_t S(void* stream) { return (hipStream_t)stream; }
+
+int nq_of(const dllm_dims& d) { return d.n_q_heads * d.head_dim; }
+int nv_of(const dllm_dims& d) { return d.n_kv_heads * d.head_dim; }
+
+dllm_status check_model(const dllm_model* m) {
+  if (!m) return fail(DLLM_E_ARG, "model is NULL");
+  return DLLM_OK;
+}
+
+dllm_status check_state(const dllm_model* m, const dllm_state* s, bool need_proxy = true) {
+  if (!s) return fail(DLLM_E_ARG, "state is NULL");
+  if (s->batch < 1 || s->batch > m->d.max_batch)
+    return fail(DLLM_E_ARG, "state.batch=%d outside [1, %d]", s->batch, m->d.max_batch);
+  if (!s->hidden || !s->k_cache || !s->v_cache || !s->tokens || !s->committed || !s->history || !s->n_history ||
+      !s->n_new || !s->block_start || !s->full_next || !s->max_entropy || !s->score)
+    return fail(DLLM_E_ARG, "state has a NULL buffer");
+  if (need_proxy && (!s->proxy_cur || !s->proxy_ref)) return fail(DLLM_E_ARG, "state has a NULL proxy buffer");
+  return DLLM_OK;
+}
+
+dllm_status check_layer(const dllm_model* m, int layer) {
+  if (layer < 0 || layer >= m->d.n_layers)
+    return fail(DLLM_E_ARG, "layer %d outside [0, %d)", layer, m->d.n_layers);
+  if (!m->layers[layer].ready) return fail(DLLM_E_STATE, "layer %d weights not initialised", layer);
+  return DLLM_OK;
+}
+
+// state slices
+void* hid(const dllm_model* m, const dllm_state* s, int slot) {
+  return (char*)s->hidden + (size_t)slot * s->batch * m->d.seq_len * m->d.d_model * m->esize;
+}
+void* kcache(const dllm_model* m, const dllm_state* s, int l) {
+  return (char*)s->k_cache + (size_t)l * s->batch * nv_of(m->d) * m->d.seq_len * m->esize;
+}
+void* vcache(const dllm_model* m, const dllm_state* s, int l) {
+  return (char*)s->v_cache + (size_t)l * s->batch * nv_of(m->d) * m->d.seq_len * m->esize;
+}
+double* pcur(const dllm_model* m, const dllm_state* s, int l) {
+  return s->proxy_cur + (size_t)l * s->batch * m->d.seq_len * m->d.proxy_rank;
+}
+double* pref(const dllm_model* m, const dllm_state* s, int l) {
+  return s->proxy_ref + (size_t)l * s->batch * m->d.seq_len * m->d.proxy_rank;
+}
+double* score(const dllm_model* m, const dllm_state* s, int l) {
+  return s->score + (size_t)l * s->batch * m->d.seq_len;
+}
+
+int clamp_rows(const dllm_model* m, const dllm_state* s, int max_rows) {
+  const int cap = s->batch * m->d.seq_len;
+  return (max_rows <= 0 || max_rows > cap) ? cap : max_rows;
+}
+
+// out = A W (partials into `out`, split count returned)
+dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int N, const void* A, const void* W,
+                 const int32_t* n_sel, float* out, size_t out_floats, int* splits) {
+  if (m->bf16) {
+    int sp = gemm_bf16_pick_splits(max_rows, K, N, m->n_cu);
+    while (sp > 1 && (size_t)sp * max_rows * N > out_floats) sp /= 2;
+    if ((size_t)sp * max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
+    HIPCHK(launch_gemm_bf16(st, max_rows, B, K, N, (const uint16_t*)A, (const uint16_t*)W, n_sel, out, sp));
+    *splits = sp;
+  } else {
+    if ((size_t)max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
+    HIPCHK(launch_gemm_f32(st, max_rows, B, K, N, (const float*)A, (const float*)W, n_sel, out));
+    *splits = 1;
+  }
+  return DLLM_OK;
+}
+
+dllm_status pack(dllm_model* m, hipStream_t st, int K, int Nsrc, const void* src, void* dst, int Ndst, int col0,
+                 int tile_stride) {
+  if (m->bf16)
+    HIPCHK(launch_pack_bf16(st, K, Nsrc, (const uint16_t*)src, Nsrc, (uint16_t*)dst, col0, tile_stride));
+  else
+    HIPCHK(launch_pack_f32(st, K, Nsrc, (const float*)src, Nsrc, (float*)dst, Ndst, col0, tile_stride));
+  return DLLM_OK;
+}
+
+dllm_status do_drift(dllm_model* m, int layer, dllm_state* s, const int32_t* rows, const int32_t* n, int max_rows,
+                     hipStream_t st) {
+  const dllm_dims& d = m->d;
+  HIPCHK(launch_proxy_drift(st, m->bf16, max_rows, s->batch, d.seq_len, d.d_model, d.proxy_rank, rows, n,
+                            hid(m, s, layer), m->layers[layer].w_proxy, m->ppart, pcur(m, s, layer),
+                            pref(m, s, layer), score(m, s, layer)));
+  return DLLM_OK;
+}
+
+dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* idx, const int32_t* n, int max_rows,
+                      hipStream_t st) {
+  const dllm_dims& d = m->d;
+  const int B = s->batch, L = d.seq_len, D = d.d_model, F = d.d_ffn;
+  const int nq = nq_of(d), nv = nv_of(d);
+  const LayerW& w = m->layers[layer];
+  const void* Hin = hid(m, s, layer);
+  int sp = 1;
+  HIPCHK(launch_gather_norm(st, m->bf16, max_rows, B, L, D, d.rms_eps, idx, n, Hin, w.attn_norm, m->A1));
+  CHK(gemm(m, st, max_rows, B, D, nq + 2 * nv, m->A1, w.w_qkv, n, m->part, m->part_floats, &sp));
+  HIPCHK(launch_qkv_epilogue(st, m->bf16, max_rows, B, L, d.n_q_heads, d.n_kv_heads, d.head_dim, sp, idx, n,
+                             m->part, m->rope_cos, m->rope_sin, m->q, kcache(m, s, layer), vcache(m, s, layer)));
+  HIPCHK(launch_attention(st, m->bf16, max_rows, B, L, d.n_q_heads, d.n_kv_heads, d.head_dim, idx, n, m->q,
+                          kcache(m, s, layer), vcache(m, s, layer), m->attn_part, m->attn_o));
+  CHK(gemm(m, st, max_rows, B, nq, D, m->attn_o, w.w_o, n, m->part, m->part_floats, &sp));
+  HIPCHK(launch_o_epilogue(st, m->bf16, max_rows, B, L, D, sp, d.rms_eps, idx, n, m->part, Hin, w.ffn_norm,
+                           m->hprime, m->A2));
+  CHK(gemm(m, st, max_rows, B, D, 2 * F, m->A2, w.w_gu, n, m->part, m->part_floats, &sp));
+  HIPCHK(launch_swiglu(st, m->bf16, max_rows, B, F, sp, n, m->part, m->act));
+  CHK(gemm(m, st, max_rows, B, F, D, m->act, w.w_down, n, m->part, m->part_floats, &sp));
+  HIPCHK(launch_down_epilogue(st, m->bf16, max_rows, B, L, D, d.proxy_rank, sp, idx, n, m->part, m->hprime,
+                              hid(m, s, layer + 1), pcur(m, s, layer), pref(m, s, layer), score(m, s, layer)));
+  return DLLM_OK;
+}
+
+dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st) {
+  const dllm_dims& d = m->d;
+  const int B = s->batch, blk = d.block_len;
+  HIPCHK(launch_lm_gather(st, m->bf16, B, d.seq_len, blk, d.d_model, d.rms_eps, s->block_start,
+                          hid(m, s, d.n_layers), m->final_norm, m->A_lm, m->lm_rows));
+  int sp = 1;
+  const size_t cap = (size_t)d.max_batch * blk * d.vocab;
+  if (m->bf16) {
+    HIPCHK(launch_gemm_bf16(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm,
+                            (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1));
+  } else {
+    CHK(gemm(m, st, B * blk, 1, d.d_model, d.vocab, m->A_lm, m->lm_head, m->lm_rows, m->logits, cap, &sp));
+  }
+  HIPCHK(launch_lm_stats(st, B * blk, d.vocab, m->logits, m->lm_part, m->lm_stats, m->lm_slabs));
+  return DLLM_OK;
+}
+
+dllm_status do_commit(dllm_model* m, dllm_state* s, double thr, double tau, hipStream_t st) {
+  CHK(do_lm_head(m, s, st));
+  const dllm_dims& d = m->d;
+  HIPCHK(launch_commit(st, s->batch, d.seq_len, d.block_len, thr, tau, m->lm_stats, s->tokens, s->committed,
+                       s->history, s->n_history, s->n_new, s->block_start, s->full_next, s->max_entropy));
+  return DLLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dllm_last_error(void) { return g_err.c_str(); }
+
+dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
+  if (!dims || !out) return fail(DLLM_E_ARG, "dims/out is NULL");
+  *out = nullptr;
+  const dllm_dims& d = *dims;
+  if (d.n_layers < 1 || d.d_model < 1 || d.n_q_heads < 1 || d.n_kv_heads < 1 || d.head_dim < 2 || d.d_ffn < 1 ||
+      d.vocab < 2 || d.max_batch < 1 || d.seq_len < 1 || d.block_len < 1 || d.proxy_rank < 1)
+    return fail(DLLM_E_ARG, "non-positive dimension");
+  if (d.dtype != DLLM_FP32 && d.dtype != DLLM_BF16) return fail(DLLM_E_ARG, "unknown dtype %d", d.dtype);
+  if (d.head_dim % 2 || d.head_dim > 256) return fail(DLLM_E_SHAPE, "head_dim must be even and <= 256");
+  if (d.n_q_heads % d.n_kv_heads) return fail(DLLM_E_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (d.seq_len > 8192) return fail(DLLM_E_SHAPE, "seq_len %d > 8192", d.seq_len);
+  if (d.block_len > 64) return fail(DLLM_E_SHAPE, "block_len %d > 64", d.block_len);
+  if (d.proxy_rank > 128 || d.proxy_rank > d.d_model) return fail(DLLM_E_SHAPE, "proxy_rank must be <= 128 and <= d_model");
+  if (d.d_model % 32 || d.d_ffn % 32) return fail(DLLM_E_SHAPE, "d_model and d_ffn must be multiples of 32");
+  if (!(d.rms_eps >= 0.f) || !(d.rope_theta > 0.f)) return fail(DLLM_E_ARG, "bad rms_eps/rope_theta");
+  const int nq = nq_of(d), nv = nv_of(d);
+  if (d.dtype == DLLM_BF16) {
+    if (d.d_model % 64 || d.d_ffn % 64 || nq % 64 || nv % 32 || d.vocab % 32)
+      return fail(DLLM_E_SHAPE, "bf16 widths: d_model, d_ffn, n_q*head_dim multiples of 64; n_kv*head_dim, vocab multiples of 32");
+  }
+  dllm_model* m = new dllm_model();
+  m->d = d;
+  m->bf16 = d.dtype == DLLM_BF16;
+  m->esize = m->bf16 ? 2 : 4;
+  m->layers.resize(d.n_layers);
+  auto cleanup = [&](dllm_status st) {
+    std::string keep = g_err;
+    dllm_destroy(m);
+    g_err = keep;
+    return st;
+  };
+  if (hipGetDevice(&m->device) != hipSuccess) return cleanup(fail(DLLM_E_HIP, "hipGetDevice failed"));
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, m->device) == hipSuccess && prop.multiProcessorCount > 0)
+    m->n_cu = prop.multiProcessorCount;
+  const int L = d.seq_len, D = d.d_model, F = d.d_ffn;
+  m->M_cap = d.max_batch * L;
+  m->M_pad = (m->M_cap + 31) / 32 * 32 + 32;
+  const size_t es = m->esize;
+  dllm_status st;
+#define ALLOC(ptr, bytes)                         \
+  do {                                            \
+    st = m->alloc((void**)&(ptr), (bytes));       \
+    if (st != DLLM_OK) return cleanup(st);        \
+  } while (0)
+  ALLOC(m->A1, (size_t)m->M_pad * D * es);
+  ALLOC(m->q, (size_t)m->M_pad * nq * es);
+  ALLOC(m->attn_o, (size_t)m->M_pad * nq * es);
+  ALLOC(m->A2, (size_t)m->M_pad * D * es);
+  ALLOC(m->act, (size_t)m->M_pad * F * es);
+  ALLOC(m->hprime, (size_t)m->M_pad * D * 4);
+  {
+    const int nmax = std::max(std::max(nq + 2 * nv, 2 * F), D);
+    // split-K partials: the sparse GEMMs split up to 16x; full passes use few splits
+    m->part_floats = (size_t)std::max(m->M_cap, 16 * 320) * nmax;
+    ALLOC(m->part, m->part_floats * 4);
+  }
+  m->ppart_doubles = proxy_partial_doubles(m->M_cap, D, d.proxy_rank);
+  ALLOC(m->ppart, m->ppart_doubles * 8);
+  {
+    const size_t af = attn_partial_floats(m->M_cap, d.n_q_heads, d.head_dim, L);
+    if (af) ALLOC(m->attn_part, af * 4);
+  }
+  for (int i = 0; i < 2; ++i) {
+    ALLOC(m->idx[i], (size_t)m->M_cap * 4);
+    ALLOC(m->nsel[i], (size_t)d.max_batch * 4);
+  }
+  ALLOC(m->idx0, (size_t)m->M_cap * 4);
+  ALLOC(m->n0, (size_t)d.max_batch * 4);
+  ALLOC(m->forced, (size_t)m->M_cap);
+  ALLOC(m->step_full, (size_t)d.max_batch);
+  const int lm_rows_cap = d.max_batch * d.block_len;
+  ALLOC(m->A_lm, (size_t)(lm_rows_cap + 32) * D * es);
+  ALLOC(m->logits, (size_t)lm_rows_cap * d.vocab * 4);
+  m->lm_slabs = lm_stats_slabs(d.vocab);
+  ALLOC(m->lm_part, (size_t)lm_rows_cap * m->lm_slabs * 4 * 8);
+  ALLOC(m->lm_stats, (size_t)lm_rows_cap * 4 * 8);
+  ALLOC(m->lm_rows, 16);
+  ALLOC(m->res_dev, 64);
+  if (hipHostMalloc(&m->res_host, 64, hipHostMallocDefault) != hipSuccess)
+    return cleanup(fail(DLLM_E_NOMEM, "hipHostMalloc failed"));
+  if (hipHostMalloc((void**)&m->full_host, (size_t)d.max_batch + 16, hipHostMallocDefault) != hipSuccess)
+    return cleanup(fail(DLLM_E_NOMEM, "hipHostMalloc failed"));
+  // RoPE tables: angle = pos * theta^(-2j/dh), computed in fp64 on the host
+  {
+    const int half = d.head_dim / 2;
+    std::vector<float> c((size_t)L * half), sn((size_t)L * half);
+    for (int p = 0; p < L; ++p)
+      for (int j = 0; j < half; ++j) {
+        const double inv = std::pow((double)d.rope_theta, -(2.0 * j) / d.head_dim);
+        const double a = (double)p * inv;
+        c[(size_t)p * half + j] = (float)std::cos(a);
+        sn[(size_t)p * half + j] = (float)std::sin(a);
+      }
+    ALLOC(m->rope_cos, c.size() * 4);
+    ALLOC(m->rope_sin, sn.size() * 4);
+    if (hipMemcpy(m->rope_cos, c.data(), c.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(m->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+      return cleanup(fail(DLLM_E_HIP, "RoPE table upload failed"));
+  }
+#undef ALLOC
+  *out = m;
+  g_err.clear();
+  return DLLM_OK;
+}
+
+dllm_status dllm_destroy(dllm_model* m) {
+  if (!m) return DLLM_OK;
+  (void)hipDeviceSynchronize();
+  for (void* p : m->allocs) (void)hipFree(p);
+  if (m->res_host) (void)hipHostFree(m->res_host);
+  if (m->full_host) (void)hipHostFree(m->full_host);
+  delete m;
+  return DLLM_OK;
+}
+
+dllm_status dllm_init_layer(dllm_model* m, int32_t layer, const dllm_layer_weights* w, void* stream) {
+  CHK(check_model(m));
+  if (!w) return fail(DLLM_E_ARG, "weights is NULL");
+  if (layer < 0 || layer >= m->d.n_layers) return fail(DLLM_E_ARG, "layer %d outside [0, %d)", layer, m->d.n_layers);
+  if (!w->attn_norm || !w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->ffn_norm || !w->w_gate || !w->w_up ||
+      !w->w_down || !w->w_proxy)
+    return fail(DLLM_E_ARG, "layer %d: a weight pointer is NULL", layer);
+  const dllm_dims& d = m->d;
+  const int D = d.d_model, F = d.d_ffn, nq = nq_of(d), nv = nv_of(d), r = d.proxy_rank;
+  const size_t es = m->esize;
+  LayerW& L = m->layers[layer];
+  hipStream_t st = S(stream);
+  if (!L.w_qkv) {
+    CHK(m->alloc((void**)&L.attn_norm, (size_t)D * 4));
+    CHK(m->alloc((void**)&L.ffn_norm, (size_t)D * 4));
+    CHK(m->alloc(&L.w_qkv, (size_t)D * (nq + 2 * nv) * es));
+    CHK(m->alloc(&L.w_o, (size_t)nq * D * es));
+    CHK(m->alloc(&L.w_gu, (size_t)D * 2 * F * es));
+    CHK(m->alloc(&L.w_down, (size_t)F * D * es));
+    CHK(m->alloc((void**)&L.w_proxy, (size_t)D * r * 8));
+  }
+  HIPCHK(hipMemcpyAsync(L.attn_norm, w->attn_norm, (size_t)D * 4, hipMemcpyDeviceToDevice, st));
+  HIPCHK(hipMemcpyAsync(L.ffn_norm, w->ffn_norm, (size_t)D * 4, hipMemcpyDeviceToDevice, st));
+  const int nqkv = nq + 2 * nv;
+  CHK(pack(m, st, D, nq, w->w_q, L.w_qkv, nqkv, 0, 32));
+  CHK(pack(m, st, D, nv, w->w_k, L.w_qkv, nqkv, nq, 32));
+  CHK(pack(m, st, D, nv, w->w_v, L.w_qkv, nqkv, nq + nv, 32));
+  CHK(pack(m, st, nq, D, w->w_o, L.w_o, D, 0, 32));
+  CHK(pack(m, st, D, F, w->w_gate, L.w_gu, 2 * F, 0, 64));
+  CHK(pack(m, st, D, F, w->w_up, L.w_gu, 2 * F, 32, 64));
+  CHK(pack(m, st, F, D, w->w_down, L.w_down, D, 0, 32));
+  HIPCHK(launch_fold_proxy(st, D, r, w->attn_norm, w->w_proxy, L.w_proxy));
+  L.ready = true;
+  return DLLM_OK;
+}
+
+dllm_status dllm_init_head(dllm_model* m, const void* embed, const float* final_norm, const void* lm_head,
+                           void* stream) {
+  CHK(check_model(m));
+  if (!embed || !final_norm || !lm_head) return fail(DLLM_E_ARG, "head pointer is NULL");
+  const dllm_dims& d = m->d;
+  hipStream_t st = S(stream);
+  if (!m->embed) {
+    CHK(m->alloc(&m->embed, (size_t)d.vocab * d.d_model * m->esize));
+    CHK(m->alloc((void**)&m->final_norm, (size_t)d.d_model * 4));
+    CHK(m->alloc(&m->lm_head, (size_t)d.d_model * d.vocab * m->esize));
+  }
+  HIPCHK(hipMemcpyAsync(m->embed, embed, (size_t)d.vocab * d.d_model * m->esize, hipMemcpyDeviceToDevice, st));
+  HIPCHK(hipMemcpyAsync(m->final_norm, final_norm, (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
+  CHK(pack(m, st, d.d_model, d.vocab, lm_head, m->lm_head, d.vocab, 0, 32));
+  m->head_ready = true;
+  return DLLM_OK;
+}
+
+dllm_status dllm_embed(dllm_model* m, const dllm_state* s, const int32_t* rows, const int32_t* n_rows, void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s, false));
+  if (!m->head_ready) return fail(DLLM_E_STATE, "head weights not initialised");
+  if ((rows == nullptr) != (n_rows == nullptr)) return fail(DLLM_E_ARG, "rows and n_rows must both be set or NULL");
+  hipStream_t st = S(stream);
+  const int B = s->batch, L = m->d.seq_len;
+  if (!rows) {
+    HIPCHK(launch_all_rows(st, B, L, m->idx0, m->n0));
+    rows = m->idx0;
+    n_rows = m->n0;
+  }
+  HIPCHK(launch_embed(st, m->bf16, B * L, B, L, m->d.d_model, m->d.vocab, rows, n_rows, s->tokens, m->embed,
+                      hid(m, s, 0)));
+  return DLLM_OK;
+}
+
+dllm_status dllm_drift_score(dllm_model* m, int32_t layer, dllm_state* s, const int32_t* rows,
+                             const int32_t* n_rows, int32_t max_rows, void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s));
+  CHK(check_layer(m, layer));
+  if ((rows == nullptr) != (n_rows == nullptr)) return fail(DLLM_E_ARG, "rows and n_rows must both be set or NULL");
+  hipStream_t st = S(stream);
+  if (!rows) {
+    HIPCHK(launch_all_rows(st, s->batch, m->d.seq_len, m->idx0, m->n0));
+    rows = m->idx0;
+    n_rows = m->n0;
+    max_rows = s->batch * m->d.seq_len;
+  }
+  return do_drift(m, layer, s, rows, n_rows, clamp_rows(m, s, max_rows), st);
+}
+
+dllm_status dllm_select(dllm_model* m, int32_t layer, const dllm_state* s, const uint8_t* forced, const uint8_t* full,
+                        double rho, int32_t* idx, int32_t* n_sel, void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s));
+  if (layer < 0 || layer >= m->d.n_layers) return fail(DLLM_E_ARG, "layer %d outside [0, %d)", layer, m->d.n_layers);
+  if (!idx || !n_sel) return fail(DLLM_E_ARG, "idx/n_sel is NULL");
+  if (!(rho >= 0.0)) return fail(DLLM_E_ARG, "rho must be >= 0");
+  const int L = m->d.seq_len;
+  const double kf = std::floor(rho * L + 0.5);
+  const int k = kf > (double)L ? L : (int)kf;
+  HIPCHK(launch_select(S(stream), s->batch, L, k, score(m, s, layer), forced, full, idx, n_sel));
+  return DLLM_OK;
+}
+
+dllm_status dllm_sparse_layer(dllm_model* m, int32_t layer, dllm_state* s, const int32_t* idx, const int32_t* n_sel,
+                              int32_t max_rows, void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s));
+  CHK(check_layer(m, layer));
+  if (!idx || !n_sel) return fail(DLLM_E_ARG, "idx/n_sel is NULL");
+  return do_sparse(m, layer, s, idx, n_sel, clamp_rows(m, s, max_rows), S(stream));
+}
+
+dllm_status dllm_lm_head(dllm_model* m, const dllm_state* s, double* stats_out, float* logits_out, void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s, false));
+  if (!m->head_ready) return fail(DLLM_E_STATE, "head weights not initialised");
+  hipStream_t st = S(stream);
+  CHK(do_lm_head(m, s, st));
+  const size_t rows = (size_t)s->batch * m->d.block_len;
+  if (stats_out) HIPCHK(hipMemcpyAsync(stats_out, m->lm_stats, rows * 4 * 8, hipMemcpyDeviceToDevice, st));
+  if (logits_out)
+    HIPCHK(hipMemcpyAsync(logits_out, m->logits, rows * m->d.vocab * 4, hipMemcpyDeviceToDevice, st));
+  return DLLM_OK;
+}
+
+dllm_status dllm_commit(dllm_model* m, dllm_state* s, double conf_threshold, double tau, void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s, false));
+  if (!m->head_ready) return fail(DLLM_E_STATE, "head weights not initialised");
+  if (std::isnan(conf_threshold) || std::isnan(tau)) return fail(DLLM_E_ARG, "threshold is NaN");
+  return do_commit(m, s, conf_threshold, tau, S(stream));
+}
+
+dllm_status dllm_forced_set(dllm_model* m, const dllm_state* s, int32_t rule, int32_t recent_k, uint8_t* forced,
+                            void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s, false));
+  if (!forced) return fail(DLLM_E_ARG, "forced is NULL");
+  if (rule < DLLM_FORCED_NONE || rule > DLLM_FORCED_BLOCK_RECENT) return fail(DLLM_E_ARG, "unknown forced rule %d", rule);
+  if (recent_k < 0) return fail(DLLM_E_ARG, "recent_k < 0");
+  HIPCHK(launch_forced(S(stream), s->batch, m->d.seq_len, m->d.block_len, rule, recent_k, s->history, s->n_history,
+                       s->block_start, forced));
+  return DLLM_OK;
+}
+
+dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, dllm_step_result* res_h,
+                      void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s));
+  if (!p || !p->rho_h) return fail(DLLM_E_ARG, "params/rho_h is NULL");
+  if (p->mode < DLLM_MODE_AUTO || p->mode > DLLM_MODE_SPARSE) return fail(DLLM_E_ARG, "unknown mode %d", p->mode);
+  if (p->forced_rule < DLLM_FORCED_NONE || p->forced_rule > DLLM_FORCED_BLOCK_RECENT)
+    return fail(DLLM_E_ARG, "unknown forced rule %d", p->forced_rule);
+  if (p->recent_k < 0) return fail(DLLM_E_ARG, "recent_k < 0");
+  if (std::isnan(p->tau) || std::isnan(p->conf_threshold)) return fail(DLLM_E_ARG, "threshold is NaN");
+  const dllm_dims& d = m->d;
+  for (int l = 0; l < d.n_layers; ++l) {
+    CHK(check_layer(m, l));
+    if (!(p->rho_h[l] >= 0.0)) return fail(DLLM_E_ARG, "rho[%d] must be >= 0", l);
+  }
+  if (!m->head_ready) return fail(DLLM_E_STATE, "head weights not initialised");
+  hipStream_t st = S(stream);
+  const int B = s->batch, L = d.seq_len;
+  bool any_full = p->mode == DLLM_MODE_FULL;
+  if (p->mode == DLLM_MODE_AUTO) {
+    HIPCHK(hipMemcpyAsync(m->full_host, s->full_next, (size_t)B, hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    for (int b = 0; b < B; ++b) any_full = any_full || m->full_host[b] != 0;
+  }
+  const int fmax = p->forced_rule == DLLM_FORCED_NONE ? 0
+                   : (p->forced_rule == DLLM_FORCED_BLOCK ? d.block_len : d.block_len + p->recent_k);
+  HIPCHK(launch_prep(st, B, L, d.block_len, p->forced_rule, p->recent_k, p->mode, s->history, s->n_history, s->n_new,
+                     s->block_start, s->full_next, m->forced, m->step_full, m->idx0, m->n0));
+  int prev_max = any_full ? B * L : B * std::min(L, d.block_len);
+  const int32_t* prev_idx = m->idx0;
+  const int32_t* prev_n = m->n0;
+  HIPCHK(launch_embed(st, m->bf16, prev_max, B, L, d.d_model, d.vocab, prev_idx, prev_n, s->tokens, m->embed,
+                      hid(m, s, 0)));
+  for (int l = 0; l < d.n_layers; ++l) {
+    CHK(do_drift(m, l, s, prev_idx, prev_n, prev_max, st));
+    const double kf = std::floor(p->rho_h[l] * L + 0.5);
+    const int k = kf > (double)L ? L : (int)kf;
+    int32_t* idx = m->idx[l & 1];
+    int32_t* n = m->nsel[l & 1];
+    HIPCHK(launch_select(st, B, L, k, score(m, s, l), m->forced, m->step_full, idx, n));
+    const int rows = any_full ? B * L : B * std::min(L, std::max(k, fmax));
+    CHK(do_sparse(m, l, s, idx, n, rows, st));
+    prev_idx = idx;
+    prev_n = n;
+    prev_max = rows;
+  }
+  CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
+  if (res_h) {
+    HIPCHK(launch_step_result(st, B, m->step_full, s->n_new, s->block_start, s->max_entropy, L, m->res_dev));
+    HIPCHK(hipMemcpyAsync(m->res_host, m->res_dev, 32, hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    const int32_t* r = (const int32_t*)m->res_host;
+    res_h->n_full = r[0];
+    res_h->n_committed = r[1];
+    res_h->n_active = r[2];
+    std::memcpy(&res_h->max_entropy, r + 4, 8);
+  }
+  return DLLM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Host-side launchers of the libdllm kernels.  Every launcher enqueues on
+// `st` and returns hipGetLastError() of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dllm {
+
+// ---- row bookkeeping (rows.hip) ----
+// forced set + layer-0 changed rows + per-sequence full flags of this step.
+// mode: 0 auto (full_next), 1 full, 2 sparse.
+hipError_t launch_prep(hipStream_t st, int B, int L, int block_len, int rule, int recent_k, int mode,
+                       const int32_t* history, const int32_t* n_history, const int32_t* n_new,
+                       const int32_t* block_start, const uint8_t* full_next, uint8_t* forced,
+                       uint8_t* step_full, int32_t* idx0, int32_t* n0);
+hipError_t launch_forced(hipStream_t st, int B, int L, int block_len, int rule, int recent_k,
+                         const int32_t* history, const int32_t* n_history, const int32_t* block_start,
+                         uint8_t* forced);
+hipError_t launch_all_rows(hipStream_t st, int B, int L, int32_t* idx, int32_t* n);
+hipError_t launch_embed(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, int V,
+                        const int32_t* idx, const int32_t* n, const int32_t* tokens, const void* embed,
+                        void* h0);
+// A[m] = RMSNorm(H[row m]) * g  (fp32 statistics), rows from idx/n.
+hipError_t launch_gather_norm(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, float eps,
+                              const int32_t* idx, const int32_t* n, const void* H, const float* g,
+                              void* A);
+// q/k RoPE + K/V scatter from QKV partials [S][M][nq + 2 nv].
+hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16, int max_rows, int B, int L, int Hq, int Hkv,
+                               int dh, int S, const int32_t* idx, const int32_t* n, const float* part,
+                               const float* rope_cos, const float* rope_sin, void* q_out, void* Kc,
+                               void* Vc);
+// h' = x + sum_s part; A2 = RMSNorm(h') * g2.
+hipError_t launch_o_epilogue(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, int S,
+                             float eps, const int32_t* idx, const int32_t* n, const float* part,
+                             const void* H, const float* g2, float* hprime, void* A2);
+// act = SiLU(gate) * up from gate|up partials interleaved by 32 columns.
+hipError_t launch_swiglu(hipStream_t st, bool bf16, int max_rows, int B, int F, int S, const int32_t* n,
+                         const float* part, void* act);
+// H_out[row] = h' + sum_s part; proxy_ref[row] = proxy_cur[row]; score[row] = 0.
+hipError_t launch_down_epilogue(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, int r,
+                                int S, const int32_t* idx, const int32_t* n, const float* part,
+                                const float* hprime, void* H_out, const double* pcur, double* pref,
+                                double* score);
+
+// ---- proxy and drift (proxy.hip) ----
+// Capacity of the split partial buffer needed for max_rows rows (doubles).
+size_t proxy_partial_doubles(int max_rows, int d, int r);
+hipError_t launch_proxy_drift(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, int r,
+                              const int32_t* idx, const int32_t* n, const void* H, const double* wg,
+                              double* partial, double* pcur, const double* pref, double* score);
+
+hipError_t launch_fold_proxy(hipStream_t st, int d, int r, const float* g1, const float* wr, double* out);
+
+// ---- selection (select.hip) ----
+hipError_t launch_select(hipStream_t st, int B, int L, int k, const double* score, const uint8_t* forced,
+                         const uint8_t* full, int32_t* idx, int32_t* n);
+
+// ---- GEMMs (gemm.hip) ----
+// out[s][m][n] = sum_{k in split s} A[m][k] W[k][n] for m < sum(n_sel).
+hipError_t launch_gemm_f32(hipStream_t st, int max_rows, int B, int K, int N, const float* A,
+                           const float* W, const int32_t* n_sel, float* out);
+// bf16 weights pre-packed by launch_pack_bf16; `splits` from gemm_bf16_pick_splits.
+hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A,
+                            const uint16_t* Wp, const int32_t* n_sel, float* out, int splits);
+int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu);
+// Pack source columns [0, Nsrc) of a row-major [K][ld_src] weight: source
+// column tile t (32 columns) lands at packed column col0 + t*tile_stride.
+// bf16: MFMA B-fragment tiles; fp32: row-major [K][Ndst].
+hipError_t launch_pack_bf16(hipStream_t st, int K, int Nsrc, const uint16_t* src, int ld_src, uint16_t* dst,
+                            int col0, int tile_stride);
+hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, int ld_src, float* dst, int Ndst,
+                           int col0, int tile_stride);
+
+// ---- attention (attn.hip) ----
+size_t attn_partial_floats(int max_rows, int Hq, int dh, int L);
+hipError_t launch_attention(hipStream_t st, bool bf16, int max_rows, int B, int L, int Hq, int Hkv, int dh,
+                            const int32_t* idx, const int32_t* n, const void* q, const void* Kc,
+                            const void* Vc, float* partial, void* out);
+
+// ---- LM head and commit (lmhead.hip) ----
+hipError_t launch_lm_gather(hipStream_t st, bool bf16, int B, int L, int blk, int d, float eps,
+                            const int32_t* block_start, const void* H, const float* g, void* A,
+                            int32_t* n_rows);
+hipError_t launch_lm_stats(hipStream_t st, int M, int V, const float* logits, double* part,
+                           double* stats, int n_slabs);
+int lm_stats_slabs(int V);
+hipError_t launch_commit(hipStream_t st, int B, int L, int blk, double thr, double tau,
+                         const double* stats, int32_t* tokens, uint8_t* committed, int32_t* history,
+                         int32_t* n_history, int32_t* n_new, int32_t* block_start, uint8_t* full_next,
+                         double* max_entropy);
+// out: {n_full, n_committed, n_active, pad} int32 then max entropy as double (24 bytes).
+hipError_t launch_step_result(hipStream_t st, int B, const uint8_t* step_full, const int32_t* n_new,
+                              const int32_t* block_start, const double* max_entropy, int L, void* out);
+
+}  // namespace dllm

@@ -1,0 +1,336 @@
+// Row bookkeeping, gathers, norms and GEMM epilogues of the sparse layer.
+//
+// Sparse execution (SPA-Cache, method step 3): only the selected rows I are
+// gathered, normed and projected; their new keys/values are scattered into
+// the cache before attention, and the layer output is written back only at I.
+#include "common.h"
+#include "kernels.h"
+
+namespace dllm {
+
+// ---------------------------------------------------------------------------
+// Forced rows (EntropyCache step 3: current mask block + k most recent
+// decoded tokens; Polestar: current block), the rows whose token changed since
+// the last step (the layer-0 rows to refresh) and this step's full flags.
+// One workgroup per sequence.
+// ---------------------------------------------------------------------------
+__global__ void prep_kernel(int L, int block_len, int rule, int recent_k, int mode,
+                            const int32_t* __restrict__ history, const int32_t* __restrict__ n_history,
+                            const int32_t* __restrict__ n_new, const int32_t* __restrict__ block_start,
+                            const uint8_t* __restrict__ full_next, uint8_t* __restrict__ forced,
+                            uint8_t* __restrict__ step_full, int32_t* __restrict__ idx0,
+                            int32_t* __restrict__ n0) {
+  const int b = blockIdx.x;
+  const int nh = n_history[b];
+  const int bs = block_start[b];
+  const int full = mode == 1 ? 1 : (mode == 2 ? 0 : (full_next[b] ? 1 : 0));
+  if (forced != nullptr) {
+    for (int i = threadIdx.x; i < L; i += blockDim.x)
+      forced[(size_t)b * L + i] = (rule >= 1 && i >= bs && i < bs + block_len) ? 1 : 0;
+    __syncthreads();
+    if (rule == 2) {
+      const int nr = min(recent_k, nh);
+      for (int j = threadIdx.x; j < nr; j += blockDim.x) {
+        const int p = history[(size_t)b * L + nh - 1 - j];
+        if (p >= 0 && p < L) forced[(size_t)b * L + p] = 1;
+      }
+    }
+  }
+  if (idx0 != nullptr) {
+    if (full) {
+      for (int i = threadIdx.x; i < L; i += blockDim.x) idx0[(size_t)b * L + i] = i;
+      if (threadIdx.x == 0) n0[b] = L;
+    } else {
+      const int nn = min(n_new[b], nh);
+      for (int j = threadIdx.x; j < nn; j += blockDim.x) idx0[(size_t)b * L + j] = history[(size_t)b * L + nh - nn + j];
+      if (threadIdx.x == 0) n0[b] = nn;
+    }
+  }
+  if (step_full != nullptr && threadIdx.x == 0) step_full[b] = (uint8_t)full;
+}
+
+hipError_t launch_prep(hipStream_t st, int B, int L, int block_len, int rule, int recent_k, int mode,
+                       const int32_t* history, const int32_t* n_history, const int32_t* n_new,
+                       const int32_t* block_start, const uint8_t* full_next, uint8_t* forced,
+                       uint8_t* step_full, int32_t* idx0, int32_t* n0) {
+  hipLaunchKernelGGL(prep_kernel, dim3(B), dim3(256), 0, st, L, block_len, rule, recent_k, mode, history,
+                     n_history, n_new, block_start, full_next, forced, step_full, idx0, n0);
+  return hipGetLastError();
+}
+
+hipError_t launch_forced(hipStream_t st, int B, int L, int block_len, int rule, int recent_k,
+                         const int32_t* history, const int32_t* n_history, const int32_t* block_start,
+                         uint8_t* forced) {
+  hipLaunchKernelGGL(prep_kernel, dim3(B), dim3(256), 0, st, L, block_len, rule, recent_k, 2, history,
+                     n_history, (const int32_t*)nullptr, block_start, (const uint8_t*)nullptr, forced,
+                     (uint8_t*)nullptr, (int32_t*)nullptr, (int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+__global__ void all_rows_kernel(int L, int32_t* __restrict__ idx, int32_t* __restrict__ n) {
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < L; i += blockDim.x) idx[(size_t)b * L + i] = i;
+  if (threadIdx.x == 0) n[b] = L;
+}
+
+hipError_t launch_all_rows(hipStream_t st, int B, int L, int32_t* idx, int32_t* n) {
+  hipLaunchKernelGGL(all_rows_kernel, dim3(B), dim3(256), 0, st, L, idx, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Layer-0 input of the listed rows: the embedding of the row's token.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void embed_kernel(int B, int L, int d, int V, const int32_t* __restrict__ idx,
+                             const int32_t* __restrict__ n, const int32_t* __restrict__ tokens,
+                             const T* __restrict__ embed, T* __restrict__ h0) {
+  int b, i;
+  if (!row_of(idx, n, B, L, blockIdx.x, b, i)) return;
+  const int tok = tokens[(size_t)b * L + i];
+  T* dst = h0 + ((size_t)b * L + i) * d;
+  if (tok < 0 || tok >= V) {
+    for (int c = threadIdx.x; c < d; c += blockDim.x) dst[c] = T(0);
+    return;
+  }
+  const T* src = embed + (size_t)tok * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) dst[c] = src[c];
+}
+
+hipError_t launch_embed(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, int V,
+                        const int32_t* idx, const int32_t* n, const int32_t* tokens, const void* embed,
+                        void* h0) {
+  if (max_rows <= 0) return hipSuccess;
+  if (bf16m)
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, V, idx, n, tokens,
+                       (const bf16*)embed, (bf16*)h0);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, V, idx, n, tokens,
+                       (const float*)embed, (float*)h0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Gather + RMSNorm (fp32 statistics) of the selected rows into compact A.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void gather_norm_kernel(int B, int L, int d, float eps,
+                                                          const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ n,
+                                                          const T* __restrict__ H, const float* __restrict__ g,
+                                                          T* __restrict__ A) {
+  __shared__ float red[4];
+  int b, i;
+  const int m = blockIdx.x;
+  if (!row_of(idx, n, B, L, m, b, i)) return;
+  const T* x = H + ((size_t)b * L + i) * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = io<T>::ld(x + c);
+    ss += v * v;
+  }
+  ss = block_sum<4>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  T* a = A + (size_t)m * d;
+  for (int c = threadIdx.x; c < d; c += 256) io<T>::st(a + c, io<T>::ld(x + c) * inv * g[c]);
+}
+
+hipError_t launch_gather_norm(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, float eps,
+                              const int32_t* idx, const int32_t* n, const void* H, const float* g,
+                              void* A) {
+  if (max_rows <= 0) return hipSuccess;
+  if (bf16m)
+    hipLaunchKernelGGL(gather_norm_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, eps, idx, n,
+                       (const bf16*)H, g, (bf16*)A);
+  else
+    hipLaunchKernelGGL(gather_norm_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, eps, idx, n,
+                       (const float*)H, g, (float*)A);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// QKV epilogue: sum split partials, rotate-half RoPE on q and k at the row's
+// position (cos/sin tables [L][dh/2]), write q (compact) and scatter k, v into
+// the cache rows [b][g][i][:].
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq, int Hkv, int dh, int S, int cap,
+                                                           const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ n,
+                                                           const float* __restrict__ part,
+                                                           const float* __restrict__ rc,
+                                                           const float* __restrict__ rs, T* __restrict__ q,
+                                                           T* __restrict__ Kc, T* __restrict__ Vc) {
+  int b, i;
+  const int m = blockIdx.x;
+  if (!row_of(idx, n, B, L, m, b, i)) return;
+  const int M = total_rows(n, B, cap);
+  const int nq = Hq * dh, nv = Hkv * dh, N = nq + 2 * nv, half = dh / 2;
+  const size_t sstride = (size_t)M * N;
+  const float* p0 = part + (size_t)m * N;
+  auto val = [&](int c) {
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += p0[s * sstride + c];
+    return v;
+  };
+  const int npairs = (Hq + Hkv) * half;
+  for (int p = threadIdx.x; p < npairs; p += 256) {
+    const int head = p / half, j = p - head * half;
+    const int c0 = head * dh + j, c1 = c0 + half;
+    const float a = val(c0), c = val(c1);
+    const float cs = rc[(size_t)i * half + j], sn = rs[(size_t)i * half + j];
+    const float r0 = a * cs - c * sn, r1 = c * cs + a * sn;
+    if (head < Hq) {
+      io<T>::st(q + (size_t)m * nq + c0, r0);
+      io<T>::st(q + (size_t)m * nq + c1, r1);
+    } else {
+      T* kr = Kc + (((size_t)b * Hkv + (head - Hq)) * L + i) * dh;
+      io<T>::st(kr + j, r0);
+      io<T>::st(kr + j + half, r1);
+    }
+  }
+  for (int c = threadIdx.x; c < nv; c += 256) {
+    const int g = c / dh, t = c - g * dh;
+    io<T>::st(Vc + (((size_t)b * Hkv + g) * L + i) * dh + t, val(nq + nv + c));
+  }
+}
+
+hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, int L, int Hq, int Hkv,
+                               int dh, int S, const int32_t* idx, const int32_t* n, const float* part,
+                               const float* rope_cos, const float* rope_sin, void* q_out, void* Kc,
+                               void* Vc) {
+  if (max_rows <= 0) return hipSuccess;
+  if (bf16m)
+    hipLaunchKernelGGL(qkv_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, Hq, Hkv, dh, S, max_rows,
+                       idx, n, part, rope_cos, rope_sin, (bf16*)q_out, (bf16*)Kc, (bf16*)Vc);
+  else
+    hipLaunchKernelGGL(qkv_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, Hq, Hkv, dh, S, max_rows,
+                       idx, n, part, rope_cos, rope_sin, (float*)q_out, (float*)Kc, (float*)Vc);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Output projection epilogue: h' = x + o W_o (fp32), then the FFN norm.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, int S, int cap, float eps,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ n,
+                                                         const float* __restrict__ part,
+                                                         const T* __restrict__ H, const float* __restrict__ g2,
+                                                         float* __restrict__ hprime, T* __restrict__ A2) {
+  __shared__ float red[4];
+  int b, i;
+  const int m = blockIdx.x;
+  if (!row_of(idx, n, B, L, m, b, i)) return;
+  const int M = total_rows(n, B, cap);
+  const size_t sstride = (size_t)M * d;
+  const T* x = H + ((size_t)b * L + i) * d;
+  float* hp = hprime + (size_t)m * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = io<T>::ld(x + c);
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) acc += part[s * sstride + (size_t)m * d + c];
+    v += acc;
+    hp[c] = v;
+    ss += v * v;
+  }
+  ss = block_sum<4>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  T* a = A2 + (size_t)m * d;
+  for (int c = threadIdx.x; c < d; c += 256) io<T>::st(a + c, hp[c] * inv * g2[c]);
+}
+
+hipError_t launch_o_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, int S,
+                             float eps, const int32_t* idx, const int32_t* n, const float* part,
+                             const void* H, const float* g2, float* hprime, void* A2) {
+  if (max_rows <= 0) return hipSuccess;
+  if (bf16m)
+    hipLaunchKernelGGL(o_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, idx, n,
+                       part, (const bf16*)H, g2, hprime, (bf16*)A2);
+  else
+    hipLaunchKernelGGL(o_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, idx, n,
+                       part, (const float*)H, g2, hprime, (float*)A2);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU: act = SiLU(gate) * up.  The fused gate|up weight interleaves the
+// two by 32-column tiles: packed tile 2t is gate tile t, tile 2t+1 is up tile t.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_kernel(int B, int F, int S, int cap, const int32_t* __restrict__ n,
+                                                     const float* __restrict__ part, T* __restrict__ act) {
+  const int M = total_rows(n, B, cap);
+  const int m = blockIdx.y;
+  if (m >= M) return;
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= F) return;
+  const int N = 2 * F;
+  const size_t sstride = (size_t)M * N;
+  const int cg = (f >> 5) * 64 + (f & 31);
+  float gv = 0.f, uv = 0.f;
+  for (int s = 0; s < S; ++s) {
+    gv += part[s * sstride + (size_t)m * N + cg];
+    uv += part[s * sstride + (size_t)m * N + cg + 32];
+  }
+  const float sl = gv / (1.0f + expf(-gv));
+  io<T>::st(act + (size_t)m * F + f, sl * uv);
+}
+
+hipError_t launch_swiglu(hipStream_t st, bool bf16m, int max_rows, int B, int F, int S, const int32_t* n,
+                         const float* part, void* act) {
+  if (max_rows <= 0) return hipSuccess;
+  dim3 grid((F + 255) / 256, max_rows);
+  if (bf16m)
+    hipLaunchKernelGGL(swiglu_kernel<bf16>, grid, dim3(256), 0, st, B, F, S, max_rows, n, part, (bf16*)act);
+  else
+    hipLaunchKernelGGL(swiglu_kernel<float>, grid, dim3(256), 0, st, B, F, S, max_rows, n, part, (float*)act);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Down-projection epilogue: out = h' + act W_down, written back at the row's
+// slot of the next layer's input; the row's proxy reference is refreshed.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void down_epilogue_kernel(int B, int L, int d, int r, int S, int cap,
+                                                            const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ n,
+                                                            const float* __restrict__ part,
+                                                            const float* __restrict__ hprime,
+                                                            T* __restrict__ Hout, const double* __restrict__ pcur,
+                                                            double* __restrict__ pref, double* __restrict__ score) {
+  int b, i;
+  const int m = blockIdx.x;
+  if (!row_of(idx, n, B, L, m, b, i)) return;
+  const int M = total_rows(n, B, cap);
+  const size_t sstride = (size_t)M * d;
+  const size_t row = (size_t)b * L + i;
+  T* o = Hout + row * d;
+  const float* hp = hprime + (size_t)m * d;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) acc += part[s * sstride + (size_t)m * d + c];
+    io<T>::st(o + c, hp[c] + acc);
+  }
+  for (int j = threadIdx.x; j < r; j += 256) pref[row * r + j] = pcur[row * r + j];
+  if (threadIdx.x == 0) score[row] = 0.0;
+}
+
+hipError_t launch_down_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, int r,
+                                int S, const int32_t* idx, const int32_t* n, const float* part,
+                                const float* hprime, void* H_out, const double* pcur, double* pref,
+                                double* score) {
+  if (max_rows <= 0) return hipSuccess;
+  if (bf16m)
+    hipLaunchKernelGGL(down_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, r, S, max_rows, idx, n,
+                       part, hprime, (bf16*)H_out, pcur, pref, score);
+  else
+    hipLaunchKernelGGL(down_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, r, S, max_rows, idx, n,
+                       part, hprime, (float*)H_out, pcur, pref, score);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

@@ -1,0 +1,116 @@
+"""Device-side model and decode-state helpers over the C-ABI.
+
+``Model`` creates a libdllm model and hands it the (seeded, synthetic)
+weights; ``State`` allocates the caller-owned decode state as torch tensors in
+the layouts include/libdllm.h documents.  Nothing here computes any part of
+the decoding step.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import torch
+
+from . import binding as B
+from . import inputs
+from .configs import BF16, FP32, Config, FORCED_BLOCK, FORCED_BLOCK_RECENT, FORCED_NONE
+
+FORCED_RULE = {FORCED_NONE: B.DLLM_FORCED_NONE, FORCED_BLOCK: B.DLLM_FORCED_BLOCK,
+               FORCED_BLOCK_RECENT: B.DLLM_FORCED_BLOCK_RECENT}
+
+
+def dims_of(cfg: Config, max_batch: Optional[int] = None) -> B.DllmDims:
+    return B.DllmDims(
+        cfg.n_layers, cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.d_ffn, cfg.vocab,
+        max_batch or cfg.batch, cfg.seq_len, cfg.block_len, cfg.proxy_rank,
+        B.DLLM_FP32 if cfg.dtype == FP32 else B.DLLM_BF16, cfg.rms_eps, cfg.rope_theta)
+
+
+class Model:
+    """A libdllm model holding one config's weights (library-owned copies)."""
+
+    def __init__(self, cfg: Config, device="cuda", gain_std: float = 0.0,
+                 layers: Optional[List[Dict[str, torch.Tensor]]] = None,
+                 head: Optional[Dict[str, torch.Tensor]] = None, max_batch: Optional[int] = None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.h = B.dllm_create(dims_of(cfg, max_batch))
+        for l in range(cfg.n_layers):
+            w = layers[l] if layers is not None else inputs.layer_weights(cfg, l, self.device, gain_std)
+            w = {k: v.to(self.device).contiguous() for k, v in w.items()}
+            B.dllm_init_layer(self.h, l, w)
+            torch.cuda.current_stream().synchronize()
+            del w
+        hw = head if head is not None else inputs.head_weights(cfg, self.device, gain_std)
+        hw = {k: v.to(self.device).contiguous() for k, v in hw.items()}
+        B.dllm_init_head(self.h, hw["embed"], hw["final_norm"], hw["lm_head"])
+        torch.cuda.current_stream().synchronize()
+
+    def close(self):
+        if self.h:
+            B.dllm_destroy(self.h)
+            self.h = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def first_block(committed: torch.Tensor, block_len: int) -> torch.Tensor:
+    """First row of the first block that still holds a masked row, per sequence."""
+    c = committed.to("cpu", torch.bool)
+    Bn, L = c.shape
+    out = torch.empty(Bn, dtype=torch.int32)
+    for b in range(Bn):
+        bs = 0
+        while bs < L and bool(c[b, bs:bs + block_len].all()):
+            bs += block_len
+        out[b] = bs
+    return out
+
+
+class State:
+    """Caller-owned decode state on the device."""
+
+    def __init__(self, cfg: Config, batch: Optional[int] = None, device="cuda", tokens=None, committed=None):
+        self.cfg = cfg
+        dev = torch.device(device)
+        Bn = batch or cfg.batch
+        N, L, d, r = cfg.n_layers, cfg.seq_len, cfg.d_model, cfg.proxy_rank
+        dt = inputs.storage_dtype(cfg)
+        self.hidden = torch.zeros((N + 1, Bn, L, d), dtype=dt, device=dev)
+        self.k_cache = torch.zeros((N, Bn, cfg.n_kv_heads, L, cfg.head_dim), dtype=dt, device=dev)
+        self.v_cache = torch.zeros_like(self.k_cache)
+        self.proxy_cur = torch.zeros((N, Bn, L, r), dtype=torch.float64, device=dev)
+        self.proxy_ref = torch.zeros_like(self.proxy_cur)
+        self.score = torch.zeros((N, Bn, L), dtype=torch.float64, device=dev)
+        if tokens is None:
+            tokens, committed = inputs.prompt_tokens(cfg.with_(batch=Bn))
+        self.tokens = tokens.to(dev, torch.int32).contiguous()
+        self.committed = committed.to(dev, torch.uint8).contiguous()
+        self.history = torch.full((Bn, L), -1, dtype=torch.int32, device=dev)
+        self.n_history = torch.zeros(Bn, dtype=torch.int32, device=dev)
+        self.n_new = torch.zeros(Bn, dtype=torch.int32, device=dev)
+        self.block_start = first_block(self.committed, cfg.block_len).to(dev)
+        self.full_next = torch.ones(Bn, dtype=torch.uint8, device=dev)
+        self.max_entropy = torch.zeros(Bn, dtype=torch.float64, device=dev)
+        self.batch = Bn
+        self.c = B.DllmState(*[t.data_ptr() for t in (
+            self.hidden, self.k_cache, self.v_cache, self.proxy_cur, self.proxy_ref, self.score, self.tokens,
+            self.committed, self.history, self.n_history, self.n_new, self.block_start, self.full_next,
+            self.max_entropy)], Bn)
+
+    def tensors(self) -> Dict[str, torch.Tensor]:
+        return {k: getattr(self, k) for k in (
+            "hidden", "k_cache", "v_cache", "proxy_cur", "proxy_ref", "score", "tokens", "committed",
+            "history", "n_history", "n_new", "block_start", "full_next", "max_entropy")}
+
+
+def step(model: Model, state: State, mode: int = B.DLLM_MODE_AUTO, want_result: bool = True, stream=None,
+         tau: Optional[float] = None):
+    cfg = model.cfg
+    return B.dllm_step(model.h, state, mode, FORCED_RULE[cfg.forced], cfg.recent_k,
+                       cfg.tau if tau is None else tau, cfg.conf_threshold, cfg.rho, want_result, stream)
