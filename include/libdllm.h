@@ -62,7 +62,7 @@ enum { DLLM_FORCED_NONE = 0, DLLM_FORCED_BLOCK = 1, DLLM_FORCED_BLOCK_RECENT = 2
 
 /* Model and sequence dimensions.  Limits checked by dllm_create:
  * head_dim even and <= 256; n_q_heads a multiple of n_kv_heads;
- * seq_len <= 8192; block_len <= 64; proxy_rank <= 128; for DLLM_BF16 the
+ * seq_len <= 8192 and a multiple of 4; block_len <= 64; proxy_rank <= 128; for DLLM_BF16 the
  * widths d_model, d_ffn, n_q_heads*head_dim, n_kv_heads*head_dim and vocab
  * must be multiples of 32 and d_model, d_ffn multiples of 64. */
 typedef struct {
@@ -97,7 +97,8 @@ typedef struct {
 typedef struct {
   void *hidden;         /* [N+1][B][L][d_model]: slot 0 = embeddings, slot l+1 = layer l output */
   void *k_cache;        /* [N][B][n_kv_heads][L][head_dim] (post-RoPE keys) */
-  void *v_cache;        /* [N][B][n_kv_heads][L][head_dim] */
+  void *v_cache;        /* [N][B][n_kv_heads][L/4][head_dim][4]: value of key j,
+                         * dimension t at [j/4][t][j%4] (four keys adjacent) */
   double *proxy_cur;    /* [N][B][L][r]  current proxy C of each row's layer input */
   double *proxy_ref;    /* [N][B][L][r]  proxy P at the row's last refresh */
   double *score;        /* [N][B][L]     drift of C against P (0 for refreshed rows) */
@@ -216,6 +217,26 @@ dllm_status dllm_forced_set(dllm_model *m, const dllm_state *s, int32_t rule, in
  * empty).  If res_h is non-NULL the call waits for the stream and fills it. */
 dllm_status dllm_step(dllm_model *m, dllm_state *s, const dllm_step_params *p,
                       dllm_step_result *res_h, void *stream);
+
+/* Diagnostics: live timing of kernel classes.  While enabled, the library
+ * records a HIP event pair on the launch stream around every launch of the
+ * class's kernels, together with the launch's algorithmic bytes and flops
+ * (weights + activations read, outputs written; split-K partials are not
+ * counted).  dllm_profile_read waits for the recorded events, writes
+ * DLLM_PROF_N entries to stats_h and clears them. */
+enum { DLLM_PROF_GEMM = 0,    /* layer GEMMs (QKV, O, gate|up, down) */
+       DLLM_PROF_LMHEAD = 1,  /* LM-head GEMM */
+       DLLM_PROF_ATTN = 2,    /* attention */
+       DLLM_PROF_PROXY = 3,   /* value proxy + drift */
+       DLLM_PROF_N = 4 };
+typedef struct {
+  int64_t launches;
+  double ms;      /* sum of event-pair durations */
+  double bytes;   /* sum of algorithmic bytes */
+  double flops;   /* sum of algorithmic flops */
+} dllm_kernel_stats;
+dllm_status dllm_profile(dllm_model *m, int32_t enable);
+dllm_status dllm_profile_read(dllm_model *m, dllm_kernel_stats *stats_h);
 
 #ifdef __cplusplus
 }

@@ -50,6 +50,14 @@ class DllmStepResult(ctypes.Structure):
     _fields_ = [("n_full", _i32), ("n_committed", _i32), ("n_active", _i32), ("max_entropy", _f64)]
 
 
+DLLM_PROF_GEMM, DLLM_PROF_LMHEAD, DLLM_PROF_ATTN, DLLM_PROF_PROXY, DLLM_PROF_N = 0, 1, 2, 3, 4
+PROF_NAMES = ("gemm", "lm_head", "attention", "proxy")
+
+
+class DllmKernelStats(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("ms", _f64), ("bytes", _f64), ("flops", _f64)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "dllm_last_error": (ctypes.c_char_p, []),
@@ -66,6 +74,8 @@ SIGNATURES = {
     "dllm_forced_set": (_i32, [_vp, ctypes.POINTER(DllmState), _i32, _i32, _vp, _vp]),
     "dllm_step": (_i32, [_vp, ctypes.POINTER(DllmState), ctypes.POINTER(DllmStepParams),
                          ctypes.POINTER(DllmStepResult), _vp]),
+    "dllm_profile": (_i32, [_vp, _i32]),
+    "dllm_profile_read": (_i32, [_vp, ctypes.POINTER(DllmKernelStats)]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -180,5 +190,12 @@ def dllm_step(m: int, state, mode: int, forced_rule: int, recent_k: int, tau: fl
     return res
 
 
-def inf() -> float:
-    return math.inf
+def dllm_profile(m: int, enable: bool):
+    _check(lib().dllm_profile(m, 1 if enable else 0))
+
+
+def dllm_profile_read(m: int) -> dict:
+    arr = (DllmKernelStats * DLLM_PROF_N)()
+    _check(lib().dllm_profile_read(m, arr))
+    return {PROF_NAMES[i]: {"launches": arr[i].launches, "ms": arr[i].ms, "bytes": arr[i].bytes,
+                            "flops": arr[i].flops} for i in range(DLLM_PROF_N)}

@@ -71,6 +71,8 @@ struct dllm_model {
   // workspace
   int M_cap = 0;   // max_batch * seq_len
   int M_pad = 0;   // rows allocated in activation buffers
+  int MTt = 0;     // 32-row tiles of the packed GEMM inputs (M_pad / 32)
+  int lm_MTt = 0;  // same for the LM-head input
   void* A1 = nullptr;
   void* q = nullptr;
   void* attn_o = nullptr;
@@ -98,6 +100,16 @@ struct dllm_model {
   void* res_host = nullptr;   // pinned, 32 bytes
   uint8_t* full_host = nullptr;  // pinned, max_batch
   std::vector<void*> allocs;
+  // diagnostics
+  struct ProfRec {
+    hipEvent_t a, b;
+    int cls;
+    double bytes, flops;
+  };
+  bool prof_on = false;
+  std::vector<ProfRec> prof_pending;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<hipEvent_t> ev_all;
 
   dllm_status alloc(void** p, size_t bytes) {
     if (bytes == 0) bytes = 16;
@@ -123,6 +135,41 @@ struct dllm_model {
 namespace {
 
 inline hipStream_t S(void* stream) { return (hipStream_t)stream; }
+
+// Event pair around a group of launches of one kernel class (diagnostics).
+struct Prof {
+  dllm_model* m;
+  hipStream_t st;
+  int cls;
+  double bytes, flops;
+  hipEvent_t a = nullptr;
+  static hipEvent_t get(dllm_model* m) {
+    if (!m->ev_pool.empty()) {
+      hipEvent_t e = m->ev_pool.back();
+      m->ev_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    m->ev_all.push_back(e);
+    return e;
+  }
+  Prof(dllm_model* m_, hipStream_t st_, int cls_, double bytes_, double flops_)
+      : m(m_), st(st_), cls(cls_), bytes(bytes_), flops(flops_) {
+    if (m->prof_on) {
+      a = get(m);
+      if (a) (void)hipEventRecord(a, st);
+    }
+  }
+  void done() {
+    if (!a) return;
+    hipEvent_t b = get(m);
+    if (!b) return;
+    (void)hipEventRecord(b, st);
+    m->prof_pending.push_back({a, b, cls, bytes, flops});
+    a = nullptr;
+  }
+};
 
 int nq_of(const dllm_dims& d) { return d.n_q_heads * d.head_dim; }
 int nv_of(const dllm_dims& d) { return d.n_kv_heads * d.head_dim; }
@@ -177,18 +224,24 @@ int clamp_rows(const dllm_model* m, const dllm_state* s, int max_rows) {
 
 // out = A W (partials into `out`, split count returned)
 dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int N, const void* A, const void* W,
-                 const int32_t* n_sel, float* out, size_t out_floats, int* splits) {
+                 const int32_t* n_sel, float* out, size_t out_floats, int* splits, int cls = DLLM_PROF_GEMM,
+                 int MTt = -1, void* act = nullptr) {
+  if (MTt < 0) MTt = m->MTt;
+  Prof prof(m, st, cls, (double)K * N * m->esize + (double)max_rows * K * m->esize + (double)max_rows * N * 4.0,
+            2.0 * max_rows * (double)K * N);
   if (m->bf16) {
-    int sp = gemm_bf16_pick_splits(max_rows, K, N, m->n_cu);
+    int sp = act ? 1 : gemm_bf16_pick_splits(max_rows, K, N, m->n_cu);
     while (sp > 1 && (size_t)sp * max_rows * N > out_floats) sp /= 2;
-    if ((size_t)sp * max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
-    HIPCHK(launch_gemm_bf16(st, max_rows, B, K, N, (const uint16_t*)A, (const uint16_t*)W, n_sel, out, sp));
+    if (!act && (size_t)sp * max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
+    HIPCHK(launch_gemm_bf16(st, max_rows, B, K, N, (const uint16_t*)A, MTt, (const uint16_t*)W, n_sel, out, sp,
+                            (uint16_t*)act, m->MTt));
     *splits = sp;
   } else {
     if ((size_t)max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
     HIPCHK(launch_gemm_f32(st, max_rows, B, K, N, (const float*)A, (const float*)W, n_sel, out));
     *splits = 1;
   }
+  prof.done();
   return DLLM_OK;
 }
 
@@ -204,9 +257,14 @@ dllm_status pack(dllm_model* m, hipStream_t st, int K, int Nsrc, const void* src
 dllm_status do_drift(dllm_model* m, int layer, dllm_state* s, const int32_t* rows, const int32_t* n, int max_rows,
                      hipStream_t st) {
   const dllm_dims& d = m->d;
+  Prof prof(m, st, DLLM_PROF_PROXY,
+            (double)max_rows * d.d_model * m->esize + (double)d.d_model * d.proxy_rank * 8.0 +
+                (double)max_rows * d.proxy_rank * 8.0 * 3.0,
+            2.0 * max_rows * (double)d.d_model * d.proxy_rank);
   HIPCHK(launch_proxy_drift(st, m->bf16, max_rows, s->batch, d.seq_len, d.d_model, d.proxy_rank, rows, n,
                             hid(m, s, layer), m->layers[layer].w_proxy, m->ppart, pcur(m, s, layer),
                             pref(m, s, layer), score(m, s, layer)));
+  prof.done();
   return DLLM_OK;
 }
 
@@ -218,17 +276,29 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
   const LayerW& w = m->layers[layer];
   const void* Hin = hid(m, s, layer);
   int sp = 1;
-  HIPCHK(launch_gather_norm(st, m->bf16, max_rows, B, L, D, d.rms_eps, idx, n, Hin, w.attn_norm, m->A1));
+  HIPCHK(launch_gather_norm(st, m->bf16, max_rows, B, L, D, d.rms_eps, m->MTt, idx, n, Hin, w.attn_norm, m->A1));
   CHK(gemm(m, st, max_rows, B, D, nq + 2 * nv, m->A1, w.w_qkv, n, m->part, m->part_floats, &sp));
   HIPCHK(launch_qkv_epilogue(st, m->bf16, max_rows, B, L, d.n_q_heads, d.n_kv_heads, d.head_dim, sp, idx, n,
                              m->part, m->rope_cos, m->rope_sin, m->q, kcache(m, s, layer), vcache(m, s, layer)));
-  HIPCHK(launch_attention(st, m->bf16, max_rows, B, L, d.n_q_heads, d.n_kv_heads, d.head_dim, idx, n, m->q,
-                          kcache(m, s, layer), vcache(m, s, layer), m->attn_part, m->attn_o));
+  {
+    Prof prof(m, st, DLLM_PROF_ATTN,
+              2.0 * B * L * nv * m->esize + 2.0 * max_rows * nq * m->esize,
+              4.0 * max_rows * (double)L * nq);
+    HIPCHK(launch_attention(st, m->bf16, max_rows, B, L, d.n_q_heads, d.n_kv_heads, d.head_dim, idx, n, m->q,
+                            kcache(m, s, layer), vcache(m, s, layer), m->attn_part, m->attn_o, m->MTt));
+    prof.done();
+  }
   CHK(gemm(m, st, max_rows, B, nq, D, m->attn_o, w.w_o, n, m->part, m->part_floats, &sp));
-  HIPCHK(launch_o_epilogue(st, m->bf16, max_rows, B, L, D, sp, d.rms_eps, idx, n, m->part, Hin, w.ffn_norm,
-                           m->hprime, m->A2));
-  CHK(gemm(m, st, max_rows, B, D, 2 * F, m->A2, w.w_gu, n, m->part, m->part_floats, &sp));
-  HIPCHK(launch_swiglu(st, m->bf16, max_rows, B, F, sp, n, m->part, m->act));
+  HIPCHK(launch_o_epilogue(st, m->bf16, max_rows, B, L, D, sp, d.rms_eps, m->MTt, idx, n, m->part, Hin,
+                           w.ffn_norm, m->hprime, m->A2));
+  if (m->bf16) {
+    // SwiGLU fused into the gate|up GEMM
+    CHK(gemm(m, st, max_rows, B, D, 2 * F, m->A2, w.w_gu, n, m->part, m->part_floats, &sp, DLLM_PROF_GEMM, m->MTt,
+             m->act));
+  } else {
+    CHK(gemm(m, st, max_rows, B, D, 2 * F, m->A2, w.w_gu, n, m->part, m->part_floats, &sp));
+    HIPCHK(launch_swiglu(st, m->bf16, max_rows, B, F, sp, n, m->part, m->act));
+  }
   CHK(gemm(m, st, max_rows, B, F, D, m->act, w.w_down, n, m->part, m->part_floats, &sp));
   HIPCHK(launch_down_epilogue(st, m->bf16, max_rows, B, L, D, d.proxy_rank, sp, idx, n, m->part, m->hprime,
                               hid(m, s, layer + 1), pcur(m, s, layer), pref(m, s, layer), score(m, s, layer)));
@@ -238,15 +308,20 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
 dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st) {
   const dllm_dims& d = m->d;
   const int B = s->batch, blk = d.block_len;
-  HIPCHK(launch_lm_gather(st, m->bf16, B, d.seq_len, blk, d.d_model, d.rms_eps, s->block_start,
+  HIPCHK(launch_lm_gather(st, m->bf16, B, d.seq_len, blk, d.d_model, d.rms_eps, m->lm_MTt, s->block_start,
                           hid(m, s, d.n_layers), m->final_norm, m->A_lm, m->lm_rows));
   int sp = 1;
   const size_t cap = (size_t)d.max_batch * blk * d.vocab;
   if (m->bf16) {
-    HIPCHK(launch_gemm_bf16(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm,
-                            (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1));
+    Prof prof(m, st, DLLM_PROF_LMHEAD,
+              (double)d.d_model * d.vocab * 2.0 + (double)B * blk * d.d_model * 2.0 + (double)B * blk * d.vocab * 4.0,
+              2.0 * B * blk * (double)d.d_model * d.vocab);
+    HIPCHK(launch_gemm_bf16(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
+                            (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0));
+    prof.done();
   } else {
-    CHK(gemm(m, st, B * blk, 1, d.d_model, d.vocab, m->A_lm, m->lm_head, m->lm_rows, m->logits, cap, &sp));
+    CHK(gemm(m, st, B * blk, 1, d.d_model, d.vocab, m->A_lm, m->lm_head, m->lm_rows, m->logits, cap, &sp,
+             DLLM_PROF_LMHEAD));
   }
   HIPCHK(launch_lm_stats(st, B * blk, d.vocab, m->logits, m->lm_part, m->lm_stats, m->lm_slabs));
   return DLLM_OK;
@@ -277,6 +352,7 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   if (d.head_dim % 2 || d.head_dim > 256) return fail(DLLM_E_SHAPE, "head_dim must be even and <= 256");
   if (d.n_q_heads % d.n_kv_heads) return fail(DLLM_E_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
   if (d.seq_len > 8192) return fail(DLLM_E_SHAPE, "seq_len %d > 8192", d.seq_len);
+  if (d.seq_len % 4) return fail(DLLM_E_SHAPE, "seq_len must be a multiple of 4");
   if (d.block_len > 64) return fail(DLLM_E_SHAPE, "block_len %d > 64", d.block_len);
   if (d.proxy_rank > 128 || d.proxy_rank > d.d_model) return fail(DLLM_E_SHAPE, "proxy_rank must be <= 128 and <= d_model");
   if (d.d_model % 32 || d.d_ffn % 32) return fail(DLLM_E_SHAPE, "d_model and d_ffn must be multiples of 32");
@@ -304,6 +380,7 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   const int L = d.seq_len, D = d.d_model, F = d.d_ffn;
   m->M_cap = d.max_batch * L;
   m->M_pad = (m->M_cap + 31) / 32 * 32 + 32;
+  m->MTt = m->M_pad / 32;
   const size_t es = m->esize;
   dllm_status st;
 #define ALLOC(ptr, bytes)                         \
@@ -338,7 +415,8 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   ALLOC(m->forced, (size_t)m->M_cap);
   ALLOC(m->step_full, (size_t)d.max_batch);
   const int lm_rows_cap = d.max_batch * d.block_len;
-  ALLOC(m->A_lm, (size_t)(lm_rows_cap + 32) * D * es);
+  m->lm_MTt = (lm_rows_cap + 31) / 32 + 1;
+  ALLOC(m->A_lm, (size_t)m->lm_MTt * 32 * D * es);
   ALLOC(m->logits, (size_t)lm_rows_cap * d.vocab * 4);
   m->lm_slabs = lm_stats_slabs(d.vocab);
   ALLOC(m->lm_part, (size_t)lm_rows_cap * m->lm_slabs * 4 * 8);
@@ -375,6 +453,7 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
 dllm_status dllm_destroy(dllm_model* m) {
   if (!m) return DLLM_OK;
   (void)hipDeviceSynchronize();
+  for (hipEvent_t e : m->ev_all) (void)hipEventDestroy(e);
   for (void* p : m->allocs) (void)hipFree(p);
   if (m->res_host) (void)hipHostFree(m->res_host);
   if (m->full_host) (void)hipHostFree(m->full_host);
@@ -582,6 +661,32 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     res_h->n_active = r[2];
     std::memcpy(&res_h->max_entropy, r + 4, 8);
   }
+  return DLLM_OK;
+}
+
+dllm_status dllm_profile(dllm_model* m, int32_t enable) {
+  CHK(check_model(m));
+  m->prof_on = enable != 0;
+  return DLLM_OK;
+}
+
+dllm_status dllm_profile_read(dllm_model* m, dllm_kernel_stats* stats_h) {
+  CHK(check_model(m));
+  if (!stats_h) return fail(DLLM_E_ARG, "stats_h is NULL");
+  for (int c = 0; c < DLLM_PROF_N; ++c) stats_h[c] = dllm_kernel_stats{0, 0.0, 0.0, 0.0};
+  for (auto& r : m->prof_pending) {
+    HIPCHK(hipEventSynchronize(r.b));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, r.a, r.b));
+    dllm_kernel_stats& k = stats_h[r.cls];
+    k.launches += 1;
+    k.ms += ms;
+    k.bytes += r.bytes;
+    k.flops += r.flops;
+    m->ev_pool.push_back(r.a);
+    m->ev_pool.push_back(r.b);
+  }
+  m->prof_pending.clear();
   return DLLM_OK;
 }
 

@@ -85,4 +85,51 @@ __device__ __forceinline__ F block_sum(F v, F* red) {
   return t;
 }
 
+// Packed activation layout (bf16 GEMM inputs).  A row-major [M][K] operand is
+// stored as 32x16 MFMA A-fragments: fragment (kt = k/16, mt = m/32) occupies
+// 1 KB at ((kt * MTt + mt) * 64 + lane) * 8 elements, where MTt is the number
+// of 32-row tiles the buffer holds and lane = m%32 + 32*((k%16)/8) holds the 8
+// consecutive k of its row.  A wave loads one fragment with one 16-byte load
+// per lane, and a wave's row tiles for one k-step are contiguous.
+__device__ __forceinline__ size_t apack_off(int m, int k, int MTt) {
+  const int kt = k >> 4, mt = m >> 5, lane = (m & 31) + ((k >> 3) & 1) * 32;
+  return (((size_t)kt * MTt + mt) * 64 + lane) * 8 + (k & 7);
+}
+
+// Store 8 consecutive values of row m starting at column k8 (a multiple of 8)
+// of a GEMM input: packed fragments for bf16 (one 16-byte store), row-major
+// [..][ld] for fp32.
+__device__ __forceinline__ void store_a8(bf16* A, int m, int k8, int MTt, int /*ld*/, const float* v) {
+  uint4 w;
+  w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  w.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  w.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  *reinterpret_cast<uint4*>(A + apack_off(m, k8, MTt)) = w;
+}
+__device__ __forceinline__ void store_a8(float* A, int m, int k8, int /*MTt*/, int ld, const float* v) {
+  float* p = A + (size_t)m * ld + k8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = v[j];
+}
+// One element of a GEMM input (packed for bf16).
+__device__ __forceinline__ void store_a1(bf16* A, int m, int k, int MTt, int, float v) { A[apack_off(m, k, MTt)] = f2bf(v); }
+__device__ __forceinline__ void store_a1(float* A, int m, int k, int, int ld, float v) { A[(size_t)m * ld + k] = v; }
+
+// Sum of S split partials p[s * stride] in split order, loads issued in
+// batches of 8 so they overlap.
+template <typename F>
+__device__ __forceinline__ F sum_splits(const F* __restrict__ p, size_t stride, int S) {
+  F acc = F(0);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    F v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (s0 + j < S) ? p[(size_t)(s0 + j) * stride] : F(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) acc += v[j];
+  }
+  return acc;
+}
+
 }  // namespace dllm

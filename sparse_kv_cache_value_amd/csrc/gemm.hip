@@ -79,16 +79,26 @@ hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, in
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM.
+//
+// Workgroup = 4 waves, a 128-column slab (4 column tiles of 32) and a row
+// block of 4*MTW row tiles; wave w owns row tiles w, w+4, ... of the block and
+// all 4 column tiles, so each A fragment it loads (straight from the packed
+// activations, 16 B per lane) feeds 4 MFMAs.  The slab's weight fragments are
+// loaded once per workgroup (wave w loads column tile w) and shared through a
+// double-buffered LDS stage.  Both operands are prefetched two chunks ahead in
+// registers, so the HBM weight stream overlaps the MFMAs of earlier chunks.
+// EPI 0 writes fp32 split-K partials out[split][m][n]; EPI 1 (one split)
+// applies SwiGLU to interleaved gate/up column tiles and writes the packed bf16
+// activation of the next GEMM.
 // ---------------------------------------------------------------------------
-template <int MT, int KS>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                           const uint16_t* __restrict__ Wp,
-                                                           float* __restrict__ out,
+template <int MTW, int KS, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const u32x4* __restrict__ Ap, int MTt,
+                                                           const u32x4* __restrict__ Wp, float* __restrict__ out,
+                                                           uint16_t* __restrict__ act, int MTt_out,
                                                            const int32_t* __restrict__ n_sel, int B, int K, int N,
                                                            int kps, int row_blocks, int n_slabs, int total, int cap) {
-  extern __shared__ u32x4 lds[];
-  constexpr int BUF = MT * KS * 64;           // 16-byte entries per buffer
-  constexpr int PPT = (MT * KS * 64) / 256;   // A pieces per thread
+  extern __shared__ u32x4 wl[];  // [2][KS][4][64]
+  constexpr int WBUF = KS * 4 * 64;
   const int G = gridDim.x;
   const int w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   if (w >= total) return;
@@ -97,140 +107,172 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
   const int rb = t2 % row_blocks;
   const int split = t2 / row_blocks;
   const int M = total_rows(n_sel, B, cap);
-  const int r0 = rb * 32 * MT;
-  if (r0 >= M) return;
-  const int mt_n = min(MT, (M - r0 + 31) >> 5);
-  const int rows_n = mt_n * 32;
+  const int mt_base = rb * 4 * MTW;
+  if (mt_base * 32 >= M) return;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int nt = slab * 4 + wv;
-  const bool wvalid = nt < (N >> 5);
-  const int k0 = split * kps;
-  const int nchunks = kps / (16 * KS);
+  const int NT = N >> 5;
+  const int nt0 = slab * 4;
   const int KT = K >> 4;
-  const u32x4* wbase = reinterpret_cast<const u32x4*>(Wp) + ((size_t)(wvalid ? nt : 0) * KT + (k0 >> 4)) * 64 + lane;
-
-  f32x16_t acc[MT];
+  const int kt0 = (split * kps) >> 4;
+  const int nchunks = kps / (16 * KS);
+  const int m_tiles = (M + 31) >> 5;
+  bool tv[MTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+  for (int j = 0; j < MTW; ++j) tv[j] = mt_base + wv + 4 * j < m_tiles;
+  const bool wload = nt0 + wv < NT;
+  const u32x4* wsrc = Wp + ((size_t)(wload ? nt0 + wv : 0) * KT + kt0) * 64 + lane;
+  const u32x4* asrc = Ap + (size_t)kt0 * MTt * 64 + (size_t)(mt_base + wv) * 64 + lane;
 
-  u32x4 wcur[KS], wnext[KS];
-  u32x4 areg[PPT];
+  f32x16_t acc[MTW][4];
+#pragma unroll
+  for (int j = 0; j < MTW; ++j)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[j][nt][i] = 0.f;
+
+  u32x4 wA[KS], wB[KS];
+  u32x4 aA[MTW][KS], aB[MTW][KS];
 
   auto load_w = [&](int c, u32x4* dst) {
-    if (wvalid) {
+    if (wload) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_nontemporal_load(wbase + (size_t)(c * KS + ks) * 64);
+      for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_nontemporal_load(wsrc + (size_t)(c * KS + ks) * 64);
     }
   };
-  auto load_a = [&](int c) {
+  auto load_a = [&](int c, u32x4 (*dst)[KS]) {
 #pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-      const int piece = tid + p * 256;
-      const int row = piece / (2 * KS), kp = piece % (2 * KS);
-      if (row < rows_n)
-        areg[p] = *reinterpret_cast<const u32x4*>(A + (size_t)(r0 + row) * K + k0 + c * 16 * KS + kp * 8);
-    }
-  };
-  auto store_a = [&](int buf) {
+    for (int j = 0; j < MTW; ++j)
+      if (tv[j]) {
 #pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-      const int piece = tid + p * 256;
-      const int row = piece / (2 * KS), kp = piece % (2 * KS);
-      if (row < rows_n) {
-        const int mt = row >> 5, rr = row & 31, ks = kp >> 1, hf = kp & 1;
-        lds[buf * BUF + (mt * KS + ks) * 64 + rr + 32 * hf] = areg[p];
+        for (int ks = 0; ks < KS; ++ks) dst[j][ks] = asrc[((size_t)(c * KS + ks) * MTt + 4 * j) * 64];
       }
+  };
+  auto store_w = [&](const u32x4* src, int buf) {
+    if (wload) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) wl[buf * WBUF + (ks * 4 + wv) * 64 + lane] = src[ks];
+    }
+  };
+  auto compute = [&](int buf, u32x4 (*a)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t bb[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bb[nt] = __builtin_bit_cast(bf16x8_t, wl[buf * WBUF + (ks * 4 + nt) * 64 + lane]);
+#pragma unroll
+      for (int j = 0; j < MTW; ++j)
+        if (tv[j]) {
+          const bf16x8_t aa = __builtin_bit_cast(bf16x8_t, a[j][ks]);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            acc[j][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, bb[nt], acc[j][nt], 0, 0, 0);
+        }
     }
   };
 
-  load_w(0, wcur);
-  load_a(0);
-  store_a(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_w(c + 1, wnext);
-      load_a(c + 1);
+  if (nchunks > 0) {
+    load_w(0, wA);
+    if (nchunks > 1) load_w(1, wB);
+    load_a(0, aA);
+    store_w(wA, 0);
+    if (nchunks > 1) load_a(1, aB);
+    if (nchunks > 2) load_w(2, wA);
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+      // A(c) in aA, W(c) in LDS 0, W(c+1) in wB, W(c+2) in wA
+      compute(0, aA);
+      if (c + 1 < nchunks) store_w(wB, 1);
+      if (c + 2 < nchunks) load_a(c + 2, aA);
+      if (c + 3 < nchunks) load_w(c + 3, wB);
+      __syncthreads();
+      if (c + 1 >= nchunks) break;
+      // A(c+1) in aB, W(c+1) in LDS 1, W(c+2) in wA
+      compute(1, aB);
+      if (c + 2 < nchunks) store_w(wA, 0);
+      if (c + 3 < nchunks) load_a(c + 3, aB);
+      if (c + 4 < nchunks) load_w(c + 4, wA);
+      __syncthreads();
     }
-    if (wvalid) {
+  }
+
+  if constexpr (EPI == 0) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, wcur[ks]);
+    for (int j = 0; j < MTW; ++j) {
+      if (!tv[j]) continue;
+      const int mrow = (mt_base + wv + 4 * j) * 32 + (lane >> 5) * 4;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if (mt < mt_n) {
-            const bf16x8_t aa = __builtin_bit_cast(bf16x8_t, lds[buf * BUF + (mt * KS + ks) * 64 + lane]);
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, bb, acc[mt], 0, 0, 0);
+      for (int nt = 0; nt < 4; ++nt) {
+        if (nt0 + nt >= NT) continue;
+        const int ncol = (nt0 + nt) * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = mrow + (i >> 2) * 8 + (i & 3);
+          if (m < M) out[((size_t)split * M + m) * N + ncol] = acc[j][nt][i];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      if (!tv[j]) continue;
+      const int mrow = (mt_base + wv + 4 * j) * 32 + (lane >> 5) * 4;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if (nt0 + 2 * p + 1 >= NT) continue;
+        const int f = (slab * 2 + p) * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = mrow + (i >> 2) * 8 + (i & 3);
+          if (m < M) {
+            const float g = acc[j][2 * p][i], u = acc[j][2 * p + 1][i];
+            act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
           }
         }
       }
     }
-    if (more) store_a(buf ^ 1);
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) wcur[ks] = wnext[ks];
-  }
-  if (!wvalid) return;
-  const int ncol = nt * 32 + (lane & 31);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt < mt_n) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = r0 + mt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-        if (m < M) out[((size_t)split * M + m) * N + ncol] = acc[mt][i];
-      }
-    }
   }
 }
 
-constexpr int GEMM_KS = 4;
+static int mtw_for_rows(int max_rows) {
+  if (max_rows <= 128) return 1;
+  if (max_rows <= 256) return 2;
+  return 3;
+}
+static int ks_for(int mtw) { return mtw <= 2 ? 8 : 4; }
 
-template <int MT>
-static hipError_t launch_mt(hipStream_t st, int grid, const uint16_t* A, const uint16_t* Wp, float* out,
-                            const int32_t* n_sel, int B, int K, int N, int kps, int row_blocks, int n_slabs,
-                            int total, int cap) {
+template <int MTW, int KS, int EPI>
+static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
+                             uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
+                             int row_blocks, int n_slabs, int total, int cap) {
   static bool attr_set = false;
-  const size_t lds = (size_t)2 * MT * GEMM_KS * 64 * 16;
+  const size_t lds = (size_t)2 * KS * 4 * 64 * 16;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MT, GEMM_KS>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MTW, KS, EPI>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<MT, GEMM_KS>), dim3(grid), dim3(256), lds, st, A, Wp, out, n_sel, B, K, N,
-                     kps, row_blocks, n_slabs, total, cap);
+  hipLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
+                     (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, cap);
   return hipGetLastError();
 }
 
-static int mt_for_rows(int max_rows) {
-  const int t = (max_rows + 31) / 32;
-  if (t <= 1) return 1;
-  if (t <= 2) return 2;
-  if (t <= 4) return 4;
-  if (t <= 6) return 6;
-  if (t <= 8) return 8;
-  if (t <= 10) return 10;
-  return 8;  // row-blocked
-}
-
 int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
-  const int MT = mt_for_rows(max_rows);
-  const int row_blocks = (max_rows + 32 * MT - 1) / (32 * MT);
+  const int mtw = mtw_for_rows(max_rows);
+  const int ks = ks_for(mtw);
+  const int row_blocks = (max_rows + 128 * mtw - 1) / (128 * mtw);
   const int n_slabs = (N + 127) / 128;
   const int base = n_slabs * row_blocks;
-  const double wbytes = (double)K * N * 2.0 * row_blocks;
+  const double wbytes = (double)K * N * 2.0;
   double best = 1e300;
   int best_s = 1;
-  for (int s = 1; s <= 64; s *= 2) {
-    if (K % (s * 16 * GEMM_KS) != 0) break;
+  for (int s = 1; s <= 32; s *= 2) {
+    if (K % (s * 16 * ks) != 0) break;
     const int waves = (base * s + n_cu - 1) / n_cu;
     const double eff = (double)base * s / ((double)waves * n_cu);
-    const double cost = wbytes / eff + 0.5 * 2.0 * 4.0 * s * (double)max_rows * N;
+    // weight stream at the achieved occupancy + split partial round trip
+    const double cost = wbytes / eff + (s > 1 ? 2.0 * 4.0 * s * (double)max_rows * N : 0.0);
     if (cost < best * 0.999) {
       best = cost;
       best_s = s;
@@ -239,24 +281,30 @@ int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
   return best_s;
 }
 
-hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A,
-                            const uint16_t* Wp, const int32_t* n_sel, float* out, int splits) {
+hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
+                            const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
+                            int MTt_out) {
   if (max_rows <= 0) return hipSuccess;
-  const int MT = mt_for_rows(max_rows);
-  const int row_blocks = (max_rows + 32 * MT - 1) / (32 * MT);
+  const int mtw = mtw_for_rows(max_rows);
+  const int ks = ks_for(mtw);
+  const int row_blocks = (max_rows + 128 * mtw - 1) / (128 * mtw);
   const int n_slabs = (N + 127) / 128;
   const int kps = K / splits;
-  if (kps * splits != K || kps % (16 * GEMM_KS) != 0) return hipErrorInvalidValue;
+  if (kps * splits != K || kps % (16 * ks) != 0) return hipErrorInvalidValue;
+  if (act != nullptr && (splits != 1 || N % 64 != 0)) return hipErrorInvalidValue;
   const int total = n_slabs * row_blocks * splits;
   const int grid = (total + 7) / 8 * 8;
-  switch (MT) {
-    case 1: return launch_mt<1>(st, grid, A, Wp, out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows);
-    case 2: return launch_mt<2>(st, grid, A, Wp, out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows);
-    case 4: return launch_mt<4>(st, grid, A, Wp, out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows);
-    case 6: return launch_mt<6>(st, grid, A, Wp, out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows);
-    case 8: return launch_mt<8>(st, grid, A, Wp, out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows);
-    default: return launch_mt<10>(st, grid, A, Wp, out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows);
+#define GL(MTW, KS, EPI) \
+  launch_cfg<MTW, KS, EPI>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows)
+  if (act == nullptr) {
+    if (mtw == 1) return GL(1, 8, 0);
+    if (mtw == 2) return GL(2, 8, 0);
+    return GL(3, 4, 0);
   }
+  if (mtw == 1) return GL(1, 8, 1);
+  if (mtw == 2) return GL(2, 8, 1);
+  return GL(3, 4, 1);
+#undef GL
 }
 
 // ---------------------------------------------------------------------------

@@ -22,7 +22,7 @@ hipError_t launch_embed(hipStream_t st, bool bf16, int max_rows, int B, int L, i
                         const int32_t* idx, const int32_t* n, const int32_t* tokens, const void* embed,
                         void* h0);
 // A[m] = RMSNorm(H[row m]) * g  (fp32 statistics), rows from idx/n.
-hipError_t launch_gather_norm(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, float eps,
+hipError_t launch_gather_norm(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, float eps, int MTt,
                               const int32_t* idx, const int32_t* n, const void* H, const float* g,
                               void* A);
 // q/k RoPE + K/V scatter from QKV partials [S][M][nq + 2 nv].
@@ -32,7 +32,7 @@ hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16, int max_rows, int B, i
                                void* Vc);
 // h' = x + sum_s part; A2 = RMSNorm(h') * g2.
 hipError_t launch_o_epilogue(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, int S,
-                             float eps, const int32_t* idx, const int32_t* n, const float* part,
+                             float eps, int MTt, const int32_t* idx, const int32_t* n, const float* part,
                              const void* H, const float* g2, float* hprime, void* A2);
 // act = SiLU(gate) * up from gate|up partials interleaved by 32 columns.
 hipError_t launch_swiglu(hipStream_t st, bool bf16, int max_rows, int B, int F, int S, const int32_t* n,
@@ -61,8 +61,12 @@ hipError_t launch_select(hipStream_t st, int B, int L, int k, const double* scor
 hipError_t launch_gemm_f32(hipStream_t st, int max_rows, int B, int K, int N, const float* A,
                            const float* W, const int32_t* n_sel, float* out);
 // bf16 weights pre-packed by launch_pack_bf16; `splits` from gemm_bf16_pick_splits.
-hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A,
-                            const uint16_t* Wp, const int32_t* n_sel, float* out, int splits);
+// A is packed (apack_off) with MTt row tiles.  act != NULL (one split, N a
+// multiple of 64, gate/up interleaved by 32 columns) writes SwiGLU(gate, up)
+// as a packed bf16 [M][N/2] activation with MTt_out row tiles instead of out.
+hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
+                            const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
+                            int MTt_out);
 int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu);
 // Pack source columns [0, Nsrc) of a row-major [K][ld_src] weight: source
 // column tile t (32 columns) lands at packed column col0 + t*tile_stride.
@@ -74,12 +78,14 @@ hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, in
 
 // ---- attention (attn.hip) ----
 size_t attn_partial_floats(int max_rows, int Hq, int dh, int L);
+// out: the GEMM input of the output projection ([M][Hq*dh], packed for bf16
+// with MTt row tiles).
 hipError_t launch_attention(hipStream_t st, bool bf16, int max_rows, int B, int L, int Hq, int Hkv, int dh,
                             const int32_t* idx, const int32_t* n, const void* q, const void* Kc,
-                            const void* Vc, float* partial, void* out);
+                            const void* Vc, float* partial, void* out, int MTt);
 
 // ---- LM head and commit (lmhead.hip) ----
-hipError_t launch_lm_gather(hipStream_t st, bool bf16, int B, int L, int blk, int d, float eps,
+hipError_t launch_lm_gather(hipStream_t st, bool bf16, int B, int L, int blk, int d, float eps, int MTt,
                             const int32_t* block_start, const void* H, const float* g, void* A,
                             int32_t* n_rows);
 hipError_t launch_lm_stats(hipStream_t st, int M, int V, const float* logits, double* part,

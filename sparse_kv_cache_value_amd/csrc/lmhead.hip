@@ -21,7 +21,7 @@ int lm_stats_slabs(int V) { return (V + LM_SLAB - 1) / LM_SLAB; }
 
 // A[m] = bf16/f32( RMSNorm_fp64(H_N[b][block_start[b] + j]) * g ), m = b*blk + j.
 template <typename T>
-__global__ __launch_bounds__(256) void lm_gather_kernel(int B, int L, int blk, int d, float eps,
+__global__ __launch_bounds__(256) void lm_gather_kernel(int B, int L, int blk, int d, float eps, int MTt,
                                                         const int32_t* __restrict__ block_start,
                                                         const T* __restrict__ H, const float* __restrict__ g,
                                                         T* __restrict__ A, int32_t* __restrict__ n_rows) {
@@ -30,9 +30,9 @@ __global__ __launch_bounds__(256) void lm_gather_kernel(int B, int L, int blk, i
   const int b = m / blk, j = m - b * blk;
   if (m == 0 && threadIdx.x == 0) n_rows[0] = B * blk;
   const int row = block_start[b] + j;
-  T* a = A + (size_t)m * d;
   if (block_start[b] >= L || row >= L) {
-    for (int c = threadIdx.x; c < d; c += 256) a[c] = T(0);
+    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int c8 = threadIdx.x * 8; c8 < d; c8 += 256 * 8) store_a8(A, m, c8, MTt, d, z);
     return;
   }
   const T* x = H + ((size_t)b * L + row) * d;
@@ -43,17 +43,21 @@ __global__ __launch_bounds__(256) void lm_gather_kernel(int B, int L, int blk, i
   }
   ss = block_sum<4>(ss, red);
   const double den = sqrt(ss / (double)d + (double)eps);
-  for (int c = threadIdx.x; c < d; c += 256)
-    io<T>::st(a + c, (float)((double)io<T>::ld(x + c) / den * (double)g[c]));
+  for (int c8 = threadIdx.x * 8; c8 < d; c8 += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int j2 = 0; j2 < 8; ++j2) v[j2] = (float)((double)io<T>::ld(x + c8 + j2) / den * (double)g[c8 + j2]);
+    store_a8(A, m, c8, MTt, d, v);
+  }
 }
 
-hipError_t launch_lm_gather(hipStream_t st, bool bf16m, int B, int L, int blk, int d, float eps,
+hipError_t launch_lm_gather(hipStream_t st, bool bf16m, int B, int L, int blk, int d, float eps, int MTt,
                             const int32_t* block_start, const void* H, const float* g, void* A, int32_t* n_rows) {
   if (bf16m)
-    hipLaunchKernelGGL(lm_gather_kernel<bf16>, dim3(B * blk), dim3(256), 0, st, B, L, blk, d, eps, block_start,
+    hipLaunchKernelGGL(lm_gather_kernel<bf16>, dim3(B * blk), dim3(256), 0, st, B, L, blk, d, eps, MTt, block_start,
                        (const bf16*)H, g, (bf16*)A, n_rows);
   else
-    hipLaunchKernelGGL(lm_gather_kernel<float>, dim3(B * blk), dim3(256), 0, st, B, L, blk, d, eps, block_start,
+    hipLaunchKernelGGL(lm_gather_kernel<float>, dim3(B * blk), dim3(256), 0, st, B, L, blk, d, eps, MTt, block_start,
                        (const float*)H, g, (float*)A, n_rows);
   return hipGetLastError();
 }

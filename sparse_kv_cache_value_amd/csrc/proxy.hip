@@ -120,8 +120,7 @@ __global__ __launch_bounds__(64) void proxy_finish_kernel(int B, int L, int r, i
     c[t] = 0.0;
     p[t] = 0.0;
     if (j < r) {
-      double v = 0.0;
-      for (int s = 0; s < S; ++s) v += partial[((size_t)s * M + m) * r + j];
+      const double v = sum_splits(partial + (size_t)m * r + j, (size_t)M * r, S);
       c[t] = v;
       p[t] = pref[row * r + j];
       pcur[row * r + j] = v;

@@ -114,7 +114,7 @@ hipError_t launch_embed(hipStream_t st, bool bf16m, int max_rows, int B, int L, 
 // Gather + RMSNorm (fp32 statistics) of the selected rows into compact A.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void gather_norm_kernel(int B, int L, int d, float eps,
+__global__ __launch_bounds__(256) void gather_norm_kernel(int B, int L, int d, float eps, int MTt,
                                                           const int32_t* __restrict__ idx,
                                                           const int32_t* __restrict__ n,
                                                           const T* __restrict__ H, const float* __restrict__ g,
@@ -131,19 +131,23 @@ __global__ __launch_bounds__(256) void gather_norm_kernel(int B, int L, int d, f
   }
   ss = block_sum<4>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  T* a = A + (size_t)m * d;
-  for (int c = threadIdx.x; c < d; c += 256) io<T>::st(a + c, io<T>::ld(x + c) * inv * g[c]);
+  for (int c8 = threadIdx.x * 8; c8 < d; c8 += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = io<T>::ld(x + c8 + j) * inv * g[c8 + j];
+    store_a8(A, m, c8, MTt, d, v);
+  }
 }
 
-hipError_t launch_gather_norm(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, float eps,
+hipError_t launch_gather_norm(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, float eps, int MTt,
                               const int32_t* idx, const int32_t* n, const void* H, const float* g,
                               void* A) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(gather_norm_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, eps, idx, n,
+    hipLaunchKernelGGL(gather_norm_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, eps, MTt, idx, n,
                        (const bf16*)H, g, (bf16*)A);
   else
-    hipLaunchKernelGGL(gather_norm_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, eps, idx, n,
+    hipLaunchKernelGGL(gather_norm_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, eps, MTt, idx, n,
                        (const float*)H, g, (float*)A);
   return hipGetLastError();
 }
@@ -168,11 +172,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq,
   const int nq = Hq * dh, nv = Hkv * dh, N = nq + 2 * nv, half = dh / 2;
   const size_t sstride = (size_t)M * N;
   const float* p0 = part + (size_t)m * N;
-  auto val = [&](int c) {
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += p0[s * sstride + c];
-    return v;
-  };
+  auto val = [&](int c) { return sum_splits(p0 + c, sstride, S); };
   const int npairs = (Hq + Hkv) * half;
   for (int p = threadIdx.x; p < npairs; p += 256) {
     const int head = p / half, j = p - head * half;
@@ -189,9 +189,10 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq,
       io<T>::st(kr + j + half, r1);
     }
   }
+  // V layout [b][g][L/4][dh][4]: four consecutive keys of one dimension adjacent
   for (int c = threadIdx.x; c < nv; c += 256) {
     const int g = c / dh, t = c - g * dh;
-    io<T>::st(Vc + (((size_t)b * Hkv + g) * L + i) * dh + t, val(nq + nv + c));
+    io<T>::st(Vc + ((size_t)b * Hkv + g) * L * dh + ((size_t)(i >> 2) * dh + t) * 4 + (i & 3), val(nq + nv + c));
   }
 }
 
@@ -213,7 +214,7 @@ hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, 
 // Output projection epilogue: h' = x + o W_o (fp32), then the FFN norm.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, int S, int cap, float eps,
+__global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, int S, int cap, float eps, int MTt,
                                                          const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ n,
                                                          const float* __restrict__ part,
@@ -229,28 +230,29 @@ __global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, in
   float* hp = hprime + (size_t)m * d;
   float ss = 0.f;
   for (int c = threadIdx.x; c < d; c += 256) {
-    float v = io<T>::ld(x + c);
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc += part[s * sstride + (size_t)m * d + c];
-    v += acc;
+    const float v = io<T>::ld(x + c) + sum_splits(part + (size_t)m * d + c, sstride, S);
     hp[c] = v;
     ss += v * v;
   }
   ss = block_sum<4>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  T* a = A2 + (size_t)m * d;
-  for (int c = threadIdx.x; c < d; c += 256) io<T>::st(a + c, hp[c] * inv * g2[c]);
+  for (int c8 = threadIdx.x * 8; c8 < d; c8 += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = hp[c8 + j] * inv * g2[c8 + j];
+    store_a8(A2, m, c8, MTt, d, v);
+  }
 }
 
 hipError_t launch_o_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, int S,
-                             float eps, const int32_t* idx, const int32_t* n, const float* part,
+                             float eps, int MTt, const int32_t* idx, const int32_t* n, const float* part,
                              const void* H, const float* g2, float* hprime, void* A2) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(o_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, idx, n,
+    hipLaunchKernelGGL(o_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, MTt, idx, n,
                        part, (const bf16*)H, g2, hprime, (bf16*)A2);
   else
-    hipLaunchKernelGGL(o_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, idx, n,
+    hipLaunchKernelGGL(o_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, MTt, idx, n,
                        part, (const float*)H, g2, hprime, (float*)A2);
   return hipGetLastError();
 }
@@ -270,11 +272,8 @@ __global__ __launch_bounds__(256) void swiglu_kernel(int B, int F, int S, int ca
   const int N = 2 * F;
   const size_t sstride = (size_t)M * N;
   const int cg = (f >> 5) * 64 + (f & 31);
-  float gv = 0.f, uv = 0.f;
-  for (int s = 0; s < S; ++s) {
-    gv += part[s * sstride + (size_t)m * N + cg];
-    uv += part[s * sstride + (size_t)m * N + cg + 32];
-  }
+  const float gv = sum_splits(part + (size_t)m * N + cg, sstride, S);
+  const float uv = sum_splits(part + (size_t)m * N + cg + 32, sstride, S);
   const float sl = gv / (1.0f + expf(-gv));
   io<T>::st(act + (size_t)m * F + f, sl * uv);
 }
@@ -310,11 +309,7 @@ __global__ __launch_bounds__(256) void down_epilogue_kernel(int B, int L, int d,
   const size_t row = (size_t)b * L + i;
   T* o = Hout + row * d;
   const float* hp = hprime + (size_t)m * d;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc += part[s * sstride + (size_t)m * d + c];
-    io<T>::st(o + c, hp[c] + acc);
-  }
+  for (int c = threadIdx.x; c < d; c += 256) io<T>::st(o + c, hp[c] + sum_splits(part + (size_t)m * d + c, sstride, S));
   for (int j = threadIdx.x; j < r; j += 256) pref[row * r + j] = pcur[row * r + j];
   if (threadIdx.x == 0) score[row] = 0.0;
 }

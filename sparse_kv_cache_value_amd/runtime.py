@@ -83,7 +83,8 @@ class State:
         dt = inputs.storage_dtype(cfg)
         self.hidden = torch.zeros((N + 1, Bn, L, d), dtype=dt, device=dev)
         self.k_cache = torch.zeros((N, Bn, cfg.n_kv_heads, L, cfg.head_dim), dtype=dt, device=dev)
-        self.v_cache = torch.zeros_like(self.k_cache)
+        # values: four consecutive keys of one head dimension adjacent
+        self.v_cache = torch.zeros((N, Bn, cfg.n_kv_heads, L // 4, cfg.head_dim, 4), dtype=dt, device=dev)
         self.proxy_cur = torch.zeros((N, Bn, L, r), dtype=torch.float64, device=dev)
         self.proxy_ref = torch.zeros_like(self.proxy_cur)
         self.score = torch.zeros((N, Bn, L), dtype=torch.float64, device=dev)

@@ -39,7 +39,9 @@ class Snap:
         t = {k: v.detach().cpu() for k, v in st.tensors().items()}
         self.H = t["hidden"].float().numpy()                                 # [N+1, B, L, d]
         self.K = t["k_cache"].float().permute(0, 1, 3, 2, 4).numpy()         # [N, B, L, Hkv, dh]
-        self.V = t["v_cache"].float().permute(0, 1, 3, 2, 4).numpy()
+        v = t["v_cache"].float()  # [N, B, Hkv, L/4, dh, 4]
+        N_, B_, G_, L4, dh, _ = v.shape
+        self.V = v.permute(0, 1, 3, 5, 2, 4).reshape(N_, B_, L4 * 4, G_, dh).numpy()
         self.Pc = t["proxy_cur"].numpy()
         self.Pr = t["proxy_ref"].numpy()
         self.score = t["score"].numpy()

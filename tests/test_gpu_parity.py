@@ -21,7 +21,9 @@ pytestmark = pytest.mark.gpu
 CFGS = {
     "c1-fp32": configs.C1.with_(n_steps=3),
     "medium-bf16": medium_cfg(),
-    "medium-gqa": medium_cfg(name="medium-gqa", n_q_heads=8, n_kv_heads=2, head_dim=64, seed=22),
+    "medium-gqa": medium_cfg(name="medium-gqa", n_q_heads=8, n_kv_heads=2, head_dim=128, seed=22),
+    "medium-dh64": medium_cfg(name="medium-dh64", n_q_heads=8, n_kv_heads=8, head_dim=64, seed=25, n_steps=2),
+    "medium-l100": medium_cfg(name="medium-l100", seq_len=100, prompt_len=50, seed=26, n_steps=2),
     "medium-b2": medium_cfg(name="medium-b2", batch=2, seq_len=96, prompt_len=40, seed=23, n_steps=3),
     "medium-none": medium_cfg(name="medium-none", forced=configs.FORCED_NONE, recent_k=0, seed=24, n_steps=3),
 }
