@@ -49,7 +49,7 @@ struct LayerW {
   void* w_o = nullptr;     // packed [nq][d]
   void* w_gu = nullptr;    // packed [d][2F], gate/up interleaved by 32 columns
   void* w_down = nullptr;  // packed [F][d]
-  double* w_proxy = nullptr;  // diag(attn_norm) W_r, fp64 [d][r]
+  float* w_proxy = nullptr;  // W_r, fp32 [d][proxy_rpad(r)] (zero columns past r)
   bool ready = false;
 };
 
@@ -258,11 +258,12 @@ dllm_status do_drift(dllm_model* m, int layer, dllm_state* s, const int32_t* row
                      hipStream_t st) {
   const dllm_dims& d = m->d;
   Prof prof(m, st, DLLM_PROF_PROXY,
-            (double)max_rows * d.d_model * m->esize + (double)d.d_model * d.proxy_rank * 8.0 +
+            (double)max_rows * d.d_model * m->esize + (double)d.d_model * d.proxy_rank * 4.0 +
                 (double)max_rows * d.proxy_rank * 8.0 * 3.0,
             2.0 * max_rows * (double)d.d_model * d.proxy_rank);
   HIPCHK(launch_proxy_drift(st, m->bf16, max_rows, s->batch, d.seq_len, d.d_model, d.proxy_rank, rows, n,
-                            hid(m, s, layer), m->layers[layer].w_proxy, m->ppart, pcur(m, s, layer),
+                            hid(m, s, layer), m->layers[layer].attn_norm, m->layers[layer].w_proxy, m->ppart,
+                            pcur(m, s, layer),
                             pref(m, s, layer), score(m, s, layer)));
   prof.done();
   return DLLM_OK;
@@ -349,7 +350,8 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
       d.vocab < 2 || d.max_batch < 1 || d.seq_len < 1 || d.block_len < 1 || d.proxy_rank < 1)
     return fail(DLLM_E_ARG, "non-positive dimension");
   if (d.dtype != DLLM_FP32 && d.dtype != DLLM_BF16) return fail(DLLM_E_ARG, "unknown dtype %d", d.dtype);
-  if (d.head_dim % 2 || d.head_dim > 256) return fail(DLLM_E_SHAPE, "head_dim must be even and <= 256");
+  if (d.head_dim % 8 || d.head_dim > 256) return fail(DLLM_E_SHAPE, "head_dim must be a multiple of 8 and <= 256");
+  if (d.d_model > 8192) return fail(DLLM_E_SHAPE, "d_model %d > 8192", d.d_model);
   if (d.n_q_heads % d.n_kv_heads) return fail(DLLM_E_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
   if (d.seq_len > 8192) return fail(DLLM_E_SHAPE, "seq_len %d > 8192", d.seq_len);
   if (d.seq_len % 4) return fail(DLLM_E_SHAPE, "seq_len must be a multiple of 4");
@@ -388,11 +390,12 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
     st = m->alloc((void**)&(ptr), (bytes));       \
     if (st != DLLM_OK) return cleanup(st);        \
   } while (0)
-  ALLOC(m->A1, (size_t)m->M_pad * D * es);
+  const size_t apad = gemm_pad_elems(m->MTt) * es;  // packed activations are read past their end
+  ALLOC(m->A1, (size_t)m->M_pad * D * es + apad);
   ALLOC(m->q, (size_t)m->M_pad * nq * es);
-  ALLOC(m->attn_o, (size_t)m->M_pad * nq * es);
-  ALLOC(m->A2, (size_t)m->M_pad * D * es);
-  ALLOC(m->act, (size_t)m->M_pad * F * es);
+  ALLOC(m->attn_o, (size_t)m->M_pad * nq * es + apad);
+  ALLOC(m->A2, (size_t)m->M_pad * D * es + apad);
+  ALLOC(m->act, (size_t)m->M_pad * F * es + apad);
   ALLOC(m->hprime, (size_t)m->M_pad * D * 4);
   {
     const int nmax = std::max(std::max(nq + 2 * nv, 2 * F), D);
@@ -416,7 +419,7 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   ALLOC(m->step_full, (size_t)d.max_batch);
   const int lm_rows_cap = d.max_batch * d.block_len;
   m->lm_MTt = (lm_rows_cap + 31) / 32 + 1;
-  ALLOC(m->A_lm, (size_t)m->lm_MTt * 32 * D * es);
+  ALLOC(m->A_lm, (size_t)m->lm_MTt * 32 * D * es + gemm_pad_elems(m->lm_MTt) * es);
   ALLOC(m->logits, (size_t)lm_rows_cap * d.vocab * 4);
   m->lm_slabs = lm_stats_slabs(d.vocab);
   ALLOC(m->lm_part, (size_t)lm_rows_cap * m->lm_slabs * 4 * 8);
@@ -476,11 +479,12 @@ dllm_status dllm_init_layer(dllm_model* m, int32_t layer, const dllm_layer_weigh
   if (!L.w_qkv) {
     CHK(m->alloc((void**)&L.attn_norm, (size_t)D * 4));
     CHK(m->alloc((void**)&L.ffn_norm, (size_t)D * 4));
-    CHK(m->alloc(&L.w_qkv, (size_t)D * (nq + 2 * nv) * es));
-    CHK(m->alloc(&L.w_o, (size_t)nq * D * es));
-    CHK(m->alloc(&L.w_gu, (size_t)D * 2 * F * es));
-    CHK(m->alloc(&L.w_down, (size_t)F * D * es));
-    CHK(m->alloc((void**)&L.w_proxy, (size_t)D * r * 8));
+    const size_t wpad = gemm_pad_elems(1) * es;  // the GEMM pipeline reads past the last chunk
+    CHK(m->alloc(&L.w_qkv, (size_t)D * (nq + 2 * nv) * es + wpad));
+    CHK(m->alloc(&L.w_o, (size_t)nq * D * es + wpad));
+    CHK(m->alloc(&L.w_gu, (size_t)D * 2 * F * es + wpad));
+    CHK(m->alloc(&L.w_down, (size_t)F * D * es + wpad));
+    CHK(m->alloc((void**)&L.w_proxy, (size_t)D * proxy_rpad(r) * 4));
   }
   HIPCHK(hipMemcpyAsync(L.attn_norm, w->attn_norm, (size_t)D * 4, hipMemcpyDeviceToDevice, st));
   HIPCHK(hipMemcpyAsync(L.ffn_norm, w->ffn_norm, (size_t)D * 4, hipMemcpyDeviceToDevice, st));
@@ -492,7 +496,7 @@ dllm_status dllm_init_layer(dllm_model* m, int32_t layer, const dllm_layer_weigh
   CHK(pack(m, st, D, F, w->w_gate, L.w_gu, 2 * F, 0, 64));
   CHK(pack(m, st, D, F, w->w_up, L.w_gu, 2 * F, 32, 64));
   CHK(pack(m, st, F, D, w->w_down, L.w_down, D, 0, 32));
-  HIPCHK(launch_fold_proxy(st, D, r, w->attn_norm, w->w_proxy, L.w_proxy));
+  HIPCHK(launch_pad_proxy(st, D, r, w->w_proxy, L.w_proxy));
   L.ready = true;
   return DLLM_OK;
 }
@@ -506,7 +510,7 @@ dllm_status dllm_init_head(dllm_model* m, const void* embed, const float* final_
   if (!m->embed) {
     CHK(m->alloc(&m->embed, (size_t)d.vocab * d.d_model * m->esize));
     CHK(m->alloc((void**)&m->final_norm, (size_t)d.d_model * 4));
-    CHK(m->alloc(&m->lm_head, (size_t)d.d_model * d.vocab * m->esize));
+    CHK(m->alloc(&m->lm_head, (size_t)d.d_model * d.vocab * m->esize + gemm_pad_elems(1) * m->esize));
   }
   HIPCHK(hipMemcpyAsync(m->embed, embed, (size_t)d.vocab * d.d_model * m->esize, hipMemcpyDeviceToDevice, st));
   HIPCHK(hipMemcpyAsync(m->final_norm, final_norm, (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));

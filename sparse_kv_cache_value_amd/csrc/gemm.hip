@@ -119,9 +119,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const u32x4* __restri
   bool tv[MTW];
 #pragma unroll
   for (int j = 0; j < MTW; ++j) tv[j] = mt_base + wv + 4 * j < m_tiles;
-  const bool wload = nt0 + wv < NT;
-  const u32x4* wsrc = Wp + ((size_t)(wload ? nt0 + wv : 0) * KT + kt0) * 64 + lane;
-  const u32x4* asrc = Ap + (size_t)kt0 * MTt * 64 + (size_t)(mt_base + wv) * 64 + lane;
+  // Every load below is unconditional so that the compiler's wait counts keep
+  // the prefetched chunks in flight: invalid tiles are clamped to a valid one
+  // and the (at most three) chunks read past the end of a range land in the
+  // padding that every weight and activation buffer carries.
+  const int ntw = min(nt0 + wv, NT - 1);
+  const u32x4* wsrc = Wp + ((size_t)ntw * KT + kt0) * 64 + lane;
+  const u32x4* asrc[MTW];
+#pragma unroll
+  for (int j = 0; j < MTW; ++j)
+    asrc[j] = Ap + (size_t)kt0 * MTt * 64 + (size_t)min(mt_base + wv + 4 * j, m_tiles - 1) * 64 + lane;
+  const size_t astep = (size_t)KS * MTt * 64;  // one chunk of A, in 16-byte units
 
   f32x16_t acc[MTW][4];
 #pragma unroll
@@ -135,65 +143,60 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const u32x4* __restri
   u32x4 aA[MTW][KS], aB[MTW][KS];
 
   auto load_w = [&](int c, u32x4* dst) {
-    if (wload) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_nontemporal_load(wsrc + (size_t)(c * KS + ks) * 64);
-    }
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_nontemporal_load(wsrc + (size_t)(c * KS + ks) * 64);
   };
   auto load_a = [&](int c, u32x4 (*dst)[KS]) {
 #pragma unroll
     for (int j = 0; j < MTW; ++j)
-      if (tv[j]) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dst[j][ks] = asrc[((size_t)(c * KS + ks) * MTt + 4 * j) * 64];
-      }
+      for (int ks = 0; ks < KS; ++ks) dst[j][ks] = asrc[j][(size_t)c * astep + (size_t)ks * MTt * 64];
   };
   auto store_w = [&](const u32x4* src, int buf) {
-    if (wload) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) wl[buf * WBUF + (ks * 4 + wv) * 64 + lane] = src[ks];
-    }
+    for (int ks = 0; ks < KS; ++ks) wl[buf * WBUF + (ks * 4 + wv) * 64 + lane] = src[ks];
   };
   auto compute = [&](int buf, u32x4 (*a)[KS]) {
+    // all B fragments of the chunk first, so one LDS latency covers them all
+    u32x4 b[KS][4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t bb[4];
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bb[nt] = __builtin_bit_cast(bf16x8_t, wl[buf * WBUF + (ks * 4 + nt) * 64 + lane]);
+      for (int nt = 0; nt < 4; ++nt) b[ks][nt] = wl[buf * WBUF + (ks * 4 + nt) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < MTW; ++j)
-        if (tv[j]) {
-          const bf16x8_t aa = __builtin_bit_cast(bf16x8_t, a[j][ks]);
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            acc[j][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, bb[nt], acc[j][nt], 0, 0, 0);
-        }
-    }
+      for (int j = 0; j < MTW; ++j) {
+        const bf16x8_t aa = __builtin_bit_cast(bf16x8_t, a[j][ks]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[j][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, __builtin_bit_cast(bf16x8_t, b[ks][nt]),
+                                                               acc[j][nt], 0, 0, 0);
+      }
   };
 
-  if (nchunks > 0) {
-    load_w(0, wA);
-    if (nchunks > 1) load_w(1, wB);
-    load_a(0, aA);
-    store_w(wA, 0);
-    if (nchunks > 1) load_a(1, aB);
-    if (nchunks > 2) load_w(2, wA);
+  // nchunks is even (the host guarantees it)
+  load_w(0, wA);
+  load_w(1, wB);
+  load_a(0, aA);
+  store_w(wA, 0);
+  load_a(1, aB);
+  load_w(2, wA);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    // A(c) in aA, W(c) in LDS 0, W(c+1) in wB, W(c+2) in wA
+    compute(0, aA);
+    store_w(wB, 1);
+    load_a(c + 2, aA);
+    load_w(c + 3, wB);
     __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-      // A(c) in aA, W(c) in LDS 0, W(c+1) in wB, W(c+2) in wA
-      compute(0, aA);
-      if (c + 1 < nchunks) store_w(wB, 1);
-      if (c + 2 < nchunks) load_a(c + 2, aA);
-      if (c + 3 < nchunks) load_w(c + 3, wB);
-      __syncthreads();
-      if (c + 1 >= nchunks) break;
-      // A(c+1) in aB, W(c+1) in LDS 1, W(c+2) in wA
-      compute(1, aB);
-      if (c + 2 < nchunks) store_w(wA, 0);
-      if (c + 3 < nchunks) load_a(c + 3, aB);
-      if (c + 4 < nchunks) load_w(c + 4, wA);
-      __syncthreads();
-    }
+    // A(c+1) in aB, W(c+1) in LDS 1, W(c+2) in wA
+    compute(1, aB);
+    store_w(wA, 0);
+    load_a(c + 3, aB);
+    load_w(c + 4, wA);
+    __syncthreads();
   }
 
   if constexpr (EPI == 0) {
@@ -239,7 +242,7 @@ static int mtw_for_rows(int max_rows) {
   if (max_rows <= 256) return 2;
   return 3;
 }
-static int ks_for(int mtw) { return mtw <= 2 ? 8 : 4; }
+static int ks_for(int) { return 4; }
 
 template <int MTW, int KS, int EPI>
 static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
@@ -258,6 +261,10 @@ static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, c
   return hipGetLastError();
 }
 
+// Elements of padding every packed weight / activation buffer needs past its
+// end: the pipeline reads up to three 64-wide k chunks beyond a range.
+size_t gemm_pad_elems(int rows_tiles) { return (size_t)3 * 4 * (size_t)(rows_tiles > 0 ? rows_tiles : 1) * 512; }
+
 int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
   const int mtw = mtw_for_rows(max_rows);
   const int ks = ks_for(mtw);
@@ -268,7 +275,7 @@ int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
   double best = 1e300;
   int best_s = 1;
   for (int s = 1; s <= 32; s *= 2) {
-    if (K % (s * 16 * ks) != 0) break;
+    if (K % (s * 32 * ks) != 0) break;  // an even number of chunks per split
     const int waves = (base * s + n_cu - 1) / n_cu;
     const double eff = (double)base * s / ((double)waves * n_cu);
     // weight stream at the achieved occupancy + split partial round trip
@@ -290,19 +297,19 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
   const int row_blocks = (max_rows + 128 * mtw - 1) / (128 * mtw);
   const int n_slabs = (N + 127) / 128;
   const int kps = K / splits;
-  if (kps * splits != K || kps % (16 * ks) != 0) return hipErrorInvalidValue;
+  if (kps * splits != K || kps % (32 * ks) != 0) return hipErrorInvalidValue;
   if (act != nullptr && (splits != 1 || N % 64 != 0)) return hipErrorInvalidValue;
   const int total = n_slabs * row_blocks * splits;
   const int grid = (total + 7) / 8 * 8;
 #define GL(MTW, KS, EPI) \
   launch_cfg<MTW, KS, EPI>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows)
   if (act == nullptr) {
-    if (mtw == 1) return GL(1, 8, 0);
-    if (mtw == 2) return GL(2, 8, 0);
+    if (mtw == 1) return GL(1, 4, 0);
+    if (mtw == 2) return GL(2, 4, 0);
     return GL(3, 4, 0);
   }
-  if (mtw == 1) return GL(1, 8, 1);
-  if (mtw == 2) return GL(2, 8, 1);
+  if (mtw == 1) return GL(1, 4, 1);
+  if (mtw == 2) return GL(2, 4, 1);
   return GL(3, 4, 1);
 #undef GL
 }

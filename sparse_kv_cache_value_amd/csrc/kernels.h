@@ -46,11 +46,15 @@ hipError_t launch_down_epilogue(hipStream_t st, bool bf16, int max_rows, int B, 
 // ---- proxy and drift (proxy.hip) ----
 // Capacity of the split partial buffer needed for max_rows rows (doubles).
 size_t proxy_partial_doubles(int max_rows, int d, int r);
+// Stored basis width: r rounded up to 32, 64 or 128.
+int proxy_rpad(int r);
+// C[row] = (H[row] * g1) W_r and score[row] = drift(C, proxy_ref[row]) for the
+// listed rows; wr is the padded fp32 basis [d][proxy_rpad(r)].
 hipError_t launch_proxy_drift(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, int r,
-                              const int32_t* idx, const int32_t* n, const void* H, const double* wg,
-                              double* partial, double* pcur, const double* pref, double* score);
-
-hipError_t launch_fold_proxy(hipStream_t st, int d, int r, const float* g1, const float* wr, double* out);
+                              const int32_t* idx, const int32_t* n, const void* H, const float* g1,
+                              const float* wr, double* partial, double* pcur, const double* pref, double* score);
+// out[d][rpad] = W_r [d][r] with zero columns appended.
+hipError_t launch_pad_proxy(hipStream_t st, int d, int r, const float* wr, float* out);
 
 // ---- selection (select.hip) ----
 hipError_t launch_select(hipStream_t st, int B, int L, int k, const double* score, const uint8_t* forced,
@@ -68,6 +72,9 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
                             const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
                             int MTt_out);
 int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu);
+// Padding (elements) a packed buffer needs past its end: for weights pass 1,
+// for packed activations the buffer's row-tile count.
+size_t gemm_pad_elems(int rows_tiles);
 // Pack source columns [0, Nsrc) of a row-major [K][ld_src] weight: source
 // column tile t (32 columns) lands at packed column col0 + t*tile_stride.
 // bf16: MFMA B-fragment tiles; fp32: row-major [K][Ndst].

@@ -112,7 +112,57 @@ hipError_t launch_embed(hipStream_t st, bool bf16m, int max_rows, int B, int L, 
 
 // ---------------------------------------------------------------------------
 // Gather + RMSNorm (fp32 statistics) of the selected rows into compact A.
+// One workgroup per row; each thread holds up to RV groups of 8 consecutive
+// values in registers between the statistics and the normalised store.
 // ---------------------------------------------------------------------------
+constexpr int RV = 4;  // groups of 8 per thread: d <= 256 * 8 * RV
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+  u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
+__device__ __forceinline__ float4 sum_splits4(const float* __restrict__ p, size_t stride, int S) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t[j] = (s0 + j < S) ? *reinterpret_cast<const float4*>(p + (size_t)(s0 + j) * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) {
+        acc.x += t[j].x; acc.y += t[j].y; acc.z += t[j].z; acc.w += t[j].w;
+      }
+  }
+  return acc;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void gather_norm_kernel(int B, int L, int d, float eps, int MTt,
                                                           const int32_t* __restrict__ idx,
@@ -124,18 +174,28 @@ __global__ __launch_bounds__(256) void gather_norm_kernel(int B, int L, int d, f
   const int m = blockIdx.x;
   if (!row_of(idx, n, B, L, m, b, i)) return;
   const T* x = H + ((size_t)b * L + i) * d;
+  float v[RV][8];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    const float v = io<T>::ld(x + c);
-    ss += v * v;
+#pragma unroll
+  for (int r = 0; r < RV; ++r) {
+    const int c8 = (threadIdx.x + r * 256) * 8;
+    if (c8 < d) {
+      load8<T>(x + c8, v[r]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[r][e] * v[r][e];
+    }
   }
   ss = block_sum<4>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c8 = threadIdx.x * 8; c8 < d; c8 += 256 * 8) {
-    float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = io<T>::ld(x + c8 + j) * inv * g[c8 + j];
-    store_a8(A, m, c8, MTt, d, v);
+  for (int r = 0; r < RV; ++r) {
+    const int c8 = (threadIdx.x + r * 256) * 8;
+    if (c8 < d) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = v[r][e] * inv * g[c8 + e];
+      store_a8(A, m, c8, MTt, d, o);
+    }
   }
 }
 
@@ -172,27 +232,36 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq,
   const int nq = Hq * dh, nv = Hkv * dh, N = nq + 2 * nv, half = dh / 2;
   const size_t sstride = (size_t)M * N;
   const float* p0 = part + (size_t)m * N;
-  auto val = [&](int c) { return sum_splits(p0 + c, sstride, S); };
-  const int npairs = (Hq + Hkv) * half;
-  for (int p = threadIdx.x; p < npairs; p += 256) {
-    const int head = p / half, j = p - head * half;
+  // rotary pairs, four consecutive j per item
+  const int nquads = (Hq + Hkv) * (half / 4);
+  for (int p = threadIdx.x; p < nquads; p += 256) {
+    const int head = p / (half / 4), j = (p - head * (half / 4)) * 4;
     const int c0 = head * dh + j, c1 = c0 + half;
-    const float a = val(c0), c = val(c1);
-    const float cs = rc[(size_t)i * half + j], sn = rs[(size_t)i * half + j];
-    const float r0 = a * cs - c * sn, r1 = c * cs + a * sn;
+    const float4 a = sum_splits4(p0 + c0, sstride, S), c = sum_splits4(p0 + c1, sstride, S);
+    const float4 cs = *reinterpret_cast<const float4*>(rc + (size_t)i * half + j);
+    const float4 sn = *reinterpret_cast<const float4*>(rs + (size_t)i * half + j);
+    const float4 r0 = make_float4(a.x * cs.x - c.x * sn.x, a.y * cs.y - c.y * sn.y, a.z * cs.z - c.z * sn.z,
+                                  a.w * cs.w - c.w * sn.w);
+    const float4 r1 = make_float4(c.x * cs.x + a.x * sn.x, c.y * cs.y + a.y * sn.y, c.z * cs.z + a.z * sn.z,
+                                  c.w * cs.w + a.w * sn.w);
     if (head < Hq) {
-      io<T>::st(q + (size_t)m * nq + c0, r0);
-      io<T>::st(q + (size_t)m * nq + c1, r1);
+      store4<T>(q + (size_t)m * nq + c0, r0);
+      store4<T>(q + (size_t)m * nq + c1, r1);
     } else {
       T* kr = Kc + (((size_t)b * Hkv + (head - Hq)) * L + i) * dh;
-      io<T>::st(kr + j, r0);
-      io<T>::st(kr + j + half, r1);
+      store4<T>(kr + j, r0);
+      store4<T>(kr + j + half, r1);
     }
   }
   // V layout [b][g][L/4][dh][4]: four consecutive keys of one dimension adjacent
-  for (int c = threadIdx.x; c < nv; c += 256) {
-    const int g = c / dh, t = c - g * dh;
-    io<T>::st(Vc + ((size_t)b * Hkv + g) * L * dh + ((size_t)(i >> 2) * dh + t) * 4 + (i & 3), val(nq + nv + c));
+  for (int c4 = threadIdx.x * 4; c4 < nv; c4 += 256 * 4) {
+    const float4 v = sum_splits4(p0 + nq + nv + c4, sstride, S);
+    const int g = c4 / dh, t = c4 - g * dh;
+    T* vb = Vc + ((size_t)b * Hkv + g) * L * dh + ((size_t)(i >> 2) * dh + t) * 4 + (i & 3);
+    io<T>::st(vb, v.x);
+    io<T>::st(vb + 4, v.y);
+    io<T>::st(vb + 8, v.z);
+    io<T>::st(vb + 12, v.w);
   }
 }
 
@@ -211,7 +280,8 @@ hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, 
 }
 
 // ---------------------------------------------------------------------------
-// Output projection epilogue: h' = x + o W_o (fp32), then the FFN norm.
+// Output projection epilogue: h' = x + o W_o (fp32, split partials summed in
+// order), then the FFN norm into the next GEMM's input.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, int S, int cap, float eps, int MTt,
@@ -228,19 +298,34 @@ __global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, in
   const size_t sstride = (size_t)M * d;
   const T* x = H + ((size_t)b * L + i) * d;
   float* hp = hprime + (size_t)m * d;
+  const float* p0 = part + (size_t)m * d;
+  float v[RV][8];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    const float v = io<T>::ld(x + c) + sum_splits(part + (size_t)m * d + c, sstride, S);
-    hp[c] = v;
-    ss += v * v;
+#pragma unroll
+  for (int r = 0; r < RV; ++r) {
+    const int c8 = (threadIdx.x + r * 256) * 8;
+    if (c8 < d) {
+      load8<T>(x + c8, v[r]);
+      const float4 a = sum_splits4(p0 + c8, sstride, S), c = sum_splits4(p0 + c8 + 4, sstride, S);
+      v[r][0] += a.x; v[r][1] += a.y; v[r][2] += a.z; v[r][3] += a.w;
+      v[r][4] += c.x; v[r][5] += c.y; v[r][6] += c.z; v[r][7] += c.w;
+      *reinterpret_cast<float4*>(hp + c8) = make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
+      *reinterpret_cast<float4*>(hp + c8 + 4) = make_float4(v[r][4], v[r][5], v[r][6], v[r][7]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[r][e] * v[r][e];
+    }
   }
   ss = block_sum<4>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c8 = threadIdx.x * 8; c8 < d; c8 += 256 * 8) {
-    float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = hp[c8 + j] * inv * g2[c8 + j];
-    store_a8(A2, m, c8, MTt, d, v);
+  for (int r = 0; r < RV; ++r) {
+    const int c8 = (threadIdx.x + r * 256) * 8;
+    if (c8 < d) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = v[r][e] * inv * g2[c8 + e];
+      store_a8(A2, m, c8, MTt, d, o);
+    }
   }
 }
 
@@ -249,11 +334,11 @@ hipError_t launch_o_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, in
                              const void* H, const float* g2, float* hprime, void* A2) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(o_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, MTt, idx, n,
-                       part, (const bf16*)H, g2, hprime, (bf16*)A2);
+    hipLaunchKernelGGL(o_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, MTt,
+                       idx, n, part, (const bf16*)H, g2, hprime, (bf16*)A2);
   else
-    hipLaunchKernelGGL(o_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, MTt, idx, n,
-                       part, (const float*)H, g2, hprime, (float*)A2);
+    hipLaunchKernelGGL(o_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, MTt,
+                       idx, n, part, (const float*)H, g2, hprime, (float*)A2);
   return hipGetLastError();
 }
 
@@ -309,7 +394,12 @@ __global__ __launch_bounds__(256) void down_epilogue_kernel(int B, int L, int d,
   const size_t row = (size_t)b * L + i;
   T* o = Hout + row * d;
   const float* hp = hprime + (size_t)m * d;
-  for (int c = threadIdx.x; c < d; c += 256) io<T>::st(o + c, hp[c] + sum_splits(part + (size_t)m * d + c, sstride, S));
+  const float* p0 = part + (size_t)m * d;
+  for (int c4 = threadIdx.x * 4; c4 < d; c4 += 256 * 4) {
+    const float4 a = sum_splits4(p0 + c4, sstride, S);
+    const float4 h = *reinterpret_cast<const float4*>(hp + c4);
+    store4<T>(o + c4, make_float4(h.x + a.x, h.y + a.y, h.z + a.z, h.w + a.w));
+  }
   for (int j = threadIdx.x; j < r; j += 256) pref[row * r + j] = pcur[row * r + j];
   if (threadIdx.x == 0) score[row] = 0.0;
 }

@@ -5,9 +5,10 @@
 // largest drift score, ties to the lower index.  One 1024-thread workgroup
 // per sequence; thread t owns the contiguous rows [t*E, t*E + E).  The k-th
 // largest score is found by an exact MSB-first radix select over the fp64
-// bit patterns (non-negative doubles order like their unsigned bits), the
-// equal-score ties are ranked by an index-order scan, and the selected rows
-// are compacted in ascending order by a second scan.
+// bit patterns (non-negative doubles order like their unsigned bits), stopping
+// as soon as the bucket holding the cut is taken whole; rows equal to the
+// threshold on the resolved bits are ranked by an index-order scan, and the
+// selected rows are compacted in ascending order by a second scan.
 #include "common.h"
 #include "kernels.h"
 
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
                                                        int32_t* __restrict__ idx, int32_t* __restrict__ n_out) {
   __shared__ int hist[256];
   __shared__ int wsum[SEL_W];
-  __shared__ int pick[2];
+  __shared__ int pick[3];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int E = (L + SEL_T - 1) / SEL_T;
   const int i0 = tid * E;
@@ -111,19 +112,26 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
           if (acc < rem && rem <= acc + c[q]) {
             pick[0] = 255 - (4 * tid + q);
             pick[1] = acc;
+            pick[2] = rem == acc + c[q];  // the digit's rows are all taken: the cut is exact
           }
           acc += c[q];
         }
       }
       __syncthreads();
       const int digit = pick[0];
+      const bool done = pick[2];
       rem -= pick[1];
       prefix |= (uint64_t)digit << shift;
       pmask |= 0xFFull << shift;
       __syncthreads();
+      if (done) break;  // uniform: every thread read the same flag
     }
     thr = prefix;
-    take_eq = rem;  // rows equal to thr to take, lowest index first
+    take_eq = rem;  // rows whose masked key equals thr to take, lowest index first
+    // compare on the resolved high bits only: below the last pass every row
+    // sharing the prefix is either all taken or ranked by index
+#pragma unroll
+    for (int e = 0; e < SEL_EMAX; ++e) key[e] &= pmask;
   }
   // rank of each equal-to-threshold candidate in index order
   int neq = 0;
