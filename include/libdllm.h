@@ -61,7 +61,7 @@ enum { DLLM_MODE_AUTO = 0, DLLM_MODE_FULL = 1, DLLM_MODE_SPARSE = 2 };
 enum { DLLM_FORCED_NONE = 0, DLLM_FORCED_BLOCK = 1, DLLM_FORCED_BLOCK_RECENT = 2 };
 
 /* Model and sequence dimensions.  Limits checked by dllm_create:
- * head_dim a multiple of 8 and <= 256; d_model <= 8192 and a multiple of 32;
+ * head_dim a multiple of 32 and <= 256; d_model <= 8192 and a multiple of 32;
  * d_ffn a multiple of 32; n_q_heads a multiple of n_kv_heads;
  * seq_len <= 8192 and a multiple of 4; block_len <= 64; proxy_rank <= 128; for DLLM_BF16 the
  * widths d_model, d_ffn, n_q_heads*head_dim, n_kv_heads*head_dim and vocab
@@ -97,9 +97,12 @@ typedef struct {
  * writes lives here, so a copy of these buffers is a checkpoint. */
 typedef struct {
   void *hidden;         /* [N+1][B][L][d_model]: slot 0 = embeddings, slot l+1 = layer l output */
-  void *k_cache;        /* [N][B][n_kv_heads][L][head_dim] (post-RoPE keys) */
-  void *v_cache;        /* [N][B][n_kv_heads][L/4][head_dim][4]: value of key j,
-                         * dimension t at [j/4][t][j%4] (four keys adjacent) */
+  void *k_cache;        /* [N][B][n_kv_heads][L32/32][head_dim/16][64][8] post-RoPE keys in
+                         * matrix-core fragment order, L32 = L rounded up to 32: key j,
+                         * dimension t at [j/32][t/16][j%32 + 32*((t/8)%2)][t%8] */
+  void *v_cache;        /* [N][B][n_kv_heads][L32/16][head_dim/32][64][8] values in fragment
+                         * order: key j (o = j%16), dimension t at
+                         * [j/16][t/32][t%32 + 32*((o/4)%2)][o%4 + 4*(o/8)] */
   double *proxy_cur;    /* [N][B][L][r]  current proxy C of each row's layer input */
   double *proxy_ref;    /* [N][B][L][r]  proxy P at the row's last refresh */
   double *score;        /* [N][B][L]     drift of C against P (0 for refreshed rows) */

@@ -150,7 +150,7 @@ struct Prof {
       return e;
     }
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     m->ev_all.push_back(e);
     return e;
   }
@@ -201,11 +201,12 @@ dllm_status check_layer(const dllm_model* m, int layer) {
 void* hid(const dllm_model* m, const dllm_state* s, int slot) {
   return (char*)s->hidden + (size_t)slot * s->batch * m->d.seq_len * m->d.d_model * m->esize;
 }
+size_t l32(const dllm_dims& d) { return (size_t)((d.seq_len + 31) / 32) * 32; }
 void* kcache(const dllm_model* m, const dllm_state* s, int l) {
-  return (char*)s->k_cache + (size_t)l * s->batch * nv_of(m->d) * m->d.seq_len * m->esize;
+  return (char*)s->k_cache + (size_t)l * s->batch * nv_of(m->d) * l32(m->d) * m->esize;
 }
 void* vcache(const dllm_model* m, const dllm_state* s, int l) {
-  return (char*)s->v_cache + (size_t)l * s->batch * nv_of(m->d) * m->d.seq_len * m->esize;
+  return (char*)s->v_cache + (size_t)l * s->batch * nv_of(m->d) * l32(m->d) * m->esize;
 }
 double* pcur(const dllm_model* m, const dllm_state* s, int l) {
   return s->proxy_cur + (size_t)l * s->batch * m->d.seq_len * m->d.proxy_rank;
@@ -230,6 +231,16 @@ dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int 
   Prof prof(m, st, cls, (double)K * N * m->esize + (double)max_rows * K * m->esize + (double)max_rows * N * 4.0,
             2.0 * max_rows * (double)K * N);
   if (m->bf16) {
+    // up to 192 rows: the weight-streaming kernel, when the shape suits it
+    int ss = gemm_stream_pick_splits(max_rows, K, N, m->n_cu, act != nullptr, MTt);
+    if (ss > 0 && !act && (size_t)ss * max_rows * N > out_floats) ss = 0;
+    if (ss > 0) {
+      HIPCHK(launch_gemm_stream(st, max_rows, B, K, N, (const uint16_t*)A, MTt, (const uint16_t*)W, n_sel, out, ss,
+                                (uint16_t*)act, m->MTt));
+      *splits = ss;
+      prof.done();
+      return DLLM_OK;
+    }
     int sp = act ? 1 : gemm_bf16_pick_splits(max_rows, K, N, m->n_cu);
     while (sp > 1 && (size_t)sp * max_rows * N > out_floats) sp /= 2;
     if (!act && (size_t)sp * max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
@@ -350,7 +361,7 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
       d.vocab < 2 || d.max_batch < 1 || d.seq_len < 1 || d.block_len < 1 || d.proxy_rank < 1)
     return fail(DLLM_E_ARG, "non-positive dimension");
   if (d.dtype != DLLM_FP32 && d.dtype != DLLM_BF16) return fail(DLLM_E_ARG, "unknown dtype %d", d.dtype);
-  if (d.head_dim % 8 || d.head_dim > 256) return fail(DLLM_E_SHAPE, "head_dim must be a multiple of 8 and <= 256");
+  if (d.head_dim % 32 || d.head_dim > 256) return fail(DLLM_E_SHAPE, "head_dim must be a multiple of 32 and <= 256");
   if (d.d_model > 8192) return fail(DLLM_E_SHAPE, "d_model %d > 8192", d.d_model);
   if (d.n_q_heads % d.n_kv_heads) return fail(DLLM_E_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
   if (d.seq_len > 8192) return fail(DLLM_E_SHAPE, "seq_len %d > 8192", d.seq_len);

@@ -3,16 +3,18 @@
 // updated KV cache; dLLM attention is non-causal, so there is no mask).
 // Query head h reads KV head floor(h * Hkv / Hq).
 //
-// Cache layouts: K [B][Hkv][L][dh] (post-RoPE), V [B][Hkv][L/4][dh][4] -- four
-// consecutive keys of one head dimension are adjacent, so a lane's PV operand
-// (4 keys x 2 runs of one dimension) is two 8-byte loads.
+// Cache layouts: K and V are stored in matrix-core fragment order (see
+// kc_off/vc_off), so every fragment a wave needs is one contiguous 1 KB load
+// (16 bytes per lane), and the value fragment's key order matches the rows of
+// the score accumulator.
 //
 // bf16, dh in {64, 128}, L % 32 == 0: MFMA flash attention.  A workgroup owns
-// 32 query rows of one sequence and one head; its 4 waves split the keys and
-// each keeps an online softmax (fp32) over 32-key tiles, computing
+// 32 query rows of one sequence and one head; its 8 waves split the keys and
+// each keeps an online softmax (fp32) over 32-key tiles (the next tile's K and
+// V loads in flight during the current tile's arithmetic), computing
 // S^T = K Q^T (so a query's scores sit in one lane pair and the row max/sum need
 // one cross-lane exchange) and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16.
-// The four partial results are merged in LDS in a fixed order.  Otherwise a
+// The eight partial results are merged in LDS by a fixed-order tree.  Otherwise a
 // reference kernel (one wave per query row and head).
 #include "common.h"
 #include "kernels.h"
@@ -25,10 +27,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 size_t attn_partial_floats(int, int, int, int) { return 0; }
-
-__device__ __forceinline__ size_t vt4_off(int j, int t, int dh) {
-  return ((size_t)(j >> 2) * dh + t) * 4 + (j & 3);
-}
 
 template <typename T>
 __global__ __launch_bounds__(64) void attn_ref_kernel(int B, int L, int Hq, int Hkv, int dh, float scale,
@@ -46,13 +44,12 @@ __global__ __launch_bounds__(64) void attn_ref_kernel(int B, int L, int Hq, int 
   const T* qr = q + (size_t)m * Hq * dh + (size_t)h * dh;
   for (int t = lane; t < dh; t += 64) qs[t] = io<T>::ld(qr + t);
   __syncthreads();
-  const T* K = Kc + ((size_t)b * Hkv + g) * L * dh;
-  const T* V = Vc + ((size_t)b * Hkv + g) * L * dh;
+  const T* K = Kc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * dh;
+  const T* V = Vc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * dh;
   float mx = -INFINITY;
   for (int j = lane; j < L; j += 64) {
-    const T* kr = K + (size_t)j * dh;
     float s = 0.f;
-    for (int t = 0; t < dh; ++t) s = fmaf(qs[t], io<T>::ld(kr + t), s);
+    for (int t = 0; t < dh; ++t) s = fmaf(qs[t], io<T>::ld(K + kc_off(j, t, dh)), s);
     s *= scale;
     ps[j] = s;
     mx = fmaxf(mx, s);
@@ -69,15 +66,15 @@ __global__ __launch_bounds__(64) void attn_ref_kernel(int B, int L, int Hq, int 
   const float inv = 1.0f / sum;
   for (int t = lane; t < dh; t += 64) {
     float acc = 0.f;
-    for (int j = 0; j < L; ++j) acc = fmaf(ps[j], io<T>::ld(V + vt4_off(j, t, dh)), acc);
+    for (int j = 0; j < L; ++j) acc = fmaf(ps[j], io<T>::ld(V + vc_off(j, t, dh)), acc);
     store_a1(out, m, h * dh + t, MTt, Hq * dh, acc * inv);
   }
 }
 
-constexpr int ATT_NW = 4;
+constexpr int ATT_NW = 8;
 
 template <int DH>
-__global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, int Hq, int Hkv, float sl2e, int cap,
+__global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, int Hq, int Hkv, int ntq, float sl2e, int cap,
                                                                 const int32_t* __restrict__ n,
                                                                 const bf16* __restrict__ q,
                                                                 const bf16* __restrict__ Kc,
@@ -86,10 +83,15 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   constexpr int KS = DH / 16;  // k-steps of S^T
   constexpr int DT = DH / 32;  // d-tiles of O^T
   __shared__ float ms[ATT_NW][32], ls[ATT_NW][32];
-  __shared__ f32x16_t ox[2][DT][64];
-  const int h = blockIdx.y;
+  __shared__ float ox[ATT_NW / 2][DT][16][64];  // element i of lane l at [i][l]: no bank conflicts
+  // Workgroups are dealt round-robin to the 8 XCDs; remap so that the query
+  // tiles of one head run on one XCD and share its K/V through that L2.
+  const int G = gridDim.x;  // ntq * Hq rounded up to a multiple of 8
+  const int wl = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int h = wl / ntq;
+  if (h >= Hq) return;
   // query tile -> (sequence, first compact row)
-  int T = blockIdx.x, b = -1, off = 0, nb = 0;
+  int T = wl - h * ntq, b = -1, off = 0, nb = 0;
   for (int bb = 0; bb < B; ++bb) {
     const int c = min(max(n[bb], 0), L);
     const int nt = (c + 31) >> 5;
@@ -116,8 +118,8 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   for (int ks = 0; ks < KS; ++ks) {
     qf[ks] = qv ? *reinterpret_cast<const u32x4*>(qrow + ks * 16) : u32x4{0u, 0u, 0u, 0u};
   }
-  const bf16* Kb = Kc + ((size_t)b * Hkv + g) * L * DH;
-  const bf16* Vb = Vc + ((size_t)b * Hkv + g) * L * DH;
+  const bf16* Kb = Kc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * DH;
+  const bf16* Vb = Vc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * DH;
   const int ntiles = L >> 5;
   const int t_beg = (wv * ntiles) / ATT_NW, t_end = ((wv + 1) * ntiles) / ATT_NW;
 
@@ -128,65 +130,81 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int kt = t_beg; kt < t_end; ++kt) {
-    const int key0 = kt * 32;
-    u32x4 kf[KS];
-    const bf16* krow = Kb + (size_t)(key0 + ln) * DH + 8 * hlf;
+  // K fragment (A operand of S^T) of key tile kt and dims ks*16 ..: 1 KB at
+  // ((kt*KS + ks)*64 + lane)*8; V fragment (A operand of O^T) of 16-key block
+  // kb and dims dt*32 ..: 1 KB at ((kb*DT + dt)*64 + lane)*8.
+  struct KV {
+    u32x4 k[KS];
+    u32x4 v[2][DT];
+  };
+  auto load_kv = [&](int kt, KV& t) {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(Kb) + (size_t)kt * KS * 64 + lane;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const u32x4*>(krow + ks * 16);
-    // V^T fragments: d = dt*32 + ln, keys kk*16 + hlf*4 + {0..3} and kk*16 + 8 + hlf*4 + {0..3}
-    u32x2 vlo[2][DT], vhi[2][DT];
+    for (int ks = 0; ks < KS; ++ks) t.k[ks] = kp[ks * 64];
+    const u32x4* vp = reinterpret_cast<const u32x4*>(Vb) + (size_t)kt * 2 * DT * 64 + lane;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int g1 = (key0 >> 2) + kk * 4 + hlf;
-        vlo[kk][dt] = *reinterpret_cast<const u32x2*>(Vb + ((size_t)g1 * DH + dt * 32 + ln) * 4);
-        vhi[kk][dt] = *reinterpret_cast<const u32x2*>(Vb + ((size_t)(g1 + 2) * DH + dt * 32 + ln) * 4);
-      }
+      for (int dt = 0; dt < DT; ++dt) t.v[kk][dt] = vp[(kk * DT + dt) * 64];
+  };
+  auto tile = [&](const KV& t, bool rescale) {
     f32x16_t s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, t.k[ks]),
                                                   __builtin_bit_cast(bf16x8_t, qf[ks]), s, 0, 0, 0);
     float mt = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2e;
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float p[16], rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p[i] = exp2f(s[i] * sl2e - m_new);
+      p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2e, -m_new));
       rs += p[i];
     }
     rs += __shfl_xor(rs, 32, 64);
     l_run = l_run * alpha + rs;
     m_run = m_new;
+    if (rescale) {  // o is still zero on a wave's first tile
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 pf;
-      pf.x = (uint32_t)f2bf(p[8 * kk + 0]) | ((uint32_t)f2bf(p[8 * kk + 1]) << 16);
-      pf.y = (uint32_t)f2bf(p[8 * kk + 2]) | ((uint32_t)f2bf(p[8 * kk + 3]) << 16);
-      pf.z = (uint32_t)f2bf(p[8 * kk + 4]) | ((uint32_t)f2bf(p[8 * kk + 5]) << 16);
-      pf.w = (uint32_t)f2bf(p[8 * kk + 6]) | ((uint32_t)f2bf(p[8 * kk + 7]) << 16);
+      pf.x = pack2bf(p[8 * kk + 0], p[8 * kk + 1]);
+      pf.y = pack2bf(p[8 * kk + 2], p[8 * kk + 3]);
+      pf.z = pack2bf(p[8 * kk + 4], p[8 * kk + 5]);
+      pf.w = pack2bf(p[8 * kk + 6], p[8 * kk + 7]);
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 va{vlo[kk][dt].x, vlo[kk][dt].y, vhi[kk][dt].x, vhi[kk][dt].y};
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va), pb, o[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, t.v[kk][dt]), pb, o[dt], 0, 0, 0);
+    }
+  };
+
+  // the next tile's loads are in flight while the current one is multiplied
+  // (the prefetch index is clamped, so every load is unconditional and in range)
+  if (t_beg < t_end) {
+    KV ta, tb;
+    load_kv(t_beg, ta);
+    for (int kt = t_beg; kt < t_end; kt += 2) {
+      load_kv(min(kt + 1, t_end - 1), tb);
+      tile(ta, kt != t_beg);
+      if (kt + 1 >= t_end) break;
+      load_kv(min(kt + 2, t_end - 1), ta);
+      tile(tb, true);
     }
   }
 
-  // merge the waves' partial softmax states in a fixed order
+  // merge the waves' partial softmax states: a fixed-order tree in LDS
   if (lane < 32) {
     ms[wv][ln] = m_run;
     ls[wv][ln] = l_run;
@@ -203,27 +221,28 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] *= f;
-  if (wv >= 2) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) ox[wv - 2][dt][lane] = o[dt];
-  }
-  __syncthreads();
-  if (wv < 2) {
+  for (int half = ATT_NW / 2; half >= 1; half >>= 1) {
+    if (wv >= half && wv < 2 * half) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] += ox[wv][dt][lane];
-  }
-  __syncthreads();
-  if (wv == 1) {
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) ox[0][dt][lane] = o[dt];
+        for (int i = 0; i < 16; ++i) ox[wv - half][dt][i][lane] = o[dt][i];
+    }
+    __syncthreads();
+    if (wv < half) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] += ox[wv][dt][i][lane];
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (wv != 0) return;
   const float inv = 1.0f / lg;
   const int m = r0 + ln;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    o[dt] += ox[0][dt][lane];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       float mine[4], part[4];
@@ -253,13 +272,14 @@ hipError_t launch_attention(hipStream_t st, bool bf16m, int max_rows, int B, int
   const float scale = 1.0f / sqrtf((float)dh);
   if (bf16m && (dh == 128 || dh == 64) && L % 32 == 0) {
     const float sl2e = scale * 1.4426950408889634f;
-    dim3 grid((max_rows + 31) / 32 + B, Hq);
+    const int ntq = (max_rows + 31) / 32 + B;  // query tiles per head, an upper bound
+    const int grid = (ntq * Hq + 7) / 8 * 8;
     if (dh == 128)
-      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, sl2e, max_rows, n,
-                         (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt);
+      hipLaunchKernelGGL(attn_mfma_kernel<128>, dim3(grid), dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, ntq, sl2e,
+                         max_rows, n, (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt);
     else
-      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, sl2e, max_rows, n,
-                         (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt);
+      hipLaunchKernelGGL(attn_mfma_kernel<64>, dim3(grid), dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, ntq, sl2e,
+                         max_rows, n, (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt);
     return hipGetLastError();
   }
   const size_t lds = (size_t)(dh + L) * sizeof(float);

@@ -10,13 +10,18 @@ typedef uint16_t bf16;  // raw bfloat16 storage
 
 __device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float(((uint32_t)v) << 16); }
 
-// float -> bfloat16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bfloat16 pair (a in the low half), round to nearest
+// even: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  const f32x2_hw v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
 }
+
+// float -> bfloat16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16 f2bf(float f) { return (bf16)(pack2bf(f, 0.0f) & 0xffffu); }
 
 template <typename T> struct io;
 template <> struct io<float> {
@@ -96,15 +101,29 @@ __device__ __forceinline__ size_t apack_off(int m, int k, int MTt) {
   return (((size_t)kt * MTt + mt) * 64 + lane) * 8 + (k & 7);
 }
 
+// Key/value cache offsets inside one (sequence, kv head) block of L32 * dh
+// elements (L32 = L rounded up to 32), in matrix-core fragment order: a wave
+// reads the fragment of 32 keys x 16 dims (K) or 16 keys x 32 dims (V) as one
+// contiguous 1 KB.  The key order inside a V fragment matches the row order of
+// the score tile's accumulator, so probabilities feed the next MFMA in place.
+__device__ __forceinline__ size_t kc_off(int j, int t, int dh) {
+  return (((size_t)(j >> 5) * (dh >> 4) + (t >> 4)) * 64 + (j & 31) + 32 * ((t >> 3) & 1)) * 8 + (t & 7);
+}
+__device__ __forceinline__ size_t vc_off(int j, int t, int dh) {
+  const int o = j & 15;
+  return (((size_t)(j >> 4) * (dh >> 5) + (t >> 5)) * 64 + (t & 31) + 32 * ((o >> 2) & 1)) * 8 + (o & 3) + 4 * (o >> 3);
+}
+__device__ __forceinline__ int l32_of(int L) { return (L + 31) & ~31; }
+
 // Store 8 consecutive values of row m starting at column k8 (a multiple of 8)
 // of a GEMM input: packed fragments for bf16 (one 16-byte store), row-major
 // [..][ld] for fp32.
 __device__ __forceinline__ void store_a8(bf16* A, int m, int k8, int MTt, int /*ld*/, const float* v) {
   uint4 w;
-  w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  w.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-  w.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  w.x = pack2bf(v[0], v[1]);
+  w.y = pack2bf(v[2], v[3]);
+  w.z = pack2bf(v[4], v[5]);
+  w.w = pack2bf(v[6], v[7]);
   *reinterpret_cast<uint4*>(A + apack_off(m, k8, MTt)) = w;
 }
 __device__ __forceinline__ void store_a8(float* A, int m, int k8, int /*MTt*/, int ld, const float* v) {

@@ -315,6 +315,227 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
 }
 
 // ---------------------------------------------------------------------------
+// Weight-streaming bf16 GEMM for up to 192 rows (6 row tiles).
+//
+// Workgroup = 4 waves and a 128-column slab; wave w owns column tile w of the
+// slab and every row tile.  Each wave streams its own weight tile straight
+// from HBM into a register ring of 4*NA k16 steps (no LDS on the weight
+// path); the activation chunk (64 k, all row tiles) is loaded once per
+// workgroup, staged in a triple-buffered LDS ring and shared by the 4 waves,
+// and the next step's activation fragments are read from LDS while the
+// current step multiplies.  Activation chunks are loaded NA+1 chunks ahead:
+// vmcnt counts loads in issue order, so both streams must be consumed at the
+// same distance or a wait for one drains the other.  EPI as above.
+// ---------------------------------------------------------------------------
+constexpr int GS_KC = 4;  // k16 steps per activation chunk
+
+// NA activation chunks in flight in registers; weight ring depth 4*NA steps, so
+// that both streams are waited for at the same distance (vmcnt is in order).
+template <int MT, int NA, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __restrict__ Ap, int MTt,
+                                                       const u32x4* __restrict__ Wp, float* __restrict__ out,
+                                                       uint16_t* __restrict__ act, int MTt_out,
+                                                       const int32_t* __restrict__ n_sel, int B, int K, int N,
+                                                       int kps, int n_slabs, int total, int cap) {
+  extern __shared__ u32x4 lds[];  // A ring: [3][GS_KC][MT][64]
+  constexpr int ABUF = GS_KC * MT * 64;
+  const int G = gridDim.x;
+  const int w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (w >= total) return;
+  const int slab = w % n_slabs, split = w / n_slabs;
+  const int M = total_rows(n_sel, B, cap);
+  if (M <= 0) return;
+  const int m_tiles = (M + 31) >> 5;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NT = N >> 5, KT = K >> 4;
+  const int nt = min(slab * 4 + wv, NT - 1);
+  const int kt0 = (split * kps) >> 4;
+  constexpr int GS_D = GS_KC * NA;  // weight ring depth (k16 steps)
+  const int nsteps = kps >> 4, nch = nsteps / GS_KC, nsup = nsteps / GS_D;
+
+  // weight ring: slot j holds step s with s % GS_D == j
+  const u32x4* wsrc = Wp + ((size_t)nt * KT + kt0) * 64 + lane;
+  u32x4 wr[GS_D];
+#pragma unroll
+  for (int j = 0; j < GS_D; ++j) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(j, nsteps - 1) * 64);
+
+  // activation chunk c: wave wv loads step wv of the chunk for every row tile
+  const u32x4* asrc = Ap + (size_t)(kt0 + wv) * MTt * 64 + lane;
+  u32x4 ra[NA][MT];
+  auto load_a = [&](int c, u32x4* dst) {
+    const int cc = min(c, nch - 1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      dst[mt] = asrc[((size_t)cc * GS_KC * MTt + min(mt, m_tiles - 1)) * 64];
+  };
+  auto store_a = [&](int buf, const u32x4* src) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) lds[buf * ABUF + (wv * MT + mt) * 64 + lane] = src[mt];
+  };
+  auto read_af = [&](int buf, int st, u32x4* dst) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) dst[mt] = lds[buf * ABUF + (st * MT + mt) * 64 + lane];
+  };
+
+  f32x16_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+
+  // LDS holds chunks c and c+1 while chunk c is multiplied; chunks c+2 ..
+  // c+NA+1 are in flight in registers (slot x % NA).
+  load_a(0, ra[0]);
+  load_a(1, ra[1 % NA]);
+  store_a(0, ra[0]);
+  store_a(1, ra[1 % NA]);
+#pragma unroll
+  for (int x = 2; x < NA + 2; ++x) load_a(x, ra[x % NA]);
+  __syncthreads();
+  u32x4 af[2][MT];
+  read_af(0, 0, af[0]);
+  int b0 = 0, b1 = 1, b2 = 2;  // LDS slots of chunks c, c+1, c+2
+  for (int sc = 0; sc < nsup; ++sc) {
+#pragma unroll
+    for (int cc = 0; cc < NA; ++cc) {
+      const int c = sc * NA + cc;
+#pragma unroll
+      for (int st = 0; st < GS_KC; ++st) {
+        const int j = cc * GS_KC + st;
+        const int s = c * GS_KC + st;
+        // the next step's activation fragments are read while this step multiplies
+        if (st + 1 < GS_KC) read_af(b0, st + 1, af[(j + 1) & 1]);
+        else read_af(b1, 0, af[(j + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, wr[j]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[j & 1][mt]), b, acc[mt],
+                                                            0, 0, 0);
+        // refill the slot only after its last use, so the new load can take
+        // the same registers (no copy of an in-flight load at the back edge)
+        __builtin_amdgcn_sched_barrier(0);
+        wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(s + GS_D, nsteps - 1) * 64);
+        if (st == 0) load_a(c + NA + 1, ra[(cc + 1) % NA]);
+      }
+      store_a(b2, ra[(cc + 2) % NA]);
+      __syncthreads();
+      const int t = b0;
+      b0 = b1;
+      b1 = b2;
+      b2 = t;
+    }
+  }
+
+  if constexpr (EPI == 0) {
+    const int ncol = nt * 32 + (lane & 31);
+    if (slab * 4 + wv < NT) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt >= m_tiles) break;
+        const int mrow = mt * 32 + (lane >> 5) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = mrow + (i >> 2) * 8 + (i & 3);
+          if (m < M) out[((size_t)split * M + m) * N + ncol] = acc[mt][i];
+        }
+      }
+    }
+  } else {
+    // gate tile 2p (wave 2p), up tile 2p+1 (wave 2p+1): exchange through LDS
+    float* ex = reinterpret_cast<float*>(lds);  // [2][MT][16][64]
+    const int p = wv >> 1;
+    if (wv & 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ex[((p * MT + mt) * 16 + i) * 64 + lane] = acc[mt][i];
+    }
+    __syncthreads();
+    if (!(wv & 1) && slab * 4 + wv + 1 < NT) {
+      const int f = (slab * 2 + p) * 32 + (lane & 31);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt >= m_tiles) break;
+        const int mrow = mt * 32 + (lane >> 5) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = mrow + (i >> 2) * 8 + (i & 3);
+          if (m < M) {
+            const float g = acc[mt][i], u = ex[((p * MT + mt) * 16 + i) * 64 + lane];
+            act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
+          }
+        }
+      }
+    }
+  }
+}
+
+
+template <int MT, int NA, int EPI>
+static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
+                             uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
+                             int n_slabs, int total, int cap) {
+  static bool attr_set = false;
+  const size_t lds = (size_t)3 * GS_KC * MT * 64 * 16;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_stream_kernel<MT, NA, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_stream_kernel<MT, NA, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
+                     (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, cap);
+  return hipGetLastError();
+}
+
+static int stream_mt(int max_rows) {
+  const int t = (max_rows + 31) / 32;
+  return t <= 2 ? 2 : (t <= 4 ? 4 : (t <= 6 ? 6 : -1));
+}
+
+// Split count for the streaming kernel: K must split into multiples of 256;
+// the largest split whose workgroup count still fits the chip in one pass (one
+// per CU).  0 when the shape does not suit the kernel (more than 192 rows, or
+// more row tiles than the activation buffer holds).
+int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, int MTt) {
+  const int mt = stream_mt(max_rows);
+  if (mt < 0 || mt > MTt || N % 128 != 0 || K % 256 != 0) return 0;
+  if (fused) return 1;
+  const int n_slabs = N / 128;
+  int best = 1;
+  for (int s = 2; s <= 32 && s <= K / 256; ++s)
+    if ((K / 256) % s == 0 && n_slabs * s <= n_cu) best = s;
+  return best;
+}
+
+hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
+                              const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
+                              int MTt_out) {
+  if (max_rows <= 0) return hipSuccess;
+  const int mt = stream_mt(max_rows);
+  if (mt < 0 || mt > MTt || N % 128 != 0 || splits < 1) return hipErrorInvalidValue;
+  const int n_slabs = N / 128;
+  const int kps = K / splits;
+  if (kps * splits != K || kps % (16 * GS_KC * 4) != 0) return hipErrorInvalidValue;
+  if (act != nullptr && splits != 1) return hipErrorInvalidValue;
+  const int total = n_slabs * splits;
+  const int grid = (total + 7) / 8 * 8;
+#define GSL(MT_, EPI_) \
+  stream_cfg<MT_, 4, EPI_>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, max_rows)
+  if (act == nullptr) {
+    if (mt == 2) return GSL(2, 0);
+    if (mt == 4) return GSL(4, 0);
+    return GSL(6, 0);
+  }
+  if (mt == 2) return GSL(2, 1);
+  if (mt == 4) return GSL(4, 1);
+  return GSL(6, 1);
+#undef GSL
+}
+
+// ---------------------------------------------------------------------------
 // fp32 GEMM (fp32 models): 64x64 tiles, 4x4 outputs per thread.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,

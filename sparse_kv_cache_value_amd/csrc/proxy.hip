@@ -4,30 +4,30 @@
 // at the row's last refresh (lowest similarity = most drift).
 //
 // Every decision-feeding quantity is fp64.  The normalised input's gain g1 is
-// applied to x in fp64 (exactly), and the basis is kept in fp32 as given, so
-// every product x*g1*w is rounded exactly once, as in the fp64 definition; only
-// the order of the fp64 sum differs.
+// applied to x in fp64 (exactly: at most 24+24 significant bits), the basis is
+// kept in fp32 as given and widened exactly, and the products are accumulated
+// by v_mfma_f64_16x16x4_f64, so the result is the fp64 definition up to the
+// order of the fp64 sum.
 #include "common.h"
 #include "kernels.h"
 
 namespace dllm {
 
-constexpr int PX_KC = 32;      // k per LDS chunk
+constexpr int PX_KC = 32;      // k per chunk: 8 MFMA steps of 4
+constexpr int PX_NCT = 2;      // 16-column tiles per wave
 constexpr int PX_TARGET = 512;  // workgroups to aim for
-constexpr int PX_SMAX = 32;     // most K splits (bounds the partial traffic)
-constexpr int PX_RPT = 8;       // rows per thread
+constexpr int PX_SMAX = 32;    // most partial splits
 
 // Basis width as stored: r rounded up to 32, 64 or 128 (zero columns).
 int proxy_rpad(int r) { return r <= 32 ? 32 : (r <= 64 ? 64 : 128); }
 
-static int proxy_rows_per_wg(int rpad) { return (256 / rpad) * PX_RPT; }
-
+// Partial splits across workgroups; each workgroup's 4 waves split its K
+// range again and are summed in LDS.
 static int proxy_splits(int max_rows, int d, int rpad) {
-  const int rm = proxy_rows_per_wg(rpad);
-  const int rt = (max_rows + rm - 1) / rm;
-  const int kt = d / PX_KC;
+  const int tasks = ((max_rows + 15) / 16) * (rpad / 16 / PX_NCT);
+  const int kq = d / PX_KC;  // k chunks
   int s = 1;
-  while (s * 2 <= kt && kt % (s * 2) == 0 && rt * s * 2 <= PX_TARGET && s * 2 <= PX_SMAX) s *= 2;
+  while (s * 2 <= PX_SMAX && kq % (s * 2) == 0 && kq / (s * 2) >= 4 && tasks * s * 2 <= PX_TARGET) s *= 2;
   return s;
 }
 
@@ -65,110 +65,111 @@ struct XVec<float> {
   }
 };
 
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
 // partial[s][m][j] = sum over k in split s of (x[m][k] g1[k]) W_r[k][j].
-// Thread (rg, j) owns column j of rows rg*8 .. rg*8+7 of the workgroup's
-// tile; chunks of 32 k are staged in LDS as fp64, the next chunk's global
-// loads issued before the current chunk's arithmetic.  x*g1 is exact in fp64
-// (at most 24+24 significant bits), so each FMA rounds the exact triple
-// product once, as the fp64 definition does.
-template <typename T, int RPAD>
-__global__ __launch_bounds__(256) void proxy_partial_kernel(int B, int L, int d, int kps, int cap,
+// A workgroup owns 16 rows x (16 * PX_NCT) columns and a K range whose 32-k
+// chunks its 4 waves split four ways.  In MFMA step t of a 32-k chunk, lane l = i + 16 q
+// supplies A[i][q] = x[row i][k0 + 8q + t] g1[k0 + 8q + t] and
+// B[q][j] = W_r[k0 + 8q + t][col j] (any assignment of k to the four MFMA
+// k-slots sums the same terms), so a lane's A values for a chunk are 8
+// consecutive inputs (one 16-byte load) and its B values are 8 consecutive
+// fp32 of the packed basis.
+template <typename T>
+__global__ __launch_bounds__(256) void proxy_partial_kernel(int B, int L, int d, int rpad, int kps, int cap,
                                                             const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ n,
                                                             const T* __restrict__ H,
                                                             const float* __restrict__ g1,
-                                                            const float* __restrict__ wr,
+                                                            const float* __restrict__ wp,
                                                             double* __restrict__ partial) {
-  constexpr int RG = 256 / RPAD, RM = RG * PX_RPT;
   constexpr int XV = XVec<T>::N;
-  constexpr int XLOADS = (RM * PX_KC / XV + 255) / 256;
-  constexpr int WLOADS = PX_KC * RPAD / 4 / 256;
-  constexpr int XS = PX_KC + 2;  // row stride (doubles): 16-byte aligned pairs
-  __shared__ __align__(16) double xs[RM * XS];
-  __shared__ double ws[PX_KC * RPAD];
-  __shared__ long long rowoff[RM];
+  __shared__ f64x4_t red[3][PX_NCT][64];
   const int M = total_rows(n, B, cap);
-  const int r0 = blockIdx.x * RM;
-  if (r0 >= M) return;
-  const int tid = threadIdx.x, j = tid % RPAD, rg = tid / RPAD;
-  if (tid < RM) {
-    int b, i;
-    rowoff[tid] = (r0 + tid < M && row_of(idx, n, B, L, r0 + tid, b, i)) ? (long long)((size_t)b * L + i) * d : -1;
+  const int ncg = rpad / (16 * PX_NCT);
+  const int task = blockIdx.x;
+  const int rt = task / ncg, cg = task % ncg;
+  if (rt * 16 >= M) return;
+  const int tid = threadIdx.x, lane = tid & 63, i = lane & 15, q = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = rt * 16 + i;
+  long long off = -1;
+  {
+    int b, li;
+    if (m < M && row_of(idx, n, B, L, m, b, li)) off = (long long)((size_t)b * L + li) * d;
+  }
+  const bool valid = off >= 0;
+  const T* xrow = H + (valid ? off : 0) + 8 * q;  // rows past M read row 0 and are zeroed
+  // this wave's chunks of the workgroup's K range
+  const int nch = kps / PX_KC;
+  const int c_beg = blockIdx.y * nch + (wv * nch) / 4;
+  const int c_end = blockIdx.y * nch + ((wv + 1) * nch) / 4;
+  const int nct = rpad / 16;
+  f64x4_t acc[PX_NCT];
+#pragma unroll
+  for (int c = 0; c < PX_NCT; ++c) acc[c] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  // one chunk's raw loads; the next chunk's are in flight during this one's MFMAs
+  struct Raw {
+    typename XVec<T>::V x[8 / XV];
+    float4 g[2];
+    float4 w[PX_NCT][2];
+  };
+  auto fetch = [&](int kc, Raw& r) {
+    const int k0 = kc * PX_KC;
+#pragma unroll
+    for (int h = 0; h < 8 / XV; ++h) r.x[h] = *reinterpret_cast<const typename XVec<T>::V*>(xrow + k0 + h * XV);
+    r.g[0] = *reinterpret_cast<const float4*>(g1 + k0 + 8 * q);
+    r.g[1] = *reinterpret_cast<const float4*>(g1 + k0 + 8 * q + 4);
+#pragma unroll
+    for (int c = 0; c < PX_NCT; ++c) {
+      const float* wsrc = wp + (((size_t)kc * nct + cg * PX_NCT + c) * 64 + lane) * 8;
+      r.w[c][0] = *reinterpret_cast<const float4*>(wsrc);
+      r.w[c][1] = *reinterpret_cast<const float4*>(wsrc + 4);
+    }
+  };
+  auto mma = [&](const Raw& r) {
+    double a[8];
+#pragma unroll
+    for (int h = 0; h < 8 / XV; ++h) XVec<T>::unpack(r.x[h], a + h * XV);
+    const float g[8] = {r.g[0].x, r.g[0].y, r.g[0].z, r.g[0].w, r.g[1].x, r.g[1].y, r.g[1].z, r.g[1].w};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) a[t] = valid ? a[t] * (double)g[t] : 0.0;
+#pragma unroll
+    for (int c = 0; c < PX_NCT; ++c) {
+      const double w[8] = {r.w[c][0].x, r.w[c][0].y, r.w[c][0].z, r.w[c][0].w,
+                           r.w[c][1].x, r.w[c][1].y, r.w[c][1].z, r.w[c][1].w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[t], w[t], acc[c], 0, 0, 0);
+    }
+  };
+  if (c_beg < c_end) {
+    Raw ra, rb;
+    fetch(c_beg, ra);
+    for (int c = c_beg; c < c_end; c += 2) {
+      fetch(min(c + 1, c_end - 1), rb);
+      mma(ra);
+      if (c + 1 >= c_end) break;
+      fetch(min(c + 2, c_end - 1), ra);
+      mma(rb);
+    }
+  }
+  // sum the four waves' K ranges in a fixed order
+  if (wv > 0) {
+#pragma unroll
+    for (int c = 0; c < PX_NCT; ++c) red[wv - 1][c][lane] = acc[c];
   }
   __syncthreads();
-  const int kbeg = blockIdx.y * kps, nch = kps / PX_KC;
-  typename XVec<T>::V xr[XLOADS];
-  float4 gr[XLOADS][XV / 4];
-  float4 wrg[WLOADS];
-  auto fetch = [&](int k0) {
+  if (wv != 0) return;
 #pragma unroll
-    for (int q = 0; q < XLOADS; ++q) {
-      const int e = tid + 256 * q, row = e / (PX_KC / XV), kk = (e % (PX_KC / XV)) * XV;
-      const long long off = (e < RM * PX_KC / XV) ? rowoff[row] : -1;
-      if (off >= 0) {
-        xr[q] = *reinterpret_cast<const typename XVec<T>::V*>(H + off + k0 + kk);
+  for (int c = 0; c < PX_NCT; ++c) {
 #pragma unroll
-        for (int h = 0; h < XV / 4; ++h) gr[q][h] = *reinterpret_cast<const float4*>(g1 + k0 + kk + 4 * h);
-      } else {
-        xr[q] = {};
+    for (int w2 = 0; w2 < 3; ++w2) acc[c] += red[w2][c][lane];
+    // D register e of lane l holds row l / 16 + 4 e, column l % 16
 #pragma unroll
-        for (int h = 0; h < XV / 4; ++h) gr[q][h] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int mr = rt * 16 + q + 4 * e;
+      if (mr < M) partial[((size_t)blockIdx.y * M + mr) * rpad + (cg * PX_NCT + c) * 16 + i] = acc[c][e];
     }
-#pragma unroll
-    for (int q = 0; q < WLOADS; ++q) {
-      const int e = tid + 256 * q;
-      wrg[q] = *reinterpret_cast<const float4*>(wr + (size_t)(k0 + e / (RPAD / 4)) * RPAD + (e % (RPAD / 4)) * 4);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int q = 0; q < XLOADS; ++q) {
-      const int e = tid + 256 * q;
-      if (e < RM * PX_KC / XV) {
-        const int row = e / (PX_KC / XV), kk = (e % (PX_KC / XV)) * XV;
-        double xv[XV];
-        XVec<T>::unpack(xr[q], xv);
-#pragma unroll
-        for (int h = 0; h < XV / 4; ++h) {
-          xs[row * XS + kk + 4 * h + 0] = xv[4 * h + 0] * (double)gr[q][h].x;
-          xs[row * XS + kk + 4 * h + 1] = xv[4 * h + 1] * (double)gr[q][h].y;
-          xs[row * XS + kk + 4 * h + 2] = xv[4 * h + 2] * (double)gr[q][h].z;
-          xs[row * XS + kk + 4 * h + 3] = xv[4 * h + 3] * (double)gr[q][h].w;
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < WLOADS; ++q) {
-      const int e = tid + 256 * q;
-      double* w = ws + (e / (RPAD / 4)) * RPAD + (e % (RPAD / 4)) * 4;
-      w[0] = wrg[q].x; w[1] = wrg[q].y; w[2] = wrg[q].z; w[3] = wrg[q].w;
-    }
-  };
-  double acc[PX_RPT];
-#pragma unroll
-  for (int a = 0; a < PX_RPT; ++a) acc[a] = 0.0;
-  fetch(kbeg);
-  for (int c = 0; c < nch; ++c) {
-    stage();
-    __syncthreads();
-    if (c + 1 < nch) fetch(kbeg + (c + 1) * PX_KC);
-#pragma unroll 4
-    for (int kk = 0; kk < PX_KC; kk += 2) {
-      const double w0 = ws[kk * RPAD + j], w1 = ws[(kk + 1) * RPAD + j];
-#pragma unroll
-      for (int a = 0; a < PX_RPT; ++a) {
-        const double2 xv = *reinterpret_cast<const double2*>(xs + (rg * PX_RPT + a) * XS + kk);
-        acc[a] = fma(xv.x, w0, acc[a]);
-        acc[a] = fma(xv.y, w1, acc[a]);
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < PX_RPT; ++a) {
-    const int m = r0 + rg * PX_RPT + a;
-    if (m < M) partial[((size_t)blockIdx.y * M + m) * RPAD + j] = acc[a];
   }
 }
 
@@ -264,22 +265,14 @@ hipError_t launch_proxy_drift(hipStream_t st, bool bf16m, int max_rows, int B, i
   const int rpad = proxy_rpad(r);
   const int S = proxy_splits(max_rows, d, rpad);
   const int kps = d / S;
-  const int rm = proxy_rows_per_wg(rpad);
-  dim3 grid((max_rows + rm - 1) / rm, S);
-#define PX_LAUNCH(T, RP)                                                                                  \
-  hipLaunchKernelGGL((proxy_partial_kernel<T, RP>), grid, dim3(256), 0, st, B, L, d, kps, max_rows, idx, n, \
-                     (const T*)H, g1, wr, partial)
-#define PX_BY_RPAD(T)          \
-  if (rpad == 32) PX_LAUNCH(T, 32);  \
-  else if (rpad == 64) PX_LAUNCH(T, 64); \
-  else PX_LAUNCH(T, 128);
-  if (bf16m) {
-    PX_BY_RPAD(bf16)
-  } else {
-    PX_BY_RPAD(float)
-  }
-#undef PX_BY_RPAD
-#undef PX_LAUNCH
+  const int tasks = ((max_rows + 15) / 16) * (rpad / 16 / PX_NCT);
+  dim3 grid(tasks, S);
+  if (bf16m)
+    hipLaunchKernelGGL(proxy_partial_kernel<bf16>, grid, dim3(256), 0, st, B, L, d, rpad, kps, max_rows, idx, n,
+                       (const bf16*)H, g1, wr, partial);
+  else
+    hipLaunchKernelGGL(proxy_partial_kernel<float>, grid, dim3(256), 0, st, B, L, d, rpad, kps, max_rows, idx, n,
+                       (const float*)H, g1, wr, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 #define PF_LAUNCH(RP)                                                                                              \
@@ -292,18 +285,24 @@ hipError_t launch_proxy_drift(hipStream_t st, bool bf16m, int max_rows, int B, i
   return hipGetLastError();
 }
 
-// Stored basis: W_r as fp32 [d][rpad], columns r .. rpad-1 zero.
-__global__ void pad_proxy_kernel(int d, int r, int rpad, const float* __restrict__ wr, float* __restrict__ out) {
+// Packed basis: fp32, element (kc, ct, lane l = i + 16 q, t) = W_r[32 kc + 8 q + t][16 ct + i],
+// zero for columns >= r.
+__global__ void pack_proxy_kernel(int d, int r, int rpad, const float* __restrict__ wr, float* __restrict__ out) {
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= (size_t)d * rpad) return;
-  const int k = (int)(e / rpad), j = (int)(e % rpad);
+  const int t = (int)(e & 7), lane = (int)((e >> 3) & 63);
+  const size_t f = e >> 9;  // (kc, ct)
+  const int nct = rpad / 16;
+  const int ct = (int)(f % nct), kc = (int)(f / nct);
+  const int k = kc * 32 + 8 * (lane >> 4) + t, j = ct * 16 + (lane & 15);
   out[e] = j < r ? wr[(size_t)k * r + j] : 0.0f;
 }
 
 hipError_t launch_pad_proxy(hipStream_t st, int d, int r, const float* wr, float* out) {
+  if (d % 32) return hipErrorInvalidValue;
   const int rpad = proxy_rpad(r);
   const size_t total = (size_t)d * rpad;
-  hipLaunchKernelGGL(pad_proxy_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, d, r, rpad, wr,
+  hipLaunchKernelGGL(pack_proxy_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, d, r, rpad, wr,
                      out);
   return hipGetLastError();
 }

@@ -142,8 +142,8 @@ __device__ __forceinline__ void store4<float>(float* p, float4 v) { *reinterpret
 template <>
 __device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
   uint2 u;
-  u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-  u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  u.x = pack2bf(v.x, v.y);
+  u.y = pack2bf(v.z, v.w);
   *reinterpret_cast<uint2*>(p) = u;
 }
 
@@ -248,20 +248,20 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq,
       store4<T>(q + (size_t)m * nq + c0, r0);
       store4<T>(q + (size_t)m * nq + c1, r1);
     } else {
-      T* kr = Kc + (((size_t)b * Hkv + (head - Hq)) * L + i) * dh;
-      store4<T>(kr + j, r0);
-      store4<T>(kr + j + half, r1);
+      // four consecutive dimensions are adjacent in the fragment layout
+      T* kb = Kc + ((size_t)b * Hkv + (head - Hq)) * (size_t)l32_of(L) * dh;
+      store4<T>(kb + kc_off(i, j, dh), r0);
+      store4<T>(kb + kc_off(i, j + half, dh), r1);
     }
   }
-  // V layout [b][g][L/4][dh][4]: four consecutive keys of one dimension adjacent
   for (int c4 = threadIdx.x * 4; c4 < nv; c4 += 256 * 4) {
     const float4 v = sum_splits4(p0 + nq + nv + c4, sstride, S);
     const int g = c4 / dh, t = c4 - g * dh;
-    T* vb = Vc + ((size_t)b * Hkv + g) * L * dh + ((size_t)(i >> 2) * dh + t) * 4 + (i & 3);
-    io<T>::st(vb, v.x);
-    io<T>::st(vb + 4, v.y);
-    io<T>::st(vb + 8, v.z);
-    io<T>::st(vb + 12, v.w);
+    T* vb = Vc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * dh;
+    io<T>::st(vb + vc_off(i, t, dh), v.x);
+    io<T>::st(vb + vc_off(i, t + 1, dh), v.y);
+    io<T>::st(vb + vc_off(i, t + 2, dh), v.z);
+    io<T>::st(vb + vc_off(i, t + 3, dh), v.w);
   }
 }
 

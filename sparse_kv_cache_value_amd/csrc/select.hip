@@ -90,8 +90,22 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
       if (tid < 256) hist[tid] = 0;
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < SEL_EMAX; ++e)
-        if (cls[e] == 0 && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255], 1);
+      for (int e = 0; e < SEL_EMAX; ++e) {
+        // the leading digits of nearby scores mostly agree: when every
+        // participating lane of the wave has the same digit, one lane adds the
+        // count (LDS atomics to one address serialise)
+        const bool part = cls[e] == 0 && (key[e] & pmask) == prefix;
+        const int dg = (int)((key[e] >> shift) & 255);
+        const unsigned long long bal = __ballot(part);
+        if (bal == 0ull) continue;
+        const int lead = __ffsll((long long)bal) - 1;
+        const int d0 = __shfl(dg, lead, 64);
+        if (__all(!part || dg == d0)) {
+          if ((threadIdx.x & 63) == lead) atomicAdd(&hist[d0], __popcll(bal));
+        } else if (part) {
+          atomicAdd(&hist[dg], 1);
+        }
+      }
       __syncthreads();
       if (tid < 64) {
         int c[4], ls = 0;

@@ -31,6 +31,23 @@ def build(cfg, gain_std=0.1):
     return model, layers_np, head_np
 
 
+def unpack_k(k):
+    """[N][B][G][L32/32][dh/16][64][8] fragment order -> [N, B, L32, G, dh]."""
+    N_, B_, G_, T_, KS, _, _ = k.shape
+    k = k.reshape(N_, B_, G_, T_, KS, 2, 32, 8)            # lane = key%32 + 32*((dim/8)%2)
+    k = k.permute(0, 1, 3, 6, 2, 4, 5, 7)                  # N B T key G KS half j
+    return k.reshape(N_, B_, T_ * 32, G_, KS * 16).numpy()
+
+
+def unpack_v(v):
+    """[N][B][G][L32/16][dh/32][64][8] fragment order -> [N, B, L32, G, dh]."""
+    N_, B_, G_, KB, DT, _, _ = v.shape
+    v = v.reshape(N_, B_, G_, KB, DT, 2, 32, 2, 4)          # lane = dim%32 + 32*h, slot = jj + 4*jh
+    # key within the 16-block = 8*jh + 4*h + jj
+    v = v.permute(0, 1, 3, 7, 5, 8, 2, 4, 6)               # N B KB jh h jj G DT dl
+    return v.reshape(N_, B_, KB * 16, G_, DT * 32).numpy()
+
+
 class Snap:
     """Host copy of a State, in the oracle's per-sequence layout."""
 
@@ -38,10 +55,9 @@ class Snap:
         torch.cuda.synchronize()
         t = {k: v.detach().cpu() for k, v in st.tensors().items()}
         self.H = t["hidden"].float().numpy()                                 # [N+1, B, L, d]
-        self.K = t["k_cache"].float().permute(0, 1, 3, 2, 4).numpy()         # [N, B, L, Hkv, dh]
-        v = t["v_cache"].float()  # [N, B, Hkv, L/4, dh, 4]
-        N_, B_, G_, L4, dh, _ = v.shape
-        self.V = v.permute(0, 1, 3, 5, 2, 4).reshape(N_, B_, L4 * 4, G_, dh).numpy()
+        L = self.H.shape[2]
+        self.K = unpack_k(t["k_cache"].float())[:, :, :L]                      # [N, B, L, Hkv, dh]
+        self.V = unpack_v(t["v_cache"].float())[:, :, :L]
         self.Pc = t["proxy_cur"].numpy()
         self.Pr = t["proxy_ref"].numpy()
         self.score = t["score"].numpy()

@@ -50,6 +50,7 @@ def _dims(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=63), B.DLLM_E_SHAPE),
     (dict(head_dim=36), B.DLLM_E_SHAPE),
+    (dict(head_dim=48), B.DLLM_E_SHAPE),
     (dict(d_model=8224), B.DLLM_E_SHAPE),
     (dict(n_q_heads=6, n_kv_heads=4), B.DLLM_E_SHAPE),
     (dict(seq_len=9000), B.DLLM_E_SHAPE),
