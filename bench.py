@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 
 METRIC = "dLLM gen tokens/s (LLaDA-8B-shape, L=1024, 16% refresh) + % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
+CAL_ELEMS = 64 << 20  # fp32 elements of the calibration copy (256 MiB read + 256 MiB written)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_llada8b_sparse_step.json")
 BF16_PEAK_TFLOPS = 2516.6
 
 
@@ -38,6 +40,20 @@ def _ensure_built():
     if not os.path.exists(binding.LIB_PATH):
         from sparse_kv_cache_value_amd import build
         build.build()
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, if it was
+    taken with the current GEMM sources (else None)."""
+    try:
+        from sparse_kv_cache_value_amd import prof_summary
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("source_hash") != prof_summary.gemm_source_hash():
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def cpu_baseline(cfg, budget_s: float = 25.0):
@@ -107,6 +123,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--full-steps", type=int, default=3, help="steps timed with the gate as specified")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 256 MiB device copy before the timed steps (untimed), the reference kernel for "
+                         "the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path.",
@@ -129,6 +148,14 @@ def main():
     st = runtime.State(cfg)
     init_s = time.perf_counter() - t_init
     stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        src = torch.ones(CAL_ELEMS, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # prefill: step 0 is a full pass (and commits)
     runtime.step(model, st, mode=B.DLLM_MODE_FULL)
@@ -211,7 +238,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": gemm_traffic(),
             "launches": dom_launches,
             "avg_launch_us": round(1e3 * dom_ms / max(dom_launches, 1), 3),
             "algorithmic_bytes_per_launch": round(dom_bytes / max(dom_launches, 1), 1),
