@@ -119,3 +119,69 @@ def commit(rows, conf, argmax, entropy, committed, threshold):
     pick = sorted(pick, key=lambda j: rows[j])
     return ([rows[j] for j in pick], [argmax[j] for j in pick],
             max([entropy[j] for j in pick], default=0.0))
+
+
+# --------------------------------------------------------------------------
+# Polestar drift path (pure Python)
+# --------------------------------------------------------------------------
+
+def unit(v):
+    n = math.sqrt(math.fsum(a * a for a in v))
+    return [a / n for a in v] if n > 0 else [0.0] * len(v)
+
+
+def dot(a, b):
+    return math.fsum(x * y for x, y in zip(a, b))
+
+
+def kmeans(X, k, iters):
+    """Spherical k-means on unit rows (lists), seeds at rows stride*j."""
+    n = len(X)
+    stride = n // k
+    C = [list(X[stride * j]) for j in range(k)]
+
+    def assign():
+        out = []
+        for x in X:
+            best, bj = None, 0
+            for j in range(k):
+                v = dot(x, C[j])
+                if best is None or v > best:
+                    best, bj = v, j
+            out.append(bj)
+        return out
+
+    for _ in range(iters):
+        a = assign()
+        for j in range(k):
+            mem = [X[i] for i in range(n) if a[i] == j]
+            if not mem:
+                continue
+            v = [math.fsum(col) for col in zip(*mem)]
+            nv = math.sqrt(math.fsum(t * t for t in v))
+            if nv > 0:
+                C[j] = [t / nv for t in v]
+    return C, assign()
+
+
+def fp_encode_exhaustive(v, values):
+    """Code of the value nearest to v >= 0 among `values` (non-negative,
+    indexed by code, NaN entries skipped), ties to the even code."""
+    best, bc = None, 0
+    for c, val in enumerate(values):
+        if val != val:
+            continue
+        d = abs(v - val)
+        if best is None or d < best or (d == best and c % 2 == 0 and bc % 2 == 1):
+            best, bc = d, c
+    return bc
+
+
+def log_softmax(s):
+    m = max(s)
+    lse = math.log(math.fsum(math.exp(t - m) for t in s))
+    return [t - m - lse for t in s]
+
+
+def kl(logp, logq):
+    return math.fsum(math.exp(a) * (a - b) for a, b in zip(logp, logq))

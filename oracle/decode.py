@@ -26,6 +26,7 @@ import numpy as np
 
 from .model import (Spec, budget_k, commit, drift, lm_stats, proxy, select,
                     sparse_layer)
+from . import polestar
 
 
 @dataclasses.dataclass
@@ -35,6 +36,8 @@ class Policy:
     recent_k: int = 0
     tau: float = float("inf")
     conf_threshold: float = 0.9
+    score: str = "spa_cos"          # or "polestar_kl" (Polestar section 2A drift path)
+    polestar: polestar.PolestarParams = dataclasses.field(default_factory=polestar.PolestarParams)
 
 
 class SeqState:
@@ -54,6 +57,7 @@ class SeqState:
         self.P = np.zeros((N, L, spec.proxy_rank), np.float64)
         self.full_next = True
         self.n_new = 0
+        self.ps = [polestar.PolestarLayerState() for _ in range(N)]
 
     def advance_block(self):
         L, b = self.spec.seq_len, self.spec.block_len
@@ -99,14 +103,23 @@ def step(st: SeqState, layers, head, spec: Spec, pol: Policy, force_mode: Option
     full = st.full_next if force_mode is None else (force_mode == "full")
     st.H[0] = np.asarray(head["embed"], spec.wd)[st.tokens]
     forced = st.forced_set(pol)
-    sets, scores = [], []
+    sets, scores, ps_info = [], [], []
     for l in range(spec.n_layers):
+        if pol.score == "polestar_kl" and not full:
+            # Polestar: the drift path picks the rows; no value proxy involved
+            r = polestar.drift_and_select(st.H[l], st.K[l], st.block_start, layers[l], spec, pol.polestar,
+                                          st.ps[l])
+            sparse_layer(st.H[l], st.K[l], st.V[l], st.H[l + 1], r["I"], layers[l], spec)
+            sets.append(r["I"])
+            scores.append(r["kl"])
+            ps_info.append(r)
+            continue
         k = None if full else budget_k(pol.rho[l], spec.seq_len)
         I, s, _ = layer_refresh(st.H[l], st.K[l], st.V[l], st.H[l + 1], st.P[l],
                                 layers[l], spec, k, forced)
         sets.append(I)
         scores.append(s)
-    info = {"full": full, "sets": sets, "scores": scores, "forced": forced}
+    info = {"full": full, "sets": sets, "scores": scores, "forced": forced, "polestar": ps_info}
     info.update(commit_block(st, head, spec, pol))
     return info
 

@@ -23,7 +23,9 @@ def spec_of(cfg: configs.Config, **kw) -> oracle.Spec:
 
 def policy_of(cfg: configs.Config, **kw) -> oracle.decode.Policy:
     base = dict(rho=cfg.rho, forced=cfg.forced, recent_k=cfg.recent_k, tau=cfg.tau,
-                conf_threshold=cfg.conf_threshold)
+                conf_threshold=cfg.conf_threshold, score=cfg.score,
+                polestar=oracle.polestar.PolestarParams(cfg.n_clusters, cfg.kmeans_iters, cfg.top_clusters,
+                                                        cfg.window_blocks))
     base.update(kw)
     return oracle.decode.Policy(**base)
 

@@ -158,6 +158,71 @@ MUTATIONS = [m_rope_sign, m_drift_unnormalised, m_drift_abs_cos, m_select_high_i
              m_key_uses_query_weights]
 
 
+# ---- Polestar drift path ----
+import oracle.polestar as ops  # noqa: E402
+
+
+def m_fp_ties_up(monkeypatch):
+    def bad(v, grid):
+        if not v > 0.0:
+            return 0
+        if v >= grid[-1]:
+            return len(grid) - 1
+        hi = 1
+        while grid[hi] < v:
+            hi += 1
+        lo = hi - 1
+        return lo if v - grid[lo] < grid[hi] - v else hi
+    monkeypatch.setattr(ops, "_rne_on_grid", bad)
+
+
+def m_kmeans_mean_not_normalised(monkeypatch):
+    def bad(X, n_clusters, iters):
+        X = np.asarray(X, np.float64)
+        n = X.shape[0]
+        C = X[(n // n_clusters) * np.arange(n_clusters)].copy()
+        for _ in range(iters):
+            a = np.argmax(X @ C.T, axis=1)
+            for j in range(n_clusters):
+                if (a == j).any():
+                    C[j] = X[a == j].mean(axis=0)
+        D = X @ C.T
+        a = np.argmax(D, axis=1)
+        return C, a, [0.0], D
+    monkeypatch.setattr(ops, "spherical_kmeans", bad)
+
+
+def m_kl_reversed(monkeypatch):
+    def bad(logA, logA_prev):
+        logA = np.asarray(logA, np.float64); lp = np.asarray(logA_prev, np.float64)
+        return np.mean(np.sum(np.exp(lp) * (lp - logA), axis=2), axis=1)
+    monkeypatch.setattr(ops, "cluster_kl", bad)
+
+
+def m_window_unclamped(monkeypatch):
+    monkeypatch.setattr(ops, "window_start", lambda bs, L, blk, wb=3: int(max(bs - blk, 0)))
+
+
+def m_proxy_attention_unscaled(monkeypatch):
+    orig = ops.proxy_log_attention
+
+    def bad(q, Kw):
+        return orig(np.asarray(q, np.float64) * math.sqrt(np.asarray(q).shape[-1]), Kw)
+    monkeypatch.setattr(ops, "proxy_log_attention", bad)
+
+
+def m_top_clusters_high_ties(monkeypatch):
+    def bad(kl, top):
+        kl = np.asarray(kl, np.float64)
+        order = sorted(range(kl.size), key=lambda j: (-kl[j], -j))
+        return np.array(sorted(order[:top]), np.int64)
+    monkeypatch.setattr(ops, "top_clusters", bad)
+
+
+MUTATIONS += [m_fp_ties_up, m_kmeans_mean_not_normalised, m_kl_reversed, m_window_unclamped,
+              m_proxy_attention_unscaled, m_top_clusters_high_ties]
+
+
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
 def test_mutation_is_caught(monkeypatch, mutation):
     mutation(monkeypatch)
