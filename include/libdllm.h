@@ -117,13 +117,46 @@ typedef struct {
   int32_t batch;
 } dllm_state;
 
+/* Drift score used by dllm_step's sparse refresh. */
+enum { DLLM_SCORE_SPA_COS = 0,       /* SPA-Cache value-proxy cosine + top-k (SPA-Cache, method steps 1-2) */
+       DLLM_SCORE_POLESTAR_KL = 1 }; /* Polestar-Cache cluster KL (Polestar, section 2A) */
+
+/* Polestar-Cache drift path parameters.  Window W = window_blocks * block_len
+ * rows (<= 120 and <= seq_len); n_clusters <= 16 and <= W; d_model % 128 == 0. */
+typedef struct {
+  int32_t n_clusters;    /* spherical k-means clusters (16) */
+  int32_t kmeans_iters;  /* assign/update iterations before the final assignment (10) */
+  int32_t top_clusters;  /* clusters refreshed per layer and step (4), <= n_clusters */
+  int32_t window_blocks; /* prefix, current and suffix block: 3 */
+} dllm_polestar_params;
+
+/* Caller-owned Polestar state (K = n_clusters, Hq = n_q_heads, W as above).
+ * log_attn/win_start persist across steps; the rest describes the last layer
+ * processed (for inspection; codes/scales are the compressed proxy that the
+ * Polestar page keeps in host memory, not consumed by the step). */
+typedef struct {
+  double *log_attn;      /* [N][B][K][Hq][W] proxy log-attention of the previous step, per layer */
+  int32_t *win_start;    /* [N][B] window that log_attn belongs to; -1 = none (initialise to -1) */
+  double *centroids;     /* [B][K][d_model] unit centroids (fp64) */
+  double *norms;         /* [B][W] Euclidean norm of each window row's layer input */
+  int32_t *assign;       /* [B][W] cluster of each window row */
+  uint8_t *codes;        /* [B][W][d_model/2] E2M1 residual codes, element 2i in the low nibble */
+  uint8_t *scales;       /* [B][W][d_model/16] E4M3 (FN) scale per 16 elements */
+  void *queries;         /* [B][K][n_q_heads*head_dim] centroid queries (storage dtype) */
+  double *kl;            /* [B][K] cluster drift (mean over heads of KL(A_t || A_t-1)) */
+  int32_t *top;          /* [B][top_clusters] refreshed clusters, ascending */
+} dllm_polestar_state;
+
 typedef struct {
   int32_t mode;          /* DLLM_MODE_*; AUTO reads state.full_next (one host wait) */
   int32_t forced_rule;   /* DLLM_FORCED_* */
   int32_t recent_k;      /* EntropyCache k: recent decoded tokens always refreshed */
   double tau;            /* entropy gate threshold in nats (+inf: never full) */
   double conf_threshold; /* commit threshold on the top-1 probability */
-  const double *rho_h;   /* [n_layers] host: per-layer update ratio rho(l) */
+  const double *rho_h;   /* [n_layers] host: per-layer update ratio rho(l) (SPA score) */
+  int32_t score;         /* DLLM_SCORE_* */
+  const dllm_polestar_params *polestar;   /* host; DLLM_SCORE_POLESTAR_KL only */
+  dllm_polestar_state *polestar_state;    /* DLLM_SCORE_POLESTAR_KL only */
 } dllm_step_params;
 
 typedef struct {
@@ -207,6 +240,30 @@ dllm_status dllm_lm_head(dllm_model *m, const dllm_state *s, double *stats_out,
 dllm_status dllm_commit(dllm_model *m, dllm_state *s, double conf_threshold, double tau,
                         void *stream);
 
+/* Polestar-Cache drift path at `layer` (Polestar, section 2A), per sequence:
+ * window rows [ws, ws + W), ws = clamp(block_start - block_len, 0, L - W);
+ * spherical k-means (fp64) of the rows' layer inputs hidden[layer] scaled to
+ * unit length, seeds at window rows (W / K) * j, kmeans_iters iterations of
+ * (assign to the largest dot product, lowest cluster on ties; each cluster
+ * with members and a non-zero member sum becomes the normalised member sum)
+ * and a final assignment; NVFP4 codes of the residuals (E4M3 scale of amax/6
+ * per 16 elements, E2M1 codes of r/scale, both round-to-nearest-even,
+ * saturating); centroid queries bf16(RMSNorm(c) * attn_norm) W_q with RoPE at
+ * the seed row's position; per query head the fp64 log-softmax over the window
+ * keys of k_cache[layer] (scale 1/sqrt(head_dim)), and the per-head KL against
+ * log_attn, which it then replaces. */
+dllm_status dllm_polestar_drift(dllm_model *m, int32_t layer, const dllm_state *s, dllm_polestar_state *ps,
+                                const dllm_polestar_params *p, void *stream);
+
+/* Polestar selection at `layer`: cluster drift = mean over heads of the KL
+ * from dllm_polestar_drift, or 0 when win_start[layer][b] != ws (the window's
+ * first step); the top_clusters of largest drift (lowest index on ties); index
+ * set I = current block rows + the window rows assigned to those clusters,
+ * ascending, into idx[b][0..n_sel[b]) ([B][L]); records win_start.  Follow
+ * with dllm_sparse_layer(max_rows = batch * W). */
+dllm_status dllm_polestar_select(dllm_model *m, int32_t layer, const dllm_state *s, dllm_polestar_state *ps,
+                                 const dllm_polestar_params *p, int32_t *idx, int32_t *n_sel, void *stream);
+
 /* Forced rows for the next step, forced[b][i] in {0,1} ([B][L]):
  * DLLM_FORCED_BLOCK marks the current block, DLLM_FORCED_BLOCK_RECENT also the
  * last recent_k entries of history, DLLM_FORCED_NONE marks nothing. */
@@ -215,7 +272,9 @@ dllm_status dllm_forced_set(dllm_model *m, const dllm_state *s, int32_t rule, in
 
 /* One denoising step for every sequence: embed the rows whose token changed
  * (every row in a full pass), then per layer drift score, selection (every
- * row in a full pass) and sparse layer, then commit.  Mode FULL or SPARSE
+ * row in a full pass) and sparse layer, then commit.  With
+ * score = DLLM_SCORE_POLESTAR_KL a sparse step uses dllm_polestar_drift and
+ * dllm_polestar_select instead of the value-proxy drift and top-k.  Mode FULL or SPARSE
  * applies to every sequence; AUTO runs a full pass for the sequences whose
  * full_next is set (the caller sets it before the first step, whose caches are
  * empty).  If res_h is non-NULL the call waits for the stream and fills it. */

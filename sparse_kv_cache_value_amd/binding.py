@@ -20,6 +20,7 @@ DLLM_OK, DLLM_E_ARG, DLLM_E_SHAPE, DLLM_E_STATE, DLLM_E_NOMEM, DLLM_E_HIP, DLLM_
 DLLM_FP32, DLLM_BF16 = 0, 1
 DLLM_MODE_AUTO, DLLM_MODE_FULL, DLLM_MODE_SPARSE = 0, 1, 2
 DLLM_FORCED_NONE, DLLM_FORCED_BLOCK, DLLM_FORCED_BLOCK_RECENT = 0, 1, 2
+DLLM_SCORE_SPA_COS, DLLM_SCORE_POLESTAR_KL = 0, 1
 
 _i32, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -41,9 +42,20 @@ class DllmState(ctypes.Structure):
         "history", "n_history", "n_new", "block_start", "full_next", "max_entropy")] + [("batch", _i32)]
 
 
+class DllmPolestarParams(ctypes.Structure):
+    _fields_ = [("n_clusters", _i32), ("kmeans_iters", _i32), ("top_clusters", _i32), ("window_blocks", _i32)]
+
+
+class DllmPolestarState(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in (
+        "log_attn", "win_start", "centroids", "norms", "assign", "codes", "scales", "queries", "kl", "top")]
+
+
 class DllmStepParams(ctypes.Structure):
     _fields_ = [("mode", _i32), ("forced_rule", _i32), ("recent_k", _i32), ("tau", _f64),
-                ("conf_threshold", _f64), ("rho_h", ctypes.POINTER(_f64))]
+                ("conf_threshold", _f64), ("rho_h", ctypes.POINTER(_f64)), ("score", _i32),
+                ("polestar", ctypes.POINTER(DllmPolestarParams)),
+                ("polestar_state", ctypes.POINTER(DllmPolestarState))]
 
 
 class DllmStepResult(ctypes.Structure):
@@ -72,6 +84,10 @@ SIGNATURES = {
     "dllm_lm_head": (_i32, [_vp, ctypes.POINTER(DllmState), _vp, _vp, _vp]),
     "dllm_commit": (_i32, [_vp, ctypes.POINTER(DllmState), _f64, _f64, _vp]),
     "dllm_forced_set": (_i32, [_vp, ctypes.POINTER(DllmState), _i32, _i32, _vp, _vp]),
+    "dllm_polestar_drift": (_i32, [_vp, _i32, ctypes.POINTER(DllmState), ctypes.POINTER(DllmPolestarState),
+                                   ctypes.POINTER(DllmPolestarParams), _vp]),
+    "dllm_polestar_select": (_i32, [_vp, _i32, ctypes.POINTER(DllmState), ctypes.POINTER(DllmPolestarState),
+                                    ctypes.POINTER(DllmPolestarParams), _vp, _vp, _vp]),
     "dllm_step": (_i32, [_vp, ctypes.POINTER(DllmState), ctypes.POINTER(DllmStepParams),
                          ctypes.POINTER(DllmStepResult), _vp]),
     "dllm_profile": (_i32, [_vp, _i32]),
@@ -179,11 +195,24 @@ def dllm_forced_set(m: int, state, rule: int, recent_k: int, forced, stream=None
     _check(lib().dllm_forced_set(m, ctypes.byref(state.c), rule, recent_k, _p(forced), _stream(stream)))
 
 
+def dllm_polestar_drift(m: int, layer: int, state, ps, params: DllmPolestarParams, stream=None):
+    _check(lib().dllm_polestar_drift(m, layer, ctypes.byref(state.c), ctypes.byref(ps.c), ctypes.byref(params),
+                                     _stream(stream)))
+
+
+def dllm_polestar_select(m: int, layer: int, state, ps, params: DllmPolestarParams, idx, n_sel, stream=None):
+    _check(lib().dllm_polestar_select(m, layer, ctypes.byref(state.c), ctypes.byref(ps.c), ctypes.byref(params),
+                                      _p(idx), _p(n_sel), _stream(stream)))
+
+
 def dllm_step(m: int, state, mode: int, forced_rule: int, recent_k: int, tau: float, conf_threshold: float,
-              rho, want_result: bool = True, stream=None) -> Optional[DllmStepResult]:
+              rho, want_result: bool = True, stream=None, score: int = DLLM_SCORE_SPA_COS,
+              polestar: Optional[DllmPolestarParams] = None, polestar_state=None) -> Optional[DllmStepResult]:
     rho_arr = (_f64 * len(rho))(*[float(r) for r in rho])
     p = DllmStepParams(mode, forced_rule, recent_k, float(tau), float(conf_threshold),
-                       ctypes.cast(rho_arr, ctypes.POINTER(_f64)))
+                       ctypes.cast(rho_arr, ctypes.POINTER(_f64)), score,
+                       ctypes.pointer(polestar) if polestar is not None else None,
+                       ctypes.pointer(polestar_state.c) if polestar_state is not None else None)
     res = DllmStepResult() if want_result else None
     _check(lib().dllm_step(m, ctypes.byref(state.c), ctypes.byref(p),
                            ctypes.byref(res) if res is not None else None, _stream(stream)))

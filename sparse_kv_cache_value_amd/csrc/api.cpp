@@ -96,6 +96,14 @@ struct dllm_model {
   double* lm_stats = nullptr;
   int32_t* lm_rows = nullptr;
   int lm_slabs = 0;
+  // Polestar drift path workspace
+  double* ps_part = nullptr;   // Gram partials [max_batch][d/128][W][W]
+  double* ps_R = nullptr;      // Gram [max_batch][W][W]
+  double* ps_coef = nullptr;   // centroid coefficients [max_batch][16][W]
+  double* ps_klp = nullptr;    // per-head KL [max_batch][Hq][16]
+  int32_t* ps_nsel = nullptr;  // centroid rows per sequence
+  void* ps_A = nullptr;        // packed centroid rows for the query GEMM
+  int ps_MTt = 0;
   void* res_dev = nullptr;
   void* res_host = nullptr;   // pinned, 32 bytes
   uint8_t* full_host = nullptr;  // pinned, max_batch
@@ -347,6 +355,78 @@ dllm_status do_commit(dllm_model* m, dllm_state* s, double thr, double tau, hipS
   return DLLM_OK;
 }
 
+dllm_status finish_step(dllm_model* m, dllm_state* s, dllm_step_result* res_h, hipStream_t st) {
+  if (!res_h) return DLLM_OK;
+  const int B = s->batch, L = m->d.seq_len;
+  HIPCHK(launch_step_result(st, B, m->step_full, s->n_new, s->block_start, s->max_entropy, L, m->res_dev));
+  HIPCHK(hipMemcpyAsync(m->res_host, m->res_dev, 32, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
+  const int32_t* r = (const int32_t*)m->res_host;
+  res_h->n_full = r[0];
+  res_h->n_committed = r[1];
+  res_h->n_active = r[2];
+  std::memcpy(&res_h->max_entropy, r + 4, 8);
+  return DLLM_OK;
+}
+
+dllm_status check_polestar(const dllm_model* m, const dllm_state* s, const dllm_polestar_state* ps,
+                           const dllm_polestar_params* p) {
+  const dllm_dims& d = m->d;
+  if (!ps || !p) return fail(DLLM_E_ARG, "polestar state/params is NULL");
+  if (!ps->log_attn || !ps->win_start || !ps->centroids || !ps->norms || !ps->assign || !ps->codes || !ps->scales ||
+      !ps->queries || !ps->kl || !ps->top)
+    return fail(DLLM_E_ARG, "polestar state has a NULL buffer");
+  if (!m->ps_part) return fail(DLLM_E_UNSUPPORTED, "the Polestar path needs d_model %% 128 == 0");
+  const int W = p->window_blocks * d.block_len;
+  if (p->n_clusters < 1 || p->n_clusters > 16) return fail(DLLM_E_ARG, "n_clusters must be in [1, 16]");
+  if (p->kmeans_iters < 0) return fail(DLLM_E_ARG, "kmeans_iters < 0");
+  if (p->top_clusters < 1 || p->top_clusters > p->n_clusters) return fail(DLLM_E_ARG, "top_clusters out of range");
+  if (p->window_blocks < 1 || W > 120 || W > d.seq_len || W < p->n_clusters)
+    return fail(DLLM_E_SHAPE, "window of %d rows: need n_clusters <= W <= min(120, seq_len)", W);
+  const size_t lds = ((size_t)p->n_clusters * d.head_dim + (size_t)W * (d.head_dim + 1) + (size_t)p->n_clusters * W) * 8;
+  if (lds > 160 * 1024) return fail(DLLM_E_SHAPE, "proxy attention tile does not fit LDS");
+  (void)s;
+  return DLLM_OK;
+}
+
+dllm_status do_polestar_drift(dllm_model* m, int layer, const dllm_state* s, dllm_polestar_state* ps,
+                              const dllm_polestar_params* p, hipStream_t st) {
+  const dllm_dims& d = m->d;
+  const int B = s->batch, L = d.seq_len, D = d.d_model, blk = d.block_len;
+  const int W = p->window_blocks * blk, K = p->n_clusters, Hq = d.n_q_heads, dh = d.head_dim;
+  const LayerW& w = m->layers[layer];
+  void* H = hid(m, const_cast<dllm_state*>(s), layer);
+  HIPCHK(launch_ps_gram(st, m->bf16, B, L, D, blk, W, s->block_start, H, m->ps_part, m->ps_R));
+  HIPCHK(launch_ps_kmeans(st, B, W, K, p->kmeans_iters, m->ps_R, ps->assign, ps->norms, m->ps_coef, m->ps_nsel));
+  HIPCHK(launch_ps_centroids(st, m->bf16, B, L, D, blk, W, K, d.rms_eps, m->ps_MTt, s->block_start, H, m->ps_coef,
+                             ps->norms, w.attn_norm, ps->centroids, m->ps_A));
+  HIPCHK(launch_ps_codes(st, m->bf16, B, L, D, blk, W, K, s->block_start, H, ps->norms, ps->assign, ps->centroids,
+                         ps->codes, ps->scales));
+  // centroid queries through the layer's query projection (the first
+  // n_q_heads*head_dim columns of the packed QKV weight; fp32 models use the
+  // whole row-major QKV weight and read the query columns)
+  const int N = m->bf16 ? nq_of(d) : nq_of(d) + 2 * nv_of(d);
+  int sp = 1;
+  CHK(gemm(m, st, B * K, B, D, N, m->ps_A, w.w_qkv, m->ps_nsel, m->part, m->part_floats, &sp, DLLM_PROF_GEMM,
+           m->ps_MTt));
+  HIPCHK(launch_ps_queries(st, m->bf16, B, L, blk, W, K, Hq, dh, sp, N, s->block_start, m->part, m->rope_cos,
+                           m->rope_sin, ps->queries));
+  double* la = ps->log_attn + (size_t)layer * B * K * Hq * W;
+  HIPCHK(launch_ps_attn_kl(st, m->bf16, B, L, blk, W, K, Hq, d.n_kv_heads, dh, s->block_start, ps->queries,
+                           kcache(m, const_cast<dllm_state*>(s), layer), la, m->ps_klp));
+  return DLLM_OK;
+}
+
+dllm_status do_polestar_select(dllm_model* m, int layer, const dllm_state* s, dllm_polestar_state* ps,
+                               const dllm_polestar_params* p, int32_t* idx, int32_t* n, hipStream_t st) {
+  const dllm_dims& d = m->d;
+  const int B = s->batch, W = p->window_blocks * d.block_len;
+  HIPCHK(launch_ps_select(st, B, d.seq_len, d.block_len, W, p->n_clusters, d.n_q_heads, p->top_clusters,
+                          s->block_start, ps->assign, m->ps_klp, ps->win_start + (size_t)layer * B, ps->kl, ps->top,
+                          idx, n));
+  return DLLM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -436,6 +516,16 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   ALLOC(m->lm_part, (size_t)lm_rows_cap * m->lm_slabs * 4 * 8);
   ALLOC(m->lm_stats, (size_t)lm_rows_cap * 4 * 8);
   ALLOC(m->lm_rows, 16);
+  if (D % 128 == 0) {
+    const size_t wmax = 120;
+    ALLOC(m->ps_part, (size_t)d.max_batch * (D / 128) * wmax * wmax * 8);
+    ALLOC(m->ps_R, (size_t)d.max_batch * wmax * wmax * 8);
+    ALLOC(m->ps_coef, (size_t)d.max_batch * 16 * wmax * 8);
+    ALLOC(m->ps_klp, (size_t)d.max_batch * d.n_q_heads * 16 * 8);
+    ALLOC(m->ps_nsel, (size_t)d.max_batch * 4);
+    m->ps_MTt = (d.max_batch * 16 + 31) / 32 + 1;
+    ALLOC(m->ps_A, (size_t)m->ps_MTt * 32 * D * es + gemm_pad_elems(m->ps_MTt) * es);
+  }
   ALLOC(m->res_dev, 64);
   if (hipHostMalloc(&m->res_host, 64, hipHostMallocDefault) != hipSuccess)
     return cleanup(fail(DLLM_E_NOMEM, "hipHostMalloc failed"));
@@ -607,6 +697,25 @@ dllm_status dllm_commit(dllm_model* m, dllm_state* s, double conf_threshold, dou
   return do_commit(m, s, conf_threshold, tau, S(stream));
 }
 
+dllm_status dllm_polestar_drift(dllm_model* m, int32_t layer, const dllm_state* s, dllm_polestar_state* ps,
+                                const dllm_polestar_params* p, void* stream) {
+  CHK(check_model(m));
+  CHK(check_layer(m, layer));
+  CHK(check_state(m, s, false));
+  CHK(check_polestar(m, s, ps, p));
+  return do_polestar_drift(m, layer, s, ps, p, S(stream));
+}
+
+dllm_status dllm_polestar_select(dllm_model* m, int32_t layer, const dllm_state* s, dllm_polestar_state* ps,
+                                 const dllm_polestar_params* p, int32_t* idx, int32_t* n_sel, void* stream) {
+  CHK(check_model(m));
+  CHK(check_layer(m, layer));
+  CHK(check_state(m, s, false));
+  CHK(check_polestar(m, s, ps, p));
+  if (!idx || !n_sel) return fail(DLLM_E_ARG, "idx/n_sel is NULL");
+  return do_polestar_select(m, layer, s, ps, p, idx, n_sel, S(stream));
+}
+
 dllm_status dllm_forced_set(dllm_model* m, const dllm_state* s, int32_t rule, int32_t recent_k, uint8_t* forced,
                             void* stream) {
   CHK(check_model(m));
@@ -629,6 +738,10 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     return fail(DLLM_E_ARG, "unknown forced rule %d", p->forced_rule);
   if (p->recent_k < 0) return fail(DLLM_E_ARG, "recent_k < 0");
   if (std::isnan(p->tau) || std::isnan(p->conf_threshold)) return fail(DLLM_E_ARG, "threshold is NaN");
+  if (p->score != DLLM_SCORE_SPA_COS && p->score != DLLM_SCORE_POLESTAR_KL)
+    return fail(DLLM_E_ARG, "unknown score %d", p->score);
+  const bool polestar = p->score == DLLM_SCORE_POLESTAR_KL;
+  if (polestar) CHK(check_polestar(m, s, p->polestar_state, p->polestar));
   const dllm_dims& d = m->d;
   for (int l = 0; l < d.n_layers; ++l) {
     CHK(check_layer(m, l));
@@ -652,6 +765,19 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
   const int32_t* prev_n = m->n0;
   HIPCHK(launch_embed(st, m->bf16, prev_max, B, L, d.d_model, d.vocab, prev_idx, prev_n, s->tokens, m->embed,
                       hid(m, s, 0)));
+  if (polestar && !any_full) {
+    // Polestar-Cache: the cluster drift path picks the rows of every layer
+    const int W = p->polestar->window_blocks * d.block_len;
+    for (int l = 0; l < d.n_layers; ++l) {
+      int32_t* idx = m->idx[l & 1];
+      int32_t* n = m->nsel[l & 1];
+      CHK(do_polestar_drift(m, l, s, p->polestar_state, p->polestar, st));
+      CHK(do_polestar_select(m, l, s, p->polestar_state, p->polestar, idx, n, st));
+      CHK(do_sparse(m, l, s, idx, n, B * W, st));
+    }
+    CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
+    return finish_step(m, s, res_h, st);
+  }
   for (int l = 0; l < d.n_layers; ++l) {
     CHK(do_drift(m, l, s, prev_idx, prev_n, prev_max, st));
     const double kf = std::floor(p->rho_h[l] * L + 0.5);
@@ -666,17 +792,7 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     prev_max = rows;
   }
   CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
-  if (res_h) {
-    HIPCHK(launch_step_result(st, B, m->step_full, s->n_new, s->block_start, s->max_entropy, L, m->res_dev));
-    HIPCHK(hipMemcpyAsync(m->res_host, m->res_dev, 32, hipMemcpyDeviceToHost, st));
-    HIPCHK(hipStreamSynchronize(st));
-    const int32_t* r = (const int32_t*)m->res_host;
-    res_h->n_full = r[0];
-    res_h->n_committed = r[1];
-    res_h->n_active = r[2];
-    std::memcpy(&res_h->max_entropy, r + 4, 8);
-  }
-  return DLLM_OK;
+  return finish_step(m, s, res_h, st);
 }
 
 dllm_status dllm_profile(dllm_model* m, int32_t enable) {

@@ -112,4 +112,25 @@ hipError_t launch_commit(hipStream_t st, int B, int L, int blk, double thr, doub
 hipError_t launch_step_result(hipStream_t st, int B, const uint8_t* step_full, const int32_t* n_new,
                               const int32_t* block_start, const double* max_entropy, int L, void* out);
 
+// ---- Polestar-Cache drift path (polestar.hip) ----
+int ps_gram_slices(int d);
+hipError_t launch_ps_gram(hipStream_t st, bool bf16, int B, int L, int d, int blk, int W, const int32_t* bstart,
+                          const void* H, double* part, double* R);
+hipError_t launch_ps_kmeans(hipStream_t st, int B, int W, int K, int iters, const double* R, int32_t* assign,
+                            double* norms, double* coef, int32_t* nsel);
+hipError_t launch_ps_centroids(hipStream_t st, bool bf16, int B, int L, int d, int blk, int W, int K, float eps,
+                               int MTt, const int32_t* bstart, const void* H, const double* coef,
+                               const double* norms, const float* g1, double* cent, void* A);
+hipError_t launch_ps_codes(hipStream_t st, bool bf16, int B, int L, int d, int blk, int W, int K,
+                           const int32_t* bstart, const void* H, const double* norms, const int32_t* assign,
+                           const double* cent, uint8_t* codes, uint8_t* scales);
+hipError_t launch_ps_queries(hipStream_t st, bool bf16, int B, int L, int blk, int W, int K, int Hq, int dh, int S,
+                             int ldp, const int32_t* bstart, const float* part, const float* rc, const float* rs,
+                             void* q);
+hipError_t launch_ps_attn_kl(hipStream_t st, bool bf16, int B, int L, int blk, int W, int K, int Hq, int Hkv,
+                             int dh, const int32_t* bstart, const void* q, const void* Kc, double* logA, double* klp);
+hipError_t launch_ps_select(hipStream_t st, int B, int L, int blk, int W, int K, int Hq, int top,
+                            const int32_t* bstart, const int32_t* assign, const double* klp, int32_t* wstart,
+                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n);
+
 }  // namespace dllm

@@ -14,7 +14,7 @@ import torch
 
 from . import binding as B
 from . import inputs
-from .configs import BF16, FP32, Config, FORCED_BLOCK, FORCED_BLOCK_RECENT, FORCED_NONE
+from .configs import BF16, FP32, Config, FORCED_BLOCK, FORCED_BLOCK_RECENT, FORCED_NONE, SCORE_POLESTAR
 
 FORCED_RULE = {FORCED_NONE: B.DLLM_FORCED_NONE, FORCED_BLOCK: B.DLLM_FORCED_BLOCK,
                FORCED_BLOCK_RECENT: B.DLLM_FORCED_BLOCK_RECENT}
@@ -112,8 +112,42 @@ class State:
             "history", "n_history", "n_new", "block_start", "full_next", "max_entropy")}
 
 
+def polestar_params(cfg: Config) -> B.DllmPolestarParams:
+    return B.DllmPolestarParams(cfg.n_clusters, cfg.kmeans_iters, cfg.top_clusters, cfg.window_blocks)
+
+
+class PolestarState:
+    """Caller-owned Polestar state (include/libdllm.h, dllm_polestar_state)."""
+
+    def __init__(self, cfg: Config, batch: Optional[int] = None, device="cuda"):
+        dev = torch.device(device)
+        Bn = batch or cfg.batch
+        N, d, K, Hq = cfg.n_layers, cfg.d_model, cfg.n_clusters, cfg.n_q_heads
+        W = cfg.window_blocks * cfg.block_len
+        self.W = W
+        self.log_attn = torch.zeros((N, Bn, K, Hq, W), dtype=torch.float64, device=dev)
+        self.win_start = torch.full((N, Bn), -1, dtype=torch.int32, device=dev)
+        self.centroids = torch.zeros((Bn, K, d), dtype=torch.float64, device=dev)
+        self.norms = torch.zeros((Bn, W), dtype=torch.float64, device=dev)
+        self.assign = torch.zeros((Bn, W), dtype=torch.int32, device=dev)
+        self.codes = torch.zeros((Bn, W, d // 2), dtype=torch.uint8, device=dev)
+        self.scales = torch.zeros((Bn, W, d // 16), dtype=torch.uint8, device=dev)
+        self.queries = torch.zeros((Bn, K, cfg.n_q), dtype=inputs.storage_dtype(cfg), device=dev)
+        self.kl = torch.zeros((Bn, K), dtype=torch.float64, device=dev)
+        self.top = torch.zeros((Bn, cfg.top_clusters), dtype=torch.int32, device=dev)
+        self.c = B.DllmPolestarState(*[t.data_ptr() for t in (
+            self.log_attn, self.win_start, self.centroids, self.norms, self.assign, self.codes, self.scales,
+            self.queries, self.kl, self.top)])
+
+
 def step(model: Model, state: State, mode: int = B.DLLM_MODE_AUTO, want_result: bool = True, stream=None,
-         tau: Optional[float] = None):
+         tau: Optional[float] = None, polestar_state: Optional[PolestarState] = None):
     cfg = model.cfg
+    if cfg.score == SCORE_POLESTAR:
+        if polestar_state is None:
+            raise ValueError("the Polestar score needs a PolestarState")
+        return B.dllm_step(model.h, state, mode, FORCED_RULE[cfg.forced], cfg.recent_k,
+                           cfg.tau if tau is None else tau, cfg.conf_threshold, cfg.rho, want_result, stream,
+                           B.DLLM_SCORE_POLESTAR_KL, polestar_params(cfg), polestar_state)
     return B.dllm_step(model.h, state, mode, FORCED_RULE[cfg.forced], cfg.recent_k,
                        cfg.tau if tau is None else tau, cfg.conf_threshold, cfg.rho, want_result, stream)

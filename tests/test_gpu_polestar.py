@@ -1,0 +1,201 @@
+"""Polestar-Cache drift path on the GPU against the oracle (shadow mode: the
+oracle's functions run on the GPU's own window inputs, keys, centroids and
+queries at each decision point): window row norms, spherical k-means
+assignment and centroids, NVFP4 codes (bit-exact), centroid queries, proxy
+log-attention, cluster KL, top clusters, the index set and the sparse layer;
+a medium bf16 model (also GQA) over several steps, dllm_step against the
+entry points, and the full C5 shape (B=4, L=4096, 32 layers) on sampled
+layers and sequences."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import polestar as ps
+from gpu_common import assert_close, build, medium_cfg, say, unpack_k, unpack_v
+from helpers import np_weights, spec_of
+from sparse_kv_cache_value_amd import binding as B
+from sparse_kv_cache_value_amd import configs, inputs, runtime
+
+pytestmark = pytest.mark.gpu
+
+MED = medium_cfg(name="medium-polestar", score=configs.SCORE_POLESTAR, forced=configs.FORCED_BLOCK, recent_k=0,
+                 seed=31, n_steps=3)
+MED_GQA = medium_cfg(name="medium-polestar-gqa", score=configs.SCORE_POLESTAR, forced=configs.FORCED_BLOCK,
+                     recent_k=0, seed=32, n_q_heads=8, n_kv_heads=2, batch=2, seq_len=128, prompt_len=64,
+                     n_steps=2)
+
+
+def _layer_slice(st, l, b):
+    torch.cuda.synchronize()
+    L = st.cfg.seq_len
+    return {
+        "x": st.hidden[l, b].float().cpu().numpy(),
+        "h": st.hidden[l + 1, b].float().cpu().numpy(),
+        "K": unpack_k(st.k_cache[l:l + 1, b:b + 1].float().cpu())[0, 0, :L],
+        "V": unpack_v(st.v_cache[l:l + 1, b:b + 1].float().cpu())[0, 0, :L],
+    }
+
+
+def _ps_slice(pst, l, b):
+    torch.cuda.synchronize()
+    return {k: getattr(pst, k)[b].cpu().numpy() for k in
+            ("centroids", "norms", "assign", "codes", "scales", "kl", "top")} | {
+        "queries": pst.queries[b].float().cpu().numpy(),
+        "log_attn": pst.log_attn[l, b].cpu().numpy(),
+        "win_start": int(pst.win_start[l, b]),
+    }
+
+
+def check_layer(cfg, spec, W, l, b, pre, pre_ps, mid_ps, post_ps, post, I_gpu, what):
+    """All shadow-mode checks of one layer and sequence."""
+    L, blk = cfg.seq_len, cfg.block_len
+    pp = ps.PolestarParams(cfg.n_clusters, cfg.kmeans_iters, cfg.top_clusters, cfg.window_blocks)
+    Wn = pp.window_blocks * blk
+    bs = pre["bs"]
+    ws = ps.window_start(bs, L, blk, pp.window_blocks)
+    X = pre["x"][ws:ws + Wn].astype(np.float64)
+    # row norms
+    n_or = np.sqrt(np.sum(X * X, axis=1))
+    assert np.max(np.abs(mid_ps["norms"] - n_or) / np.maximum(n_or, 1e-300)) < 1e-12, f"{what}: norms"
+    # k-means on the unit rows
+    C_or, a_or, _, D = ps.spherical_kmeans(ps.unit_rows(X), pp.n_clusters, pp.iters)
+    a_gpu = mid_ps["assign"]
+    srt = np.sort(D, axis=1)
+    margin = srt[:, -1] - srt[:, -2]
+    if not np.array_equal(a_gpu, a_or):
+        bad = np.nonzero(a_gpu != a_or)[0]
+        assert np.all(margin[bad] < 1e-9), f"{what}: assignment differs at rows {bad[:8]} (margins {margin[bad][:4]})"
+        say(f"{what}: k-means tie at rows {bad}, skipped")
+        return
+    assert_close(mid_ps["centroids"], C_or, 1e-12, f"{what}: centroids")
+    # NVFP4 codes from the GPU's norms and centroids: bit-exact
+    R = X / mid_ps["norms"][:, None] - mid_ps["centroids"][a_gpu]
+    codes, scales = ps.nvfp4_encode(R)
+    assert np.array_equal(scales, mid_ps["scales"]), f"{what}: NVFP4 scales"
+    assert np.array_equal(codes, mid_ps["codes"]), f"{what}: NVFP4 codes"
+    # centroid queries (bf16 path) from the GPU's centroids
+    pos = ws + (Wn // pp.n_clusters) * np.arange(pp.n_clusters)
+    q_or = ps.centroid_queries(mid_ps["centroids"], pos, W, spec).reshape(pp.n_clusters, -1)
+    assert_close(mid_ps["queries"], q_or, 2e-2, f"{what}: centroid queries")
+    # proxy attention and KL from the GPU's queries and keys
+    qg = mid_ps["queries"].reshape(pp.n_clusters, cfg.n_q_heads, cfg.head_dim)
+    lA = ps.proxy_log_attention(qg, pre["K"][ws:ws + Wn])
+    assert np.max(np.abs(mid_ps["log_attn"] - lA)) < 1e-10, f"{what}: proxy log-attention"
+    if pre_ps["win_start"] == ws:
+        kl = ps.cluster_kl(lA, pre_ps["log_attn"])
+    else:
+        kl = np.zeros(pp.n_clusters)
+    assert np.all(np.abs(post_ps["kl"] - kl) <= 1e-9 * np.abs(kl) + 1e-13), f"{what}: KL {post_ps['kl']} vs {kl}"
+    assert post_ps["win_start"] == ws
+    top = ps.top_clusters(kl, pp.top)
+    srt_kl = np.sort(kl)[::-1]
+    cut = srt_kl[pp.top - 1]
+    band = {j for j in range(pp.n_clusters) if abs(kl[j] - cut) <= 1e-6 * abs(cut)} if cut > 0 else set()
+    if set(post_ps["top"].tolist()) - band != set(top.tolist()) - band:
+        raise AssertionError(f"{what}: top clusters {post_ps['top']} vs {top}")
+    I_or = ps.select_rows(np.arange(bs, min(bs + blk, L)), ws, a_gpu, post_ps["top"])
+    assert list(I_gpu) == I_or.tolist(), f"{what}: index set"
+    # the sparse layer on I (shadow)
+    Kx, Vx, Hx = pre["K"].copy(), pre["V"].copy(), pre["h"].copy()
+    oracle.sparse_layer(pre["x"], Kx, Vx, Hx, I_gpu, W, spec)
+    mask = np.zeros(L, bool)
+    mask[I_gpu] = True
+    e = assert_close(post["h"][mask], Hx[mask], 2e-2, f"{what}: sparse layer H")
+    assert np.array_equal(post["h"][~mask], pre["h"][~mask])
+    assert_close(post["K"][mask], Kx[mask], 2e-2, f"{what}: K rows")
+    say(f"{what}: ws={ws} |I|={len(I_gpu)} top={list(post_ps['top'])} kl max {kl.max():.3e} H err {e:.2e}")
+
+
+def _run(cfg, layers_np, model, st, pst, steps, check_layers, check_seqs, spec):
+    dev = "cuda"
+    Bn, L, N = st.batch, cfg.seq_len, cfg.n_layers
+    params = runtime.polestar_params(cfg)
+    idx = torch.zeros((Bn, L), dtype=torch.int32, device=dev)
+    n = torch.zeros(Bn, dtype=torch.int32, device=dev)
+    for t in range(1, steps + 1):
+        nh = st.n_history.cpu().numpy()
+        nn = st.n_new.cpu().numpy()
+        hist = st.history.cpu().numpy()
+        rows0 = torch.zeros((Bn, L), dtype=torch.int32)
+        n0 = torch.zeros(Bn, dtype=torch.int32)
+        for b in range(Bn):
+            rows0[b, :nn[b]] = torch.from_numpy(hist[b][nh[b] - nn[b]:nh[b]].copy())
+            n0[b] = int(nn[b])
+        B.dllm_embed(model.h, st, rows0.to(dev), n0.to(dev))
+        bs = st.block_start.cpu().numpy()
+        for l in range(N):
+            chk = l in check_layers
+            if chk:
+                pre = {b: _layer_slice(st, l, b) | {"bs": int(bs[b])} for b in check_seqs}
+                pre_ps = {b: _ps_slice(pst, l, b) for b in check_seqs}
+            B.dllm_polestar_drift(model.h, l, st, pst, params)
+            if chk:
+                mid_ps = {b: _ps_slice(pst, l, b) for b in check_seqs}
+            B.dllm_polestar_select(model.h, l, st, pst, params, idx, n)
+            if chk:
+                post_ps = {b: _ps_slice(pst, l, b) for b in check_seqs}
+                I_all, n_all = idx.cpu().numpy(), n.cpu().numpy()
+            B.dllm_sparse_layer(model.h, l, st, idx, n, Bn * pst.W)
+            if chk:
+                for b in check_seqs:
+                    post = _layer_slice(st, l, b)
+                    check_layer(cfg, spec, layers_np[l], l, b, pre[b], pre_ps[b], mid_ps[b], post_ps[b], post,
+                                I_all[b][:n_all[b]], f"{cfg.name} t={t} l={l} b={b}")
+        B.dllm_commit(model.h, st, cfg.conf_threshold, cfg.tau)
+
+
+@pytest.mark.parametrize("cfg", [MED, MED_GQA], ids=lambda c: c.name)
+def test_polestar_layerwise(cfg):
+    say(f"== {cfg.name}")
+    spec = spec_of(cfg)
+    model, layers, head = build(cfg)
+    st = runtime.State(cfg)
+    pst = runtime.PolestarState(cfg)
+    runtime.step(model, st, mode=B.DLLM_MODE_FULL, polestar_state=pst)
+    _run(cfg, layers, model, st, pst, cfg.n_steps, set(range(cfg.n_layers)), range(cfg.batch), spec)
+    model.close()
+
+
+def test_polestar_step_equals_entry_points():
+    """dllm_step with the Polestar score is bit-for-bit the composition of the
+    entry points (embed, polestar drift/select, sparse layer, commit)."""
+    cfg = MED
+    model, _, _ = build(cfg)
+    a, pa = runtime.State(cfg), runtime.PolestarState(cfg)
+    runtime.step(model, a, mode=B.DLLM_MODE_FULL, polestar_state=pa)
+    b_, pb = runtime.State(cfg), runtime.PolestarState(cfg)
+    for k, v in a.tensors().items():
+        getattr(b_, k).copy_(v)
+    for t in range(3):
+        runtime.step(model, a, mode=B.DLLM_MODE_SPARSE, polestar_state=pa)
+        _run(cfg, None, model, b_, pb, 1, set(), [], None)
+        torch.cuda.synchronize()
+        for k, v in a.tensors().items():
+            assert torch.equal(v, getattr(b_, k)), f"t={t}: {k} differs"
+        for k in ("log_attn", "win_start", "assign", "codes", "scales", "kl", "top"):
+            assert torch.equal(getattr(pa, k), getattr(pb, k)), f"t={t}: polestar {k} differs"
+    model.close()
+
+
+def test_c5_full_size_sampled():
+    """The C5 shape: LLaDA-8B layers, batch 4, L = 4096 (2048 prompt), window 96,
+    16 clusters, 10 iterations, top 4; checks on layers 0 and 31 of sequences 0
+    and 3 over two sparse steps."""
+    cfg = configs.C5
+    spec = spec_of(cfg)
+    N = cfg.n_layers
+    check = {0, N - 1}
+    say("== C5: building the 32-layer model")
+    model = runtime.Model(cfg, "cuda")
+    W = {l: np_weights(inputs.layer_weights(cfg, l, "cuda")) for l in check}
+    torch.cuda.empty_cache()
+    st = runtime.State(cfg)
+    pst = runtime.PolestarState(cfg)
+    runtime.step(model, st, mode=B.DLLM_MODE_FULL, polestar_state=pst)
+    say("C5: full pass done")
+    _run(cfg, W, model, st, pst, 2, check, (0, 3), spec)
+    model.close()
