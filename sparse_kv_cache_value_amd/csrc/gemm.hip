@@ -315,29 +315,61 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming bf16 GEMM for up to 192 rows (6 row tiles).
+// Weight-streaming bf16 GEMM for up to 384 rows (12 row tiles).
 //
 // Workgroup = 4 waves and a 128-column slab; wave w owns column tile w of the
 // slab and every row tile.  Each wave streams its own weight tile straight
-// from HBM into a register ring of 4*NA k16 steps (no LDS on the weight
-// path); the activation chunk (64 k, all row tiles) is loaded once per
-// workgroup, staged in a triple-buffered LDS ring and shared by the 4 waves,
-// and the next step's activation fragments are read from LDS while the
-// current step multiplies.  Activation chunks are loaded NA+1 chunks ahead:
-// vmcnt counts loads in issue order, so both streams must be consumed at the
-// same distance or a wait for one drains the other.  EPI as above.
+// from HBM into a register ring of 16 k16 steps (no LDS on the weight path).
+// The activation chunk (64 k, all row tiles) goes from global memory straight
+// into LDS by DMA (global_load_lds_dwordx4: no registers, no ds_write), into a
+// ring of NS chunk slots requested NS-1 chunks ahead, and is shared by the 4
+// waves; the next step's activation fragments are read from LDS while the
+// current step multiplies.
+//
+// The DMA is issued from inline asm so that the compiler does not make every
+// later LDS read wait for it; its completion is waited for explicitly.  vmcnt
+// retires in issue order, and the order of the memory operations inside a
+// step is pinned by scheduling barriers, so the number of operations issued
+// after the request of chunk c+1 is a compile-time constant (DMA_AFTER): a
+// wait down to that count (minus a margin) followed by a workgroup barrier
+// makes chunk c+1 visible to every wave before its first fragment is read.
+// The compiler's own waits for the weight ring see only the weight loads, so
+// they wait at least as long as needed.  EPI as above.
 // ---------------------------------------------------------------------------
 constexpr int GS_KC = 4;  // k16 steps per activation chunk
+constexpr int GS_MAXMT = 12;
 
-// NA activation chunks in flight in registers; weight ring depth 4*NA steps, so
-// that both streams are waited for at the same distance (vmcnt is in order).
-template <int MT, int NA, int EPI>
+template <int MT>
+struct StreamShape {
+  static constexpr int NS = MT <= 9 ? 4 : 3;  // activation ring slots (chunks)
+  static constexpr int P = NS - 1;             // chunks requested ahead
+  static constexpr int NW = 4;  // chunks per weight-ring turn (ring depth GS_KC * NW steps)
+  // VMEM operations issued after the request of chunk c+1 (step 0 of chunk
+  // c+1-P, before that step's weight refill) until the wait at the end of
+  // step GS_KC-2 of chunk c: the rest of that chunk's refills, MT requests and
+  // GS_KC refills for each chunk in between, MT requests and GS_KC-1 refills in
+  // chunk c.
+  static constexpr int DMA_AFTER = GS_KC + (P - 2) * (MT + GS_KC) + MT + (GS_KC - 1);
+  static constexpr int WAIT = DMA_AFTER - 2;
+  static constexpr size_t LDS = (size_t)NS * GS_KC * MT * 64 * 16;
+  static_assert(WAIT >= 0 && WAIT < 64, "vmcnt field");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt untouched)
+#define GS_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
+
+template <int MT, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __restrict__ Ap, int MTt,
                                                        const u32x4* __restrict__ Wp, float* __restrict__ out,
                                                        uint16_t* __restrict__ act, int MTt_out,
                                                        const int32_t* __restrict__ n_sel, int B, int K, int N,
                                                        int kps, int n_slabs, int total, int cap) {
-  extern __shared__ u32x4 lds[];  // A ring: [3][GS_KC][MT][64]
+  using S = StreamShape<MT>;
+  constexpr int NS = S::NS, P = S::P;
+  extern __shared__ u32x4 lds[];  // activation ring: [NS][GS_KC][MT][64]
   constexpr int ABUF = GS_KC * MT * 64;
   const int G = gridDim.x;
   const int w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
@@ -351,31 +383,35 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
   const int NT = N >> 5, KT = K >> 4;
   const int nt = min(slab * 4 + wv, NT - 1);
   const int kt0 = (split * kps) >> 4;
-  constexpr int GS_D = GS_KC * NA;  // weight ring depth (k16 steps)
+  constexpr int GS_NW = S::NW;
+  constexpr int GS_D = GS_KC * GS_NW;  // weight ring depth (k16 steps)
   const int nsteps = kps >> 4, nch = nsteps / GS_KC, nsup = nsteps / GS_D;
 
-  // weight ring: slot j holds step s with s % GS_D == j
   const u32x4* wsrc = Wp + ((size_t)nt * KT + kt0) * 64 + lane;
-  u32x4 wr[GS_D];
-#pragma unroll
-  for (int j = 0; j < GS_D; ++j) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(j, nsteps - 1) * 64);
-
-  // activation chunk c: wave wv loads step wv of the chunk for every row tile
-  const u32x4* asrc = Ap + (size_t)(kt0 + wv) * MTt * 64 + lane;
-  u32x4 ra[NA][MT];
-  auto load_a = [&](int c, u32x4* dst) {
+  // chunk c: wave wv requests step wv of the chunk for every row tile (row
+  // tiles past M repeat the last one; chunks past the range repeat the last).
+  // Fragment base in scalar registers, lane byte offset in one VGPR; the DMA
+  // writes lane l's 16 bytes at m0 + 16 l.
+  const unsigned voff = (unsigned)lane * 16u;
+  auto request_a = [&](int c) {
     const int cc = min(c, nch - 1);
+    const int slot = c % NS;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is only ever set here
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      dst[mt] = asrc[((size_t)cc * GS_KC * MTt + min(mt, m_tiles - 1)) * 64];
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4* g = Ap + ((size_t)(kt0 + wv + cc * GS_KC) * MTt + min(mt, m_tiles - 1)) * 64;
+      const unsigned l = (unsigned)(uintptr_t)(lds_void_t*)&lds[slot * ABUF + (wv * MT + mt) * 64];
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(l)),
+                   "v"(voff), "s"(g)
+                   : "memory", "m0");
+    }
+#pragma clang diagnostic pop
   };
-  auto store_a = [&](int buf, const u32x4* src) {
+  auto read_af = [&](int c, int st, u32x4* dst) {
+    const int slot = c % NS;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) lds[buf * ABUF + (wv * MT + mt) * 64 + lane] = src[mt];
-  };
-  auto read_af = [&](int buf, int st, u32x4* dst) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) dst[mt] = lds[buf * ABUF + (st * MT + mt) * 64 + lane];
+    for (int mt = 0; mt < MT; ++mt) dst[mt] = lds[slot * ABUF + (st * MT + mt) * 64 + lane];
   };
 
   f32x16_t acc[MT];
@@ -384,56 +420,58 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
 
-  // LDS holds chunks c and c+1 while chunk c is multiplied; chunks c+2 ..
-  // c+NA+1 are in flight in registers (slot x % NA).
-  load_a(0, ra[0]);
-  load_a(1, ra[1 % NA]);
-  store_a(0, ra[0]);
-  store_a(1, ra[1 % NA]);
 #pragma unroll
-  for (int x = 2; x < NA + 2; ++x) load_a(x, ra[x % NA]);
-  __syncthreads();
+  for (int c = 0; c < P; ++c) request_a(c);
+  u32x4 wr[GS_D];  // slot j holds step s with s % GS_D == j
+#pragma unroll
+  for (int j = 0; j < GS_D; ++j) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(j, nsteps - 1) * 64);
+  GS_WAIT_VM_LGKM0(0);
+  __builtin_amdgcn_s_barrier();
   u32x4 af[2][MT];
   read_af(0, 0, af[0]);
-  int b0 = 0, b1 = 1, b2 = 2;  // LDS slots of chunks c, c+1, c+2
   for (int sc = 0; sc < nsup; ++sc) {
 #pragma unroll
-    for (int cc = 0; cc < NA; ++cc) {
-      const int c = sc * NA + cc;
+    for (int cc = 0; cc < GS_NW; ++cc) {
+      const int c = sc * GS_NW + cc;
 #pragma unroll
       for (int st = 0; st < GS_KC; ++st) {
         const int j = cc * GS_KC + st;
         const int s = c * GS_KC + st;
         // the next step's activation fragments are read while this step multiplies
-        if (st + 1 < GS_KC) read_af(b0, st + 1, af[(j + 1) & 1]);
-        else read_af(b1, 0, af[(j + 1) & 1]);
+        if (st + 1 < GS_KC) read_af(c, st + 1, af[(j + 1) & 1]);
+        else read_af(c + 1, 0, af[(j + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8_t b = __builtin_bit_cast(bf16x8_t, wr[j]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[j & 1][mt]), b, acc[mt],
                                                             0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // slot (c+P) % NS held chunk c-1, which every wave finished reading
+        // before the barrier of chunk c-1
+        if (st == 0) request_a(c + P);
+        __builtin_amdgcn_sched_barrier(0);
         // refill the slot only after its last use, so the new load can take
         // the same registers (no copy of an in-flight load at the back edge)
-        __builtin_amdgcn_sched_barrier(0);
         wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(s + GS_D, nsteps - 1) * 64);
-        if (st == 0) load_a(c + NA + 1, ra[(cc + 1) % NA]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st == GS_KC - 2) {
+          // this wave's requests for chunk c+1 have landed and its reads of
+          // chunk c are complete; after the barrier, for every wave
+          GS_WAIT_VM_LGKM0(S::WAIT);
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      store_a(b2, ra[(cc + 2) % NA]);
-      __syncthreads();
-      const int t = b0;
-      b0 = b1;
-      b1 = b2;
-      b2 = t;
     }
   }
+  GS_WAIT_VM_LGKM0(0);  // no request may still be writing LDS
 
   if constexpr (EPI == 0) {
     const int ncol = nt * 32 + (lane & 31);
     if (slab * 4 + wv < NT) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (mt >= m_tiles) break;
         const int mrow = mt * 32 + (lane >> 5) * 4;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -444,6 +482,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
     }
   } else {
     // gate tile 2p (wave 2p), up tile 2p+1 (wave 2p+1): exchange through LDS
+    __builtin_amdgcn_s_barrier();
     float* ex = reinterpret_cast<float*>(lds);  // [2][MT][16][64]
     const int p = wv >> 1;
     if (wv & 1) {
@@ -457,7 +496,6 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
       const int f = (slab * 2 + p) * 32 + (lane & 31);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (mt >= m_tiles) break;
         const int mrow = mt * 32 + (lane >> 5) * 4;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -471,33 +509,33 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
     }
   }
 }
+#undef GS_WAIT_VM_LGKM0
 
-
-template <int MT, int NA, int EPI>
+template <int MT, int EPI>
 static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
                              uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
                              int n_slabs, int total, int cap) {
   static bool attr_set = false;
-  const size_t lds = (size_t)3 * GS_KC * MT * 64 * 16;
+  const size_t lds = StreamShape<MT>::LDS;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_stream_kernel<MT, NA, EPI>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_stream_kernel<MT, EPI>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_stream_kernel<MT, NA, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
+  hipLaunchKernelGGL((gemm_stream_kernel<MT, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
                      (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, cap);
   return hipGetLastError();
 }
 
 static int stream_mt(int max_rows) {
   const int t = (max_rows + 31) / 32;
-  return t <= 2 ? 2 : (t <= 4 ? 4 : (t <= 6 ? 6 : -1));
+  return t <= GS_MAXMT ? (t < 1 ? 1 : t) : -1;
 }
 
 // Split count for the streaming kernel: K must split into multiples of 256;
 // the largest split whose workgroup count still fits the chip in one pass (one
-// per CU).  0 when the shape does not suit the kernel (more than 192 rows, or
+// per CU).  0 when the shape does not suit the kernel (more than 384 rows, or
 // more row tiles than the activation buffer holds).
 int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, int MTt) {
   const int mt = stream_mt(max_rows);
@@ -522,16 +560,16 @@ hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N,
   if (act != nullptr && splits != 1) return hipErrorInvalidValue;
   const int total = n_slabs * splits;
   const int grid = (total + 7) / 8 * 8;
-#define GSL(MT_, EPI_) \
-  stream_cfg<MT_, 4, EPI_>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, max_rows)
-  if (act == nullptr) {
-    if (mt == 2) return GSL(2, 0);
-    if (mt == 4) return GSL(4, 0);
-    return GSL(6, 0);
+#define GSL(MT_)                                                                                                  \
+  case MT_:                                                                                                       \
+    return act ? stream_cfg<MT_, 1>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, \
+                                    max_rows)                                                                     \
+               : stream_cfg<MT_, 0>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, \
+                                    max_rows);
+  switch (mt) {
+    GSL(1) GSL(2) GSL(3) GSL(4) GSL(5) GSL(6) GSL(7) GSL(8) GSL(9) GSL(10) GSL(11) GSL(12)
+    default: return hipErrorInvalidValue;
   }
-  if (mt == 2) return GSL(2, 1);
-  if (mt == 4) return GSL(4, 1);
-  return GSL(6, 1);
 #undef GSL
 }
 

@@ -115,7 +115,8 @@ hipError_t launch_embed(hipStream_t st, bool bf16m, int max_rows, int B, int L, 
 // One workgroup per row; each thread holds up to RV groups of 8 consecutive
 // values in registers between the statistics and the normalised store.
 // ---------------------------------------------------------------------------
-constexpr int RV = 4;  // groups of 8 per thread: d <= 256 * 8 * RV
+constexpr int RT = 512;  // threads of the row-wide (normalising) kernels
+constexpr int RV = 2;    // groups of 8 per thread: d <= RT * 8 * RV
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* v);
@@ -164,12 +165,12 @@ __device__ __forceinline__ float4 sum_splits4(const float* __restrict__ p, size_
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void gather_norm_kernel(int B, int L, int d, float eps, int MTt,
+__global__ __launch_bounds__(RT) void gather_norm_kernel(int B, int L, int d, float eps, int MTt,
                                                           const int32_t* __restrict__ idx,
                                                           const int32_t* __restrict__ n,
                                                           const T* __restrict__ H, const float* __restrict__ g,
                                                           T* __restrict__ A) {
-  __shared__ float red[4];
+  __shared__ float red[RT / 64];
   int b, i;
   const int m = blockIdx.x;
   if (!row_of(idx, n, B, L, m, b, i)) return;
@@ -178,18 +179,18 @@ __global__ __launch_bounds__(256) void gather_norm_kernel(int B, int L, int d, f
   float ss = 0.f;
 #pragma unroll
   for (int r = 0; r < RV; ++r) {
-    const int c8 = (threadIdx.x + r * 256) * 8;
+    const int c8 = (threadIdx.x + r * RT) * 8;
     if (c8 < d) {
       load8<T>(x + c8, v[r]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += v[r][e] * v[r][e];
     }
   }
-  ss = block_sum<4>(ss, red);
+  ss = block_sum<RT / 64>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
   for (int r = 0; r < RV; ++r) {
-    const int c8 = (threadIdx.x + r * 256) * 8;
+    const int c8 = (threadIdx.x + r * RT) * 8;
     if (c8 < d) {
       float o[8];
 #pragma unroll
@@ -204,10 +205,10 @@ hipError_t launch_gather_norm(hipStream_t st, bool bf16m, int max_rows, int B, i
                               void* A) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(gather_norm_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, eps, MTt, idx, n,
+    hipLaunchKernelGGL(gather_norm_kernel<bf16>, dim3(max_rows), dim3(RT), 0, st, B, L, d, eps, MTt, idx, n,
                        (const bf16*)H, g, (bf16*)A);
   else
-    hipLaunchKernelGGL(gather_norm_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, eps, MTt, idx, n,
+    hipLaunchKernelGGL(gather_norm_kernel<float>, dim3(max_rows), dim3(RT), 0, st, B, L, d, eps, MTt, idx, n,
                        (const float*)H, g, (float*)A);
   return hipGetLastError();
 }
@@ -234,7 +235,8 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq,
   const float* p0 = part + (size_t)m * N;
   // rotary pairs, four consecutive j per item
   const int nquads = (Hq + Hkv) * (half / 4);
-  for (int p = threadIdx.x; p < nquads; p += 256) {
+  const int t0 = blockIdx.y * 256 + threadIdx.x, tstep = 256 * gridDim.y;
+  for (int p = t0; p < nquads; p += tstep) {
     const int head = p / (half / 4), j = (p - head * (half / 4)) * 4;
     const int c0 = head * dh + j, c1 = c0 + half;
     const float4 a = sum_splits4(p0 + c0, sstride, S), c = sum_splits4(p0 + c1, sstride, S);
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq,
       store4<T>(kb + kc_off(i, j + half, dh), r1);
     }
   }
-  for (int c4 = threadIdx.x * 4; c4 < nv; c4 += 256 * 4) {
+  for (int c4 = t0 * 4; c4 < nv; c4 += tstep * 4) {
     const float4 v = sum_splits4(p0 + nq + nv + c4, sstride, S);
     const int g = c4 / dh, t = c4 - g * dh;
     T* vb = Vc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * dh;
@@ -271,11 +273,11 @@ hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, 
                                void* Vc) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(qkv_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, Hq, Hkv, dh, S, max_rows,
-                       idx, n, part, rope_cos, rope_sin, (bf16*)q_out, (bf16*)Kc, (bf16*)Vc);
+    hipLaunchKernelGGL(qkv_epilogue_kernel<bf16>, dim3(max_rows, 4), dim3(256), 0, st, B, L, Hq, Hkv, dh, S,
+                       max_rows, idx, n, part, rope_cos, rope_sin, (bf16*)q_out, (bf16*)Kc, (bf16*)Vc);
   else
-    hipLaunchKernelGGL(qkv_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, Hq, Hkv, dh, S, max_rows,
-                       idx, n, part, rope_cos, rope_sin, (float*)q_out, (float*)Kc, (float*)Vc);
+    hipLaunchKernelGGL(qkv_epilogue_kernel<float>, dim3(max_rows, 4), dim3(256), 0, st, B, L, Hq, Hkv, dh, S,
+                       max_rows, idx, n, part, rope_cos, rope_sin, (float*)q_out, (float*)Kc, (float*)Vc);
   return hipGetLastError();
 }
 
@@ -284,13 +286,13 @@ hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, 
 // order), then the FFN norm into the next GEMM's input.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, int S, int cap, float eps, int MTt,
+__global__ __launch_bounds__(RT) void o_epilogue_kernel(int B, int L, int d, int S, int cap, float eps, int MTt,
                                                          const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ n,
                                                          const float* __restrict__ part,
                                                          const T* __restrict__ H, const float* __restrict__ g2,
                                                          float* __restrict__ hprime, T* __restrict__ A2) {
-  __shared__ float red[4];
+  __shared__ float red[RT / 64];
   int b, i;
   const int m = blockIdx.x;
   if (!row_of(idx, n, B, L, m, b, i)) return;
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, in
   float ss = 0.f;
 #pragma unroll
   for (int r = 0; r < RV; ++r) {
-    const int c8 = (threadIdx.x + r * 256) * 8;
+    const int c8 = (threadIdx.x + r * RT) * 8;
     if (c8 < d) {
       load8<T>(x + c8, v[r]);
       const float4 a = sum_splits4(p0 + c8, sstride, S), c = sum_splits4(p0 + c8 + 4, sstride, S);
@@ -315,11 +317,11 @@ __global__ __launch_bounds__(256) void o_epilogue_kernel(int B, int L, int d, in
       for (int e = 0; e < 8; ++e) ss += v[r][e] * v[r][e];
     }
   }
-  ss = block_sum<4>(ss, red);
+  ss = block_sum<RT / 64>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
   for (int r = 0; r < RV; ++r) {
-    const int c8 = (threadIdx.x + r * 256) * 8;
+    const int c8 = (threadIdx.x + r * RT) * 8;
     if (c8 < d) {
       float o[8];
 #pragma unroll
@@ -334,10 +336,10 @@ hipError_t launch_o_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, in
                              const void* H, const float* g2, float* hprime, void* A2) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(o_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, MTt,
+    hipLaunchKernelGGL(o_epilogue_kernel<bf16>, dim3(max_rows), dim3(RT), 0, st, B, L, d, S, max_rows, eps, MTt,
                        idx, n, part, (const bf16*)H, g2, hprime, (bf16*)A2);
   else
-    hipLaunchKernelGGL(o_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, S, max_rows, eps, MTt,
+    hipLaunchKernelGGL(o_epilogue_kernel<float>, dim3(max_rows), dim3(RT), 0, st, B, L, d, S, max_rows, eps, MTt,
                        idx, n, part, (const float*)H, g2, hprime, (float*)A2);
   return hipGetLastError();
 }
@@ -395,11 +397,12 @@ __global__ __launch_bounds__(256) void down_epilogue_kernel(int B, int L, int d,
   T* o = Hout + row * d;
   const float* hp = hprime + (size_t)m * d;
   const float* p0 = part + (size_t)m * d;
-  for (int c4 = threadIdx.x * 4; c4 < d; c4 += 256 * 4) {
+  for (int c4 = (blockIdx.y * 256 + threadIdx.x) * 4; c4 < d; c4 += 256 * gridDim.y * 4) {
     const float4 a = sum_splits4(p0 + c4, sstride, S);
     const float4 h = *reinterpret_cast<const float4*>(hp + c4);
     store4<T>(o + c4, make_float4(h.x + a.x, h.y + a.y, h.z + a.z, h.w + a.w));
   }
+  if (blockIdx.y != 0) return;
   for (int j = threadIdx.x; j < r; j += 256) pref[row * r + j] = pcur[row * r + j];
   if (threadIdx.x == 0) score[row] = 0.0;
 }
@@ -410,10 +413,10 @@ hipError_t launch_down_epilogue(hipStream_t st, bool bf16m, int max_rows, int B,
                                 double* score) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(down_epilogue_kernel<bf16>, dim3(max_rows), dim3(256), 0, st, B, L, d, r, S, max_rows, idx, n,
+    hipLaunchKernelGGL(down_epilogue_kernel<bf16>, dim3(max_rows, 4), dim3(256), 0, st, B, L, d, r, S, max_rows, idx, n,
                        part, hprime, (bf16*)H_out, pcur, pref, score);
   else
-    hipLaunchKernelGGL(down_epilogue_kernel<float>, dim3(max_rows), dim3(256), 0, st, B, L, d, r, S, max_rows, idx, n,
+    hipLaunchKernelGGL(down_epilogue_kernel<float>, dim3(max_rows, 4), dim3(256), 0, st, B, L, d, r, S, max_rows, idx, n,
                        part, hprime, (float*)H_out, pcur, pref, score);
   return hipGetLastError();
 }

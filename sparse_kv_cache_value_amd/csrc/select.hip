@@ -2,7 +2,7 @@
 //
 // Forced rows (current mask block, recent decoded tokens) are always in I;
 // the remaining max(k, |F|) - |F| rows are the non-forced rows with the
-// largest drift score, ties to the lower index.  One 1024-thread workgroup
+// largest drift score, ties to the lower index.  One 256-thread workgroup
 // per sequence; thread t owns the contiguous rows [t*E, t*E + E).  The k-th
 // largest score is found by an exact MSB-first radix select over the fp64
 // bit patterns (non-negative doubles order like their unsigned bits), stopping
@@ -14,9 +14,9 @@
 
 namespace dllm {
 
-constexpr int SEL_T = 1024;
+constexpr int SEL_T = 256;  // 4 waves: cheap barriers between the radix passes
 constexpr int SEL_W = SEL_T / 64;
-constexpr int SEL_EMAX = 8;  // L <= 8192
+constexpr int SEL_EMAX = 32;  // L <= 8192
 
 // Exclusive prefix sum over the block (thread order); *total gets the sum.
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
@@ -45,6 +45,8 @@ __device__ __forceinline__ uint64_t score_key(double s) {
   return (u >> 63) ? 0ull : u;  // -0.0 (and negatives, which drift never yields) rank as +0
 }
 
+// EM: rows held per thread, the smallest of 8/16/32 that covers ceil(L/256).
+template <int EM>
 __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const double* __restrict__ score,
                                                        const uint8_t* __restrict__ forced,
                                                        const uint8_t* __restrict__ full,
@@ -58,11 +60,11 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
   const double* s = score + (size_t)b * L;
   const uint8_t* fr = forced ? forced + (size_t)b * L : nullptr;
 
-  uint64_t key[SEL_EMAX];
-  int cls[SEL_EMAX];  // 0 = candidate, 1 = forced, 2 = past the end
+  uint64_t key[EM];
+  int cls[EM];  // 0 = candidate, 1 = forced, 2 = past the end
   int nf = 0;
 #pragma unroll
-  for (int e = 0; e < SEL_EMAX; ++e) {
+  for (int e = 0; e < EM; ++e) {
     const int i = i0 + e;
     key[e] = 0;
     cls[e] = 2;
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
       if (tid < 256) hist[tid] = 0;
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < SEL_EMAX; ++e) {
+      for (int e = 0; e < EM; ++e) {
         // the leading digits of nearby scores mostly agree: when every
         // participating lane of the wave has the same digit, one lane adds the
         // count (LDS atomics to one address serialise)
@@ -145,20 +147,20 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
     // compare on the resolved high bits only: below the last pass every row
     // sharing the prefix is either all taken or ranked by index
 #pragma unroll
-    for (int e = 0; e < SEL_EMAX; ++e) key[e] &= pmask;
+    for (int e = 0; e < EM; ++e) key[e] &= pmask;
   }
   // rank of each equal-to-threshold candidate in index order
   int neq = 0;
   if (mode == 2) {
 #pragma unroll
-    for (int e = 0; e < SEL_EMAX; ++e) neq += (cls[e] == 0 && key[e] == thr);
+    for (int e = 0; e < EM; ++e) neq += (cls[e] == 0 && key[e] == thr);
   }
   int tot_eq;
   int eq_before = block_excl_scan(neq, wsum, &tot_eq);
-  bool sel[SEL_EMAX];
+  bool sel[EM];
   int nsel = 0;
 #pragma unroll
-  for (int e = 0; e < SEL_EMAX; ++e) {
+  for (int e = 0; e < EM; ++e) {
     bool v = false;
     if (cls[e] == 1) {
       v = true;
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
   int pos = block_excl_scan(nsel, wsum, &total);
   int32_t* out = idx + (size_t)b * L;
 #pragma unroll
-  for (int e = 0; e < SEL_EMAX; ++e)
+  for (int e = 0; e < EM; ++e)
     if (sel[e]) out[pos++] = i0 + e;
   if (tid == 0) n_out[b] = total;
 }
@@ -188,7 +190,12 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
 hipError_t launch_select(hipStream_t st, int B, int L, int k, const double* score, const uint8_t* forced,
                          const uint8_t* full, int32_t* idx, int32_t* n) {
   if (L > SEL_T * SEL_EMAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(select_kernel, dim3(B), dim3(SEL_T), 0, st, L, k, score, forced, full, idx, n);
+  if (L <= SEL_T * 8)
+    hipLaunchKernelGGL(select_kernel<8>, dim3(B), dim3(SEL_T), 0, st, L, k, score, forced, full, idx, n);
+  else if (L <= SEL_T * 16)
+    hipLaunchKernelGGL(select_kernel<16>, dim3(B), dim3(SEL_T), 0, st, L, k, score, forced, full, idx, n);
+  else
+    hipLaunchKernelGGL(select_kernel<32>, dim3(B), dim3(SEL_T), 0, st, L, k, score, forced, full, idx, n);
   return hipGetLastError();
 }
 

@@ -1,0 +1,68 @@
+"""One sparse layer at every row-count regime of the dense contractions.
+
+The gathered-row GEMMs pick their kernel and tiling from the row count M
+(1..384 rows: the weight-streaming kernel with 1..12 row tiles and split K;
+more rows: the row-blocked kernel).  Each case refreshes a random index set of
+M rows spread over the batch and compares the new hidden rows, keys and values
+with the oracle's sparse layer on the same inputs.  The host row bound
+``max_rows`` is passed both exact and loose (the kernels read the true count on
+the device).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import TOL, Snap, assert_close, build, medium_cfg, say
+from helpers import spec_of
+from sparse_kv_cache_value_amd import binding as B
+from sparse_kv_cache_value_amd import runtime
+
+pytestmark = pytest.mark.gpu
+
+# (rows in batch 0, rows in batch 1, extra slack on the host bound)
+CASES = [(1, 0, 0), (17, 16, 0), (50, 40, 0), (40, 57, 5), (70, 65, 0), (100, 91, 0), (120, 73, 0),
+         (128, 128, 0), (140, 131, 0), (150, 133, 9), (190, 162, 0), (200, 184, 0), (240, 145, 0), (256, 256, 0)]
+
+
+def test_sparse_layer_row_counts():
+    torch.manual_seed(0)
+    cfg = medium_cfg(name="rows-bf16", n_layers=1, batch=2, seq_len=256, prompt_len=128, seed=31, n_steps=1)
+    spec = spec_of(cfg)
+    tol = TOL[cfg.dtype]
+    model, layers, head = build(cfg)
+    st = runtime.State(cfg)
+    Bn, L = cfg.batch, cfg.seq_len
+    runtime.step(model, st, mode=B.DLLM_MODE_FULL)
+    rng = np.random.default_rng(7)
+    dev = "cuda"
+    for (n0, n1, slack) in CASES:
+        counts = (n0, n1)
+        M = n0 + n1
+        idx_h = np.zeros((Bn, L), np.int32)
+        for b in range(Bn):
+            idx_h[b, :counts[b]] = np.sort(rng.choice(L, counts[b], replace=False))
+        idx = torch.from_numpy(idx_h).to(dev)
+        n = torch.tensor(counts, dtype=torch.int32, device=dev)
+        say(f"rows case M={M} ({n0}+{n1}) max_rows={M + slack}")
+        Sd = Snap(st)
+        B.dllm_sparse_layer(model.h, 0, st, idx, n, max_rows=M + slack)
+        Sa = Snap(st)
+        for b in range(Bn):
+            I = idx_h[b, :counts[b]].astype(np.int64)
+            x = Sd.H[0][b]
+            Kx, Vx, Hx = Sd.K[0][b].copy(), Sd.V[0][b].copy(), Sd.H[1][b].copy()
+            oracle.sparse_layer(x, Kx, Vx, Hx, I, layers[0], spec)
+            mask = np.zeros(L, bool)
+            mask[I] = True
+            if I.size:
+                e = assert_close(Sa.H[1][b][mask], Hx[mask], tol, f"M={M} b={b} H")
+                assert_close(Sa.K[0][b][mask], Kx[mask], tol, f"M={M} b={b} K")
+                assert_close(Sa.V[0][b][mask], Vx[mask], tol, f"M={M} b={b} V")
+                say(f"  b={b} |I|={I.size} H rel err {e:.2e}")
+            assert np.array_equal(Sa.H[1][b][~mask], Sd.H[1][b][~mask]), "rows outside I changed"
+            assert np.array_equal(Sa.K[0][b][~mask], Sd.K[0][b][~mask]), "keys outside I changed"
+    model.close()
