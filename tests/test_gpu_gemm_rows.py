@@ -1,12 +1,13 @@
-"""One sparse layer at every row-count regime of the dense contractions.
+"""One sparse layer at every row-count regime of the kernels.
 
 The gathered-row GEMMs pick their kernel and tiling from the row count M
 (1..384 rows: the weight-streaming kernel with 1..12 row tiles and split K;
-more rows: the row-blocked kernel).  Each case refreshes a random index set of
-M rows spread over the batch and compares the new hidden rows, keys and values
-with the oracle's sparse layer on the same inputs.  The host row bound
-``max_rows`` is passed both exact and loose (the kernels read the true count on
-the device).
+more rows: the row-blocked kernel); attention runs 1..33 query tiles per head
+over a 1024-key cache.  Each case refreshes a
+random index set of M rows spread over the batch and compares the new hidden
+rows, keys and values with the oracle's sparse layer on the same inputs.  The
+host row bound ``max_rows`` is passed both exact and loose (the kernels read
+the true count on the device).
 """
 
 from __future__ import annotations
@@ -28,9 +29,8 @@ CASES = [(1, 0, 0), (17, 16, 0), (50, 40, 0), (40, 57, 5), (70, 65, 0), (100, 91
          (128, 128, 0), (140, 131, 0), (150, 133, 9), (190, 162, 0), (200, 184, 0), (240, 145, 0), (256, 256, 0)]
 
 
-def test_sparse_layer_row_counts():
+def _run_cases(cfg, cases):
     torch.manual_seed(0)
-    cfg = medium_cfg(name="rows-bf16", n_layers=1, batch=2, seq_len=256, prompt_len=128, seed=31, n_steps=1)
     spec = spec_of(cfg)
     tol = TOL[cfg.dtype]
     model, layers, head = build(cfg)
@@ -39,15 +39,15 @@ def test_sparse_layer_row_counts():
     runtime.step(model, st, mode=B.DLLM_MODE_FULL)
     rng = np.random.default_rng(7)
     dev = "cuda"
-    for (n0, n1, slack) in CASES:
-        counts = (n0, n1)
-        M = n0 + n1
+    for case in cases:
+        counts, slack = case[:-1], case[-1]
+        M = sum(counts)
         idx_h = np.zeros((Bn, L), np.int32)
         for b in range(Bn):
             idx_h[b, :counts[b]] = np.sort(rng.choice(L, counts[b], replace=False))
         idx = torch.from_numpy(idx_h).to(dev)
         n = torch.tensor(counts, dtype=torch.int32, device=dev)
-        say(f"rows case M={M} ({n0}+{n1}) max_rows={M + slack}")
+        say(f"{cfg.name}: M={M} {counts} max_rows={M + slack}")
         Sd = Snap(st)
         B.dllm_sparse_layer(model.h, 0, st, idx, n, max_rows=M + slack)
         Sa = Snap(st)
@@ -66,3 +66,17 @@ def test_sparse_layer_row_counts():
             assert np.array_equal(Sa.H[1][b][~mask], Sd.H[1][b][~mask]), "rows outside I changed"
             assert np.array_equal(Sa.K[0][b][~mask], Sd.K[0][b][~mask]), "keys outside I changed"
     model.close()
+
+
+def test_sparse_layer_row_counts():
+    """Every GEMM row-tile count, batch 2."""
+    cfg = medium_cfg(name="rows-bf16", n_layers=1, batch=2, seq_len=256, prompt_len=128, seed=31, n_steps=1)
+    _run_cases(cfg, CASES)
+
+
+@pytest.mark.parametrize("heads,dh", [(8, 64), (4, 128)])
+def test_attention_long_cache(heads, dh):
+    """L = 1024 (GQA 2:1) with 1..1024 selected rows."""
+    cfg = medium_cfg(name=f"split-h{heads}-d{dh}", n_layers=1, batch=1, seq_len=1024, prompt_len=512,
+                     n_q_heads=heads, n_kv_heads=heads // 2, head_dim=dh, seed=33, n_steps=1)
+    _run_cases(cfg, [(1, 0), (37, 3), (200, 0), (700, 0), (1024, 0)])
