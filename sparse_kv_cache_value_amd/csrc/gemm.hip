@@ -400,7 +400,8 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
   // chunk c: wave wv requests step wv of the chunk for every row tile (row
   // tiles past M repeat the last one; chunks past the range repeat the last).
   // Fragment base in scalar registers, lane byte offset in one VGPR; the DMA
-  // writes lane l's 16 bytes at m0 + 16 l.
+  // writes lane l's 16 bytes at m0 + 16 l.  An M0 write needs one wait state
+  // before an LDS DMA (the compiler's hazard pass does not look inside asm).
   const unsigned voff = (unsigned)lane * 16u;
   auto request_a = [&](int c) {
     const int cc = min(c, nch - 1);
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
     for (int mt = 0; mt < MT; ++mt) {
       const u32x4* g = Ap + ((size_t)(kt0 + wv + cc * GS_KC) * MTt + min(mt, m_tiles - 1)) * 64;
       const unsigned l = (unsigned)(uintptr_t)(lds_void_t*)&lds[slot * ABUF + (wv * MT + mt) * 64];
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(l)),
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(l)),
                    "v"(voff), "s"(uniform_ptr(g))
                    : "memory", "m0");
     }
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_quad_kernel(const u32x4* _
       const int stp = f / MT, mt = f % MT;
       const u32x4* g = Ap + ((size_t)(kt0 + cc * GS_KC + stp) * MTt + min(mt, m_tiles - 1)) * 64;
       const unsigned l = (unsigned)(uintptr_t)(lds_void_t*)&lds[slot * ABUF + f * 64];
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(l)),
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(l)),
                    "v"(voff), "s"(uniform_ptr(g))
                    : "memory", "m0");
     }

@@ -80,3 +80,11 @@ def test_attention_long_cache(heads, dh):
     cfg = medium_cfg(name=f"split-h{heads}-d{dh}", n_layers=1, batch=1, seq_len=1024, prompt_len=512,
                      n_q_heads=heads, n_kv_heads=heads // 2, head_dim=dh, seed=33, n_steps=1)
     _run_cases(cfg, [(1, 0), (37, 3), (200, 0), (700, 0), (1024, 0)])
+
+
+def test_wide_layer_shapes():
+    """d = 2048, SwiGLU 5632 (K split 8 and 11 ways, 32..88 slabs), GQA 2:1;
+    1..288 rows."""
+    cfg = medium_cfg(name="wide-bf16", n_layers=1, batch=2, seq_len=256, prompt_len=128, d_model=2048,
+                     n_q_heads=16, n_kv_heads=8, head_dim=128, d_ffn=5632, seed=35, n_steps=1)
+    _run_cases(cfg, [(1, 0, 0), (20, 20, 0), (64, 36, 3), (90, 70, 0), (110, 90, 0), (140, 110, 0), (150, 138, 0)])
