@@ -116,6 +116,81 @@ def cpu_baseline(cfg, budget_s: float = 25.0):
     }
 
 
+WORKLOADS = {
+    "C1": "tiny fp32 dLLM: 2 layers, d=256, 4x64 heads, SwiGLU 1024, vocab 1024, batch 1, L=128 "
+          "(64 prompt + 64 masked, block 32), r=16, k=16 refreshed rows/layer",
+    "C2": "one LLaDA-8B-shaped layer (d=4096, 32x128, SwiGLU 12288) + LM head 4096x126464 on the 32 block "
+          "rows, batch 1, L=512 (256 + 256 masked), k=82 rows, r=128",
+    "C4": "Dream-7B-shaped GQA model: 28 layers, d=3584, 28/4 heads x 128, SwiGLU 18944, vocab 152064, "
+          "batch 8, L=2048 (1024 + 1024 masked), 328 rows/layer per sequence (16%), r=128, "
+          "forced = block + recent 32, gate disabled",
+    "C5": "Polestar drift path on the LLaDA-8B layer shape: 32 layers, batch 4, L=4096 (2048 + 2048 masked), "
+          "window 96, 16 spherical k-means centroids x 10 iterations, NVFP4 residual codes, top-4 clusters",
+}
+
+
+def bench_config(name, steps, warmup):
+    """Sparse steps of one of the other configs (the per-config figures of the
+    scope table's measurement row): tokens/s, TPF, per-layer us, the kernel
+    classes, and the GEMM class against its roofline (HBM, or the bf16 MFMA
+    peak where the GEMMs are compute-bound)."""
+    import torch
+    from sparse_kv_cache_value_amd import binding as B
+    from sparse_kv_cache_value_amd import configs, runtime
+
+    cfg = getattr(configs, name)
+    model = runtime.Model(cfg, "cuda")
+    st = runtime.State(cfg)
+    ps = runtime.PolestarState(cfg) if cfg.score == configs.SCORE_POLESTAR else None
+    stream = torch.cuda.current_stream()
+    runtime.step(model, st, mode=B.DLLM_MODE_FULL, polestar_state=ps)
+    for _ in range(warmup):
+        runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps)
+    torch.cuda.synchronize()
+    nh = int(st.n_history.sum())
+    B.dllm_profile(model.h, True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = B.dllm_profile_read(model.h)
+    B.dllm_profile(model.h, False)
+    tokens = int(st.n_history.sum()) - nh
+    model.close()
+    del st, ps, model
+    torch.cuda.empty_cache()
+    ms = 1e3 * wall / steps
+    classes = {k: {"ms_per_step": round(v["ms"] / steps, 4),
+                   "GB_per_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] > 0 else None,
+                   "TFLOP_per_s": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] > 0 else None}
+               for k, v in prof.items() if v["launches"] > 0}
+    g = prof["gemm"]
+    gb = g["bytes"] / (g["ms"] * 1e-3) / 1e9 if g["ms"] > 0 else 0.0
+    tf = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] > 0 else 0.0
+    # intensity above the machine balance (peak FLOP/s over peak B/s): MFMA-bound
+    mfma_bound = g["bytes"] > 0 and g["flops"] / g["bytes"] > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gb / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = "layer GEMMs (gemm class)"
+    lm_ms = prof["lm_head"]["ms"] / steps
+    return {
+        "workload": WORKLOADS[name],
+        "dtype": "f32" if cfg.dtype == configs.FP32 else "bf16",
+        "tokens_per_s": round(tokens / wall, 3),
+        "ms_per_step": round(ms, 4),
+        "tpf": round(tokens / steps / cfg.batch, 3),
+        "per_layer_sparse_us": round(1e3 * (ms - lm_ms) / cfg.n_layers, 2),
+        "steps": steps,
+        "roofline": roof,
+        "kernel_classes": classes,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +198,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--full-steps", type=int, default=3, help="steps timed with the gate as specified")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the short per-config runs (C1, C2, C4, C5) reported under other_configs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 256 MiB device copy before the timed steps (untimed), the reference kernel for "
                          "the HBM byte counters")
@@ -257,6 +334,13 @@ def main():
         "init_s": round(init_s, 1),
     }
     model.close()
+    del st, model
+    torch.cuda.empty_cache()
+    if not args.no_other_configs:
+        # the other configs of the scope table, a few sparse steps each
+        out["other_configs"] = {}
+        for name, n, w in (("C1", 20, 3), ("C2", 20, 3), ("C4", 8, 2), ("C5", 8, 2)):
+            out["other_configs"][name] = bench_config(name, n, w)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)
