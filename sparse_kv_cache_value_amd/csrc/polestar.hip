@@ -82,29 +82,33 @@ __global__ void ps_gram_reduce_kernel(int W, int nsl, const double* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Spherical k-means on the Gram matrix (one workgroup per sequence).
-// Seeds: window rows stride*j.  Each iteration: assign each row to the cluster
-// of largest dot product (lowest index on ties); every cluster with members
-// and a non-zero member sum becomes the normalised member sum; others keep
-// their centroid.  Then a final assignment.  Outputs the assignment, the row
-// norms and each centroid's coefficients over the unit rows.
+// Spherical k-means on the Gram matrix (one workgroup per sequence, wave j
+// owns cluster j).  Seeds: window rows stride*j.  Each iteration: assign each
+// row to the cluster of largest dot product (lowest index on ties); every
+// cluster with members and a non-zero member sum becomes the normalised
+// member sum; others keep their centroid.  Then a final assignment.  Outputs
+// the assignment, the row norms and each centroid's coefficients over the
+// unit rows.  A cluster's members come from two 64-row ballots and are
+// visited in ascending row order; member sums and the squared norm are added
+// in that order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void ps_kmeans_kernel(int W, int K, int iters, const double* __restrict__ R,
-                                                        int32_t* __restrict__ assign, double* __restrict__ norms,
-                                                        double* __restrict__ coef, int32_t* __restrict__ nsel) {
+constexpr int PS_KM_THREADS = 1024;  // 16 waves: one per cluster (K <= 16)
+
+__global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, int iters, const double* __restrict__ R,
+                                                                 int32_t* __restrict__ assign,
+                                                                 double* __restrict__ norms,
+                                                                 double* __restrict__ coef, int32_t* __restrict__ nsel) {
   extern __shared__ double sm[];
-  double* G = sm;                 // [W][W]
+  double* G = sm;                 // [W][W]  Gram of the unit rows
   double* D = G + W * W;          // [K][W]  centroid . unit row
-  double* V = D + K * W;          // [K][W]  member sums of G rows
-  double* nrm = V + K * W;        // [W]
-  double* n2 = nrm + W;           // [K]
-  int* a = reinterpret_cast<int*>(n2 + K);  // [W]
-  int* cnt = a + W;                          // [K]
+  double* nrm = D + K * W;        // [W]
+  int* a = reinterpret_cast<int*>(nrm + W);  // [W] (W <= 128)
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const double* Rb = R + (size_t)b * W * W;
-  for (int i = tid; i < W; i += 256) nrm[i] = sqrt(Rb[(size_t)i * W + i]);
+  for (int i = tid; i < W; i += PS_KM_THREADS) nrm[i] = sqrt(Rb[(size_t)i * W + i]);
   __syncthreads();
-  for (int e = tid; e < W * W; e += 256) {
+  for (int e = tid; e < W * W; e += PS_KM_THREADS) {
     const int i = e / W, j = e - i * W;
     const double ni = nrm[i], nj = nrm[j];
     G[e] = (ni > 0.0 && nj > 0.0) ? Rb[e] / (ni * nj) : 0.0;
@@ -112,14 +116,14 @@ __global__ __launch_bounds__(256) void ps_kmeans_kernel(int W, int K, int iters,
   const int stride = W / K;
   double* cf = coef + (size_t)b * K * W;
   __syncthreads();
-  for (int e = tid; e < K * W; e += 256) {
+  for (int e = tid; e < K * W; e += PS_KM_THREADS) {
     const int j = e / W, k = e - j * W;
     D[e] = G[(size_t)(stride * j) * W + k];
     cf[e] = (k == stride * j) ? 1.0 : 0.0;
   }
   __syncthreads();
   auto do_assign = [&]() {
-    for (int i = tid; i < W; i += 256) {
+    for (int i = tid; i < W; i += PS_KM_THREADS) {
       int best = 0;
       double bv = D[i];
       for (int j = 1; j < K; ++j) {
@@ -135,38 +139,48 @@ __global__ __launch_bounds__(256) void ps_kmeans_kernel(int W, int K, int iters,
   };
   for (int it = 0; it < iters; ++it) {
     do_assign();
-    for (int e = tid; e < K * W; e += 256) {
-      const int j = e / W, k = e - j * W;
-      double acc = 0.0;
-      for (int i = 0; i < W; ++i)
-        if (a[i] == j) acc += G[(size_t)i * W + k];
-      V[e] = acc;
-    }
-    __syncthreads();
-    for (int j = tid; j < K; j += 256) {
-      double acc = 0.0;
-      int c = 0;
-      for (int k = 0; k < W; ++k)
-        if (a[k] == j) {
-          acc += V[j * W + k];
-          ++c;
+    if (wv < K) {
+      const int j = wv;
+      // members of cluster j, rows 0..63 and 64..127
+      const unsigned long long m0 = __ballot(lane < W && a[lane] == j);
+      const unsigned long long m1 = __ballot(lane + 64 < W && a[lane + 64] == j);
+      // member sums of this lane's columns k = lane, lane + 64
+      double v0 = 0.0, v1 = 0.0;
+      for (int h = 0; h < 2; ++h) {
+        unsigned long long m = h ? m1 : m0;
+        while (m) {
+          const int i = __ffsll((long long)m) - 1 + 64 * h;
+          m &= m - 1;
+          if (lane < W) v0 += G[(size_t)i * W + lane];
+          if (lane + 64 < W) v1 += G[(size_t)i * W + lane + 64];
         }
-      n2[j] = acc;
-      cnt[j] = c;
-    }
-    __syncthreads();
-    for (int e = tid; e < K * W; e += 256) {
-      const int j = e / W, k = e - j * W;
-      if (cnt[j] > 0 && n2[j] > 0.0) {
-        const double nv = sqrt(n2[j]);
-        D[e] = V[e] / nv;
-        cf[e] = (a[k] == j) ? 1.0 / nv : 0.0;
+      }
+      // |member sum|^2 = sum over member columns k (ascending) of v[k]
+      double n2 = 0.0;
+      for (int h = 0; h < 2; ++h) {
+        unsigned long long m = h ? m1 : m0;
+        while (m) {
+          const int k = __ffsll((long long)m) - 1;
+          m &= m - 1;
+          n2 += __shfl(h ? v1 : v0, k, 64);
+        }
+      }
+      if ((m0 | m1) != 0ull && n2 > 0.0) {
+        const double inv = 1.0 / sqrt(n2);
+        if (lane < W) {
+          D[j * W + lane] = v0 * inv;
+          cf[j * W + lane] = ((m0 >> lane) & 1ull) ? inv : 0.0;
+        }
+        if (lane + 64 < W) {
+          D[j * W + lane + 64] = v1 * inv;
+          cf[j * W + lane + 64] = ((m1 >> lane) & 1ull) ? inv : 0.0;
+        }
       }
     }
     __syncthreads();
   }
   do_assign();
-  for (int i = tid; i < W; i += 256) {
+  for (int i = tid; i < W; i += PS_KM_THREADS) {
     assign[(size_t)b * W + i] = a[i];
     norms[(size_t)b * W + i] = nrm[i];
   }
@@ -483,18 +497,18 @@ hipError_t launch_ps_gram(hipStream_t st, bool bf16m, int B, int L, int d, int b
 
 hipError_t launch_ps_kmeans(hipStream_t st, int B, int W, int K, int iters, const double* R, int32_t* assign,
                             double* norms, double* coef, int32_t* nsel) {
-  if (W > PS_WMAX || K > 16 || K < 1 || W < K) return hipErrorInvalidValue;
-  const size_t lds = ((size_t)W * W + 2 * K * W + W + K) * sizeof(double) + (size_t)(W + K) * sizeof(int);
+  if (W > PS_WMAX || W > 128 || K > 16 || K < 1 || W < K) return hipErrorInvalidValue;
+  const size_t lds = ((size_t)W * W + K * W + W) * sizeof(double) + (size_t)W * sizeof(int);
   static bool attr = false;
   if (!attr) {
-    const size_t mx =
-        ((size_t)PS_WMAX * PS_WMAX + 2 * 16 * PS_WMAX + PS_WMAX + 16) * sizeof(double) + (PS_WMAX + 16) * sizeof(int);
+    const size_t mx = ((size_t)PS_WMAX * PS_WMAX + 16 * PS_WMAX + PS_WMAX) * sizeof(double) + PS_WMAX * sizeof(int);
     hipError_t e = hipFuncSetAttribute((const void*)ps_kmeans_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)mx);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(ps_kmeans_kernel, dim3(B), dim3(256), lds, st, W, K, iters, R, assign, norms, coef, nsel);
+  hipLaunchKernelGGL(ps_kmeans_kernel, dim3(B), dim3(PS_KM_THREADS), lds, st, W, K, iters, R, assign, norms, coef,
+                     nsel);
   return hipGetLastError();
 }
 
