@@ -122,7 +122,8 @@ enum { DLLM_SCORE_SPA_COS = 0,       /* SPA-Cache value-proxy cosine + top-k (SP
        DLLM_SCORE_POLESTAR_KL = 1 }; /* Polestar-Cache cluster KL (Polestar, section 2A) */
 
 /* Polestar-Cache drift path parameters.  Window W = window_blocks * block_len
- * rows (<= 120 and <= seq_len); n_clusters <= 16 and <= W; d_model % 128 == 0. */
+ * rows (<= 120 and <= seq_len); n_clusters <= 16 and <= W; d_model % 128 == 0;
+ * head_dim <= 128.  Other shapes return DLLM_E_SHAPE or DLLM_E_UNSUPPORTED. */
 typedef struct {
   int32_t n_clusters;    /* spherical k-means clusters (16) */
   int32_t kmeans_iters;  /* assign/update iterations before the final assignment (10) */

@@ -97,8 +97,7 @@ struct dllm_model {
   int32_t* lm_rows = nullptr;
   int lm_slabs = 0;
   // Polestar drift path workspace
-  double* ps_part = nullptr;   // Gram partials [max_batch][d/128][W][W]
-  double* ps_R = nullptr;      // Gram [max_batch][W][W]
+  double* ps_R = nullptr;      // Gram split partials [max_batch][ps_gram_splits()][W][W]
   double* ps_coef = nullptr;   // centroid coefficients [max_batch][16][W]
   double* ps_klp = nullptr;    // per-head KL [max_batch][Hq][16]
   int32_t* ps_nsel = nullptr;  // centroid rows per sequence
@@ -376,15 +375,15 @@ dllm_status check_polestar(const dllm_model* m, const dllm_state* s, const dllm_
   if (!ps->log_attn || !ps->win_start || !ps->centroids || !ps->norms || !ps->assign || !ps->codes || !ps->scales ||
       !ps->queries || !ps->kl || !ps->top)
     return fail(DLLM_E_ARG, "polestar state has a NULL buffer");
-  if (!m->ps_part) return fail(DLLM_E_UNSUPPORTED, "the Polestar path needs d_model %% 128 == 0");
+  if (!m->ps_R) return fail(DLLM_E_UNSUPPORTED, "the Polestar path needs d_model %% 128 == 0");
   const int W = p->window_blocks * d.block_len;
   if (p->n_clusters < 1 || p->n_clusters > 16) return fail(DLLM_E_ARG, "n_clusters must be in [1, 16]");
   if (p->kmeans_iters < 0) return fail(DLLM_E_ARG, "kmeans_iters < 0");
   if (p->top_clusters < 1 || p->top_clusters > p->n_clusters) return fail(DLLM_E_ARG, "top_clusters out of range");
   if (p->window_blocks < 1 || W > 120 || W > d.seq_len || W < p->n_clusters)
     return fail(DLLM_E_SHAPE, "window of %d rows: need n_clusters <= W <= min(120, seq_len)", W);
-  const size_t lds = ((size_t)p->n_clusters * d.head_dim + (size_t)W * (d.head_dim + 1) + (size_t)p->n_clusters * W) * 8;
-  if (lds > 160 * 1024) return fail(DLLM_E_SHAPE, "proxy attention tile does not fit LDS");
+  if (d.head_dim % 32 || d.head_dim > 128)
+    return fail(DLLM_E_UNSUPPORTED, "the Polestar proxy attention needs head_dim %% 32 == 0 and <= 128");
   (void)s;
   return DLLM_OK;
 }
@@ -396,7 +395,7 @@ dllm_status do_polestar_drift(dllm_model* m, int layer, const dllm_state* s, dll
   const int W = p->window_blocks * blk, K = p->n_clusters, Hq = d.n_q_heads, dh = d.head_dim;
   const LayerW& w = m->layers[layer];
   void* H = hid(m, const_cast<dllm_state*>(s), layer);
-  HIPCHK(launch_ps_gram(st, m->bf16, B, L, D, blk, W, s->block_start, H, m->ps_part, m->ps_R));
+  HIPCHK(launch_ps_gram(st, m->bf16, B, L, D, blk, W, s->block_start, H, m->ps_R));
   HIPCHK(launch_ps_kmeans(st, B, W, K, p->kmeans_iters, m->ps_R, ps->assign, ps->norms, m->ps_coef, m->ps_nsel));
   HIPCHK(launch_ps_centroids(st, m->bf16, B, L, D, blk, W, K, d.rms_eps, m->ps_MTt, s->block_start, H, m->ps_coef,
                              ps->norms, w.attn_norm, ps->centroids, m->ps_A));
@@ -518,8 +517,7 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   ALLOC(m->lm_rows, 16);
   if (D % 128 == 0) {
     const size_t wmax = 120;
-    ALLOC(m->ps_part, (size_t)d.max_batch * (D / 128) * wmax * wmax * 8);
-    ALLOC(m->ps_R, (size_t)d.max_batch * wmax * wmax * 8);
+    ALLOC(m->ps_R, (size_t)d.max_batch * ps_gram_splits() * wmax * wmax * 8);
     ALLOC(m->ps_coef, (size_t)d.max_batch * 16 * wmax * 8);
     ALLOC(m->ps_klp, (size_t)d.max_batch * d.n_q_heads * 16 * 8);
     ALLOC(m->ps_nsel, (size_t)d.max_batch * 4);

@@ -113,9 +113,10 @@ hipError_t launch_step_result(hipStream_t st, int B, const uint8_t* step_full, c
                               const int32_t* block_start, const double* max_entropy, int L, void* out);
 
 // ---- Polestar-Cache drift path (polestar.hip) ----
-int ps_gram_slices(int d);
+// R: Gram split partials [B][ps_gram_splits()][W][W], added by the k-means.
+int ps_gram_splits();
 hipError_t launch_ps_gram(hipStream_t st, bool bf16, int B, int L, int d, int blk, int W, const int32_t* bstart,
-                          const void* H, double* part, double* R);
+                          const void* H, double* R);
 hipError_t launch_ps_kmeans(hipStream_t st, int B, int W, int K, int iters, const double* R, int32_t* assign,
                             double* norms, double* coef, int32_t* nsel);
 hipError_t launch_ps_centroids(hipStream_t st, bool bf16, int B, int L, int d, int blk, int W, int K, float eps,

@@ -17,68 +17,105 @@ namespace dllm {
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int PS_SD = 128;    // dims per Gram slice
 constexpr int PS_WMAX = 120;  // window rows: the k-means keeps W x W fp64 in LDS
 
 __device__ __forceinline__ int ps_window_start(int bs, int L, int blk, int W) {
   return min(max(bs - blk, 0), L - W);
 }
 
-// ---------------------------------------------------------------------------
-// Gram partials: part[b][s][i][j] = sum over dims of slice s of x_i x_j, for
-// the W window rows of sequence b (raw layer inputs, fp64 products are exact).
-// Upper-triangle 16x16 tiles on v_mfma_f64_16x16x4_f64, mirrored on store.
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void ps_gram_kernel(int L, int d, int blk, int W, const int32_t* __restrict__ bstart,
-                                                      const T* __restrict__ H, double* __restrict__ part) {
-  extern __shared__ double xs[];  // [TW*16][PS_SD + 1]
-  const int b = blockIdx.y, s = blockIdx.x, nsl = gridDim.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ws = ps_window_start(bstart[b], L, blk, W);
-  const int TW = (W + 15) / 16;
-  const int XS = PS_SD + 1;
-  const int d0 = s * PS_SD;
-  for (int e = tid; e < TW * 16 * PS_SD; e += 256) {
-    const int r = e / PS_SD, t = e - r * PS_SD;
-    xs[r * XS + t] = r < W ? (double)io<T>::ld(H + ((size_t)b * L + ws + r) * d + d0 + t) : 0.0;
-  }
-  __syncthreads();
-  const int npairs = TW * (TW + 1) / 2;
-  const size_t pbase = ((size_t)b * nsl + s) * W * W;
-  for (int p = wv; p < npairs; p += 4) {
-    int ti = 0, rem = p;
-    while (rem >= TW - ti) {
-      rem -= TW - ti;
-      ++ti;
-    }
-    const int tj = ti + rem;
-    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
-    const int ra = ti * 16 + (lane & 15), rb = tj * 16 + (lane & 15), kq = lane >> 4;
-#pragma unroll 4
-    for (int k = 0; k < PS_SD; k += 4)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[ra * XS + k + kq], xs[rb * XS + k + kq], acc, 0, 0, 0);
-    // D register e of lane l: row l/16 + 4e of tile ti, column l%16 of tile tj
+// Eight consecutive elements (16-byte aligned for bf16, 32 for fp32) as
+// doubles.
+__device__ __forceinline__ void ld8d(const bf16* p, double* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = ti * 16 + (lane >> 4) + 4 * e, j = tj * 16 + (lane & 15);
-      if (i < W && j < W) {
-        part[pbase + (size_t)i * W + j] = acc[e];
-        part[pbase + (size_t)j * W + i] = acc[e];
-      }
-    }
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = (double)__uint_as_float(w[e] << 16);
+    v[2 * e + 1] = (double)__uint_as_float(w[e] & 0xffff0000u);
   }
 }
+__device__ __forceinline__ void ld8d(const float* p, double* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 c = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+}
 
-// R[b][i][j] = sum over slices in slice order.
-__global__ void ps_gram_reduce_kernel(int W, int nsl, const double* __restrict__ part, double* __restrict__ R) {
-  const int b = blockIdx.y;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= W * W) return;
-  const double* p = part + (size_t)b * nsl * W * W + e;
-  double acc = 0.0;
-  for (int s = 0; s < nsl; ++s) acc += p[(size_t)s * W * W];
-  R[(size_t)b * W * W + e] = acc;
+// ---------------------------------------------------------------------------
+// Gram partials R[b][s][i][j] = sum over the dims of split s of x_i x_j, for
+// the W window rows of sequence b (raw layer inputs; fp64 products of the
+// stored values are exact); the k-means adds the PS_GRAM_SPLITS partials in
+// split order.  One workgroup per (upper-triangle pair of 16-row tiles,
+// sequence, split); the 8 waves of all splits take interleaved 32-dim chunks
+// on v_mfma_f64_16x16x4_f64 and a workgroup adds its waves' tiles in wave
+// order.  Within a chunk, lane l feeds row l%16 and the 8 dims
+// 8*(l/16) .. 8*(l/16)+7 one per MFMA (the same order for both operands, so
+// every dim's product enters once).  The tile is stored at (i, j) and (j, i);
+// diagonal tiles store only i <= j, so R is exactly symmetric.
+// ---------------------------------------------------------------------------
+constexpr int PS_GRAM_WAVES = 8;
+constexpr int PS_GRAM_SPLITS = 4;
+
+template <typename T>
+__global__ __launch_bounds__(64 * PS_GRAM_WAVES) void ps_gram_kernel(int L, int d, int blk, int W,
+                                                                     const int32_t* __restrict__ bstart,
+                                                                     const T* __restrict__ H,
+                                                                     double* __restrict__ R) {
+  __shared__ f64x4_t red[PS_GRAM_WAVES][64];
+  const int b = blockIdx.y, sp = blockIdx.z;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int TW = (W + 15) / 16;
+  int ti = 0, rem = blockIdx.x;
+  while (rem >= TW - ti) {
+    rem -= TW - ti;
+    ++ti;
+  }
+  const int tj = ti + rem;
+  const int ws = ps_window_start(bstart[b], L, blk, W);
+  const int ra = ti * 16 + (lane & 15), rb = tj * 16 + (lane & 15);
+  const int k8 = (lane >> 4) * 8;
+  const T* pa = H + ((size_t)b * L + ws + min(ra, W - 1)) * d + k8;
+  const T* pb = H + ((size_t)b * L + ws + min(rb, W - 1)) * d + k8;
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+  // chunk stride over all waves of all splits; four chunks per pass, all
+  // loads issued before the MFMAs
+  constexpr int CS = PS_GRAM_SPLITS * PS_GRAM_WAVES * 32;
+  for (int c0 = (sp * PS_GRAM_WAVES + wv) * 32; c0 < d; c0 += 4 * CS) {
+    double xa[4][8], xb[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = min(c0 + u * CS, d - 32);
+      ld8d(pa + c, xa[u]);
+      ld8d(pb + c, xb[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool live = c0 + u * CS < d;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (ra >= W || !live) xa[u][e] = 0.0;
+        if (rb >= W || !live) xb[u][e] = 0.0;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[u][e], xb[u][e], acc, 0, 0, 0);
+    }
+  }
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
+  f64x4_t t = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < PS_GRAM_WAVES; ++w) t += red[w][lane];
+  // D register e of lane l: row l/16 + 4e of tile ti, column l%16 of tile tj
+  double* Rb = R + ((size_t)b * PS_GRAM_SPLITS + sp) * W * W;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = ti * 16 + (lane >> 4) + 4 * e, j = tj * 16 + (lane & 15);
+    if (i < W && j < W && (ti != tj || i <= j)) {
+      Rb[(size_t)i * W + j] = t[e];
+      Rb[(size_t)j * W + i] = t[e];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -105,13 +142,31 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
   int* a = reinterpret_cast<int*>(nrm + W);  // [W] (W <= 128)
   const int b = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const double* Rb = R + (size_t)b * W * W;
-  for (int i = tid; i < W; i += PS_KM_THREADS) nrm[i] = sqrt(Rb[(size_t)i * W + i]);
+  // Gram = sum of the split partials in split order, then normalised
+  const double* Rb = R + (size_t)b * PS_GRAM_SPLITS * W * W;
+  const size_t WW = (size_t)W * W;
+  for (int e0 = tid; e0 < W * W; e0 += 4 * PS_KM_THREADS) {
+    double v[4][PS_GRAM_SPLITS];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < PS_GRAM_SPLITS; ++q) v[u][q] = Rb[q * WW + min(e0 + u * PS_KM_THREADS, W * W - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * PS_KM_THREADS;
+      double t = v[u][0];
+#pragma unroll
+      for (int q = 1; q < PS_GRAM_SPLITS; ++q) t += v[u][q];
+      if (e < W * W) G[e] = t;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < W; i += PS_KM_THREADS) nrm[i] = sqrt(G[(size_t)i * W + i]);
   __syncthreads();
   for (int e = tid; e < W * W; e += PS_KM_THREADS) {
     const int i = e / W, j = e - i * W;
     const double ni = nrm[i], nj = nrm[j];
-    G[e] = (ni > 0.0 && nj > 0.0) ? Rb[e] / (ni * nj) : 0.0;
+    G[e] = (ni > 0.0 && nj > 0.0) ? G[e] / (ni * nj) : 0.0;
   }
   const int stride = W / K;
   double* cf = coef + (size_t)b * K * W;
@@ -122,7 +177,10 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
     cf[e] = (k == stride * j) ? 1.0 : 0.0;
   }
   __syncthreads();
-  auto do_assign = [&]() {
+  for (int i = tid; i < W; i += PS_KM_THREADS) a[i] = -1;
+  // returns whether any row changed cluster
+  auto do_assign = [&]() -> bool {
+    int changed = 0;
     for (int i = tid; i < W; i += PS_KM_THREADS) {
       int best = 0;
       double bv = D[i];
@@ -133,12 +191,15 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
           best = j;
         }
       }
+      changed |= a[i] != best;
       a[i] = best;
     }
-    __syncthreads();
+    return __syncthreads_or(changed) != 0;
   };
   for (int it = 0; it < iters; ++it) {
-    do_assign();
+    // an unchanged assignment rebuilds the same centroids, so every later
+    // iteration repeats this one: stop early (the result is identical)
+    if (!do_assign()) break;
     if (wv < K) {
       const int j = wv;
       // members of cluster j, rows 0..63 and 64..127
@@ -179,7 +240,7 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
     }
     __syncthreads();
   }
-  do_assign();
+  (void)do_assign();
   for (int i = tid; i < W; i += PS_KM_THREADS) {
     assign[(size_t)b * W + i] = a[i];
     norms[(size_t)b * W + i] = nrm[i];
@@ -190,53 +251,69 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
 // ---------------------------------------------------------------------------
 // Explicit centroids c_j = sum_i coef[j][i] * x_i / |x_i| (fp64, ascending i),
 // and the packed query-path input bf16(RMSNorm(c_j) * g1) (fp64 norm, rounded
-// to fp32 then to the storage dtype, as the layer's own input path).
+// to fp32 then to the storage dtype, as the layer's own input path).  One
+// workgroup per (cluster, sequence); each thread owns 8 consecutive dims and
+// reads the members' rows in batches of 4 so their loads overlap.
 // ---------------------------------------------------------------------------
+constexpr int PS_CENT_THREADS = 512;
+
 template <typename T>
-__global__ __launch_bounds__(256) void ps_centroid_kernel(int L, int d, int blk, int W, int K, float eps, int MTt,
-                                                          const int32_t* __restrict__ bstart,
-                                                          const T* __restrict__ H, const double* __restrict__ coef,
-                                                          const double* __restrict__ norms,
-                                                          const float* __restrict__ g1, double* __restrict__ cent,
-                                                          T* __restrict__ A) {
-  __shared__ double red[4];
+__global__ __launch_bounds__(PS_CENT_THREADS) void ps_centroid_kernel(
+    int L, int d, int blk, int W, int K, float eps, int MTt, const int32_t* __restrict__ bstart,
+    const T* __restrict__ H, const double* __restrict__ coef, const double* __restrict__ norms,
+    const float* __restrict__ g1, double* __restrict__ cent, T* __restrict__ A) {
+  __shared__ double red[PS_CENT_THREADS / 64];
   __shared__ int mem[128];
-  __shared__ double w[128];
-  __shared__ int nm;
-  const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x;
+  __shared__ int nm_s;
+  const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ws = ps_window_start(bstart[b], L, blk, W);
-  if (tid == 0) {
-    int c = 0;
-    for (int i = 0; i < W; ++i) {
-      const double cw = coef[((size_t)b * K + j) * W + i];
-      if (cw != 0.0) {
-        mem[c] = i;
-        w[c] = cw;
-        ++c;
-      }
-    }
-    nm = c;
+  const double* cw = coef + ((size_t)b * K + j) * W;
+  if (wv == 0) {  // members in ascending row order (W <= 128)
+    const bool f0 = lane < W && cw[lane] != 0.0;
+    const bool f1 = lane + 64 < W && cw[lane + 64] != 0.0;
+    const unsigned long long m0 = __ballot(f0), m1 = __ballot(f1);
+    const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int c0 = __popcll(m0);
+    if (f0) mem[__popcll(m0 & below)] = lane;
+    if (f1) mem[c0 + __popcll(m1 & below)] = lane + 64;
+    if (lane == 0) nm_s = c0 + __popcll(m1);
   }
   __syncthreads();
+  const int nm = nm_s;
+  const T* xw = H + ((size_t)b * L + ws) * d;
+  const double* nb = norms + (size_t)b * W;
   double* cj = cent + ((size_t)b * K + j) * d;
   double ss = 0.0;
-  for (int t = tid; t < d; t += 256) {
-    double acc = 0.0;
-    for (int q = 0; q < nm; ++q) {
-      const int i = mem[q];
-      const double x = (double)io<T>::ld(H + ((size_t)b * L + ws + i) * d + t);
-      acc += w[q] * (x / norms[(size_t)b * W + i]);
+  for (int t8 = tid * 8; t8 < d; t8 += PS_CENT_THREADS * 8) {
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int q0 = 0; q0 < nm; q0 += 4) {
+      double x[4][8], wq[4], nq[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = mem[min(q0 + u, nm - 1)];
+        ld8d(xw + (size_t)i * d + t8, x[u]);
+        wq[u] = cw[i];
+        nq[u] = nb[i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (q0 + u < nm) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += wq[u] * (x[u][e] / nq[u]);
+        }
     }
-    cj[t] = acc;
-    ss += acc * acc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      cj[t8 + e] = acc[e];
+      ss += acc[e] * acc[e];
+    }
   }
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
-  __syncthreads();
-  const double tot = red[0] + red[1] + red[2] + red[3];
+  const double tot = block_sum<PS_CENT_THREADS / 64>(ss, red);
   const double rms = sqrt(tot / (double)d + (double)eps);
   const int m = b * K + j;
-  for (int t8 = tid * 8; t8 < d; t8 += 256 * 8) {
+  for (int t8 = tid * 8; t8 < d; t8 += PS_CENT_THREADS * 8) {
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (float)(cj[t8 + e] / rms * (double)g1[t8 + e]);
@@ -334,82 +411,119 @@ __global__ __launch_bounds__(256) void ps_query_kernel(int L, int blk, int W, in
                                                        const float* __restrict__ part, const float* __restrict__ rc,
                                                        const float* __restrict__ rs, T* __restrict__ q) {
   const int m = blockIdx.x, b = m / K, j = m - b * K;
+  const int half = dh / 2;
+  const int e = blockIdx.y * 256 + threadIdx.x;  // one rotation pair per thread
+  if (e >= Hq * half) return;
   const int ws = ps_window_start(bstart[b], L, blk, W);
   const int pos = ws + (W / K) * j;
-  const int nq = Hq * dh, half = dh / 2;
+  const int nq = Hq * dh;
+  const int h = e / half, t = e - h * half;
+  const int c0 = h * dh + t, c1 = c0 + half;
   const float* p0 = part + (size_t)m * ldp;
-  for (int e = threadIdx.x; e < Hq * half; e += 256) {
-    const int h = e / half, t = e - h * half;
-    const int c0 = h * dh + t, c1 = c0 + half;
-    float a = 0.f, c = 0.f;
-    for (int s = 0; s < S; ++s) {
-      a += p0[(size_t)s * M * ldp + c0];
-      c += p0[(size_t)s * M * ldp + c1];
-    }
-    const float cs = rc[(size_t)pos * half + t], sn = rs[(size_t)pos * half + t];
-    io<T>::st(q + (size_t)m * nq + c0, a * cs - c * sn);
-    io<T>::st(q + (size_t)m * nq + c1, c * cs + a * sn);
-  }
+  const size_t sstride = (size_t)M * ldp;
+  const float a = sum_splits(p0 + c0, sstride, S);
+  const float c = sum_splits(p0 + c1, sstride, S);
+  const float cs = rc[(size_t)pos * half + t], sn = rs[(size_t)pos * half + t];
+  io<T>::st(q + (size_t)m * nq + c0, a * cs - c * sn);
+  io<T>::st(q + (size_t)m * nq + c1, c * cs + a * sn);
 }
 
 // ---------------------------------------------------------------------------
 // Proxy attention and per-head KL: for query head h, log A[j][w] =
 // log-softmax_w(q_j . k_w / sqrt(dh)) over the window keys of h's KV group
 // (fp64), KL_h[j] = sum_w A (log A - log A_prev); log A replaces log A_prev.
+// The scores are one 16-row tile of cluster queries against 16-key tiles on
+// v_mfma_f64_16x16x4_f64 (products of stored values are exact in fp64); lane
+// l feeds query/key row l%16 and the dims (dh/4)*(l/16) .. +dh/4, one per
+// MFMA, in the same order for both operands.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void ps_attn_kl_kernel(int L, int blk, int W, int K, int Hq, int Hkv, int dh,
                                                          const int32_t* __restrict__ bstart,
                                                          const T* __restrict__ q, const T* __restrict__ Kc,
                                                          double* __restrict__ logA, double* __restrict__ klp) {
-  extern __shared__ double sm[];
-  double* qs = sm;            // [K][dh]
-  double* ks = qs + K * dh;   // [W][dh + 1]
-  double* sc = ks + W * (dh + 1);  // [K][W]
+  __shared__ double sc[16 * PS_WMAX];  // [K][W]
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
-  const int B = gridDim.y;
+  const int lane = tid & 63, wv = tid >> 6;
   const int g = (h * Hkv) / Hq;
   const int ws = ps_window_start(bstart[b], L, blk, W);
-  const int nq = Hq * dh, DS = dh + 1;
-  for (int e = tid; e < K * dh; e += 256) {
-    const int j = e / dh, t = e - j * dh;
-    qs[e] = (double)io<T>::ld(q + ((size_t)b * K + j) * nq + h * dh + t);
-  }
+  const int nq = Hq * dh, kq = dh / 4;
+  const int r = lane & 15, slot = lane >> 4;
+  const T* qrow = q + ((size_t)b * K + min(r, K - 1)) * nq + h * dh + slot * kq;
   const T* kb = Kc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * dh;
-  for (int e = tid; e < W * dh; e += 256) {
-    const int w = e / dh, t = e - w * dh;
-    ks[w * DS + t] = (double)io<T>::ld(kb + kc_off(ws + w, t, dh));
-  }
-  __syncthreads();
   const double sq = sqrt((double)dh);
-  for (int e = tid; e < K * W; e += 256) {
-    const int j = e / W, w = e - j * W;
-    double acc = 0.0;
-    for (int t = 0; t < dh; ++t) acc += qs[j * dh + t] * ks[w * DS + t];
-    sc[e] = acc / sq;
+  const int TW = (W + 15) / 16;
+  // previous log-attention of this wave's rows (j = wv + 4u, keys lane and
+  // lane + 64), fetched before the scores so its latency overlaps them
+  double prev[4][2];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = min(wv + 4 * u, K - 1);
+    const double* la = logA + (((size_t)b * K + j) * Hq + h) * W;
+    prev[u][0] = la[min(lane, W - 1)];
+    prev[u][1] = la[min(lane + 64, W - 1)];
+  }
+  for (int tw = wv; tw < TW; tw += 4) {
+    const int w = tw * 16 + r;
+    const int wc = min(w, W - 1);
+    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+    // kq is 8, 16 or 32 (dh % 32 == 0, dh <= 128): up to four 8-dim chunks,
+    // all loads issued before the MFMAs
+    double xa[4][8], xb[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = min(u * 8, kq - 8);
+      ld8d(qrow + c, xa[u]);
+      ld8d(kb + kc_off(ws + wc, slot * kq + c, dh), xb[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u * 8 >= kq) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (r >= K) xa[u][e] = 0.0;
+        if (w >= W) xb[u][e] = 0.0;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[u][e], xb[u][e], acc, 0, 0, 0);
+    }
+    // D register e of lane l: query row l/16 + 4e, key tw*16 + l%16
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = slot + 4 * e, wk = tw * 16 + r;
+      if (j < K && wk < W) sc[j * W + wk] = acc[e] / sq;
+    }
   }
   __syncthreads();
   // one wave per cluster row: log-softmax, KL against the previous step
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int j = wv; j < K; j += 4) {
-    double mx = -INFINITY;
-    for (int w = lane; w < W; w += 64) mx = fmax(mx, sc[j * W + w]);
-    mx = wave_max(mx);
-    double se = 0.0;
-    for (int w = lane; w < W; w += 64) se += exp(sc[j * W + w] - mx);
+  // (W <= 120: each lane holds keys lane and lane + 64)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = wv + 4 * u;
+    if (j >= K) break;
+    const bool k1 = lane + 64 < W, k0 = lane < W;
+    const double s0 = k0 ? sc[j * W + lane] : -INFINITY;
+    const double s1 = k1 ? sc[j * W + lane + 64] : -INFINITY;
+    const double mx = wave_max(fmax(s0, s1));
+    double se = (k0 ? exp(s0 - mx) : 0.0);
+    if (k1) se += exp(s1 - mx);
     se = wave_sum(se);
     const double lse = log(se);
     double* la = logA + (((size_t)b * K + j) * Hq + h) * W;
     double kl = 0.0;
-    for (int w = lane; w < W; w += 64) {
-      const double lv = (sc[j * W + w] - mx) - lse;
-      kl += exp(lv) * (lv - la[w]);
-      la[w] = lv;
+    if (k0) {
+      const double lv = (s0 - mx) - lse;
+      kl += exp(lv) * (lv - prev[u][0]);
+      la[lane] = lv;
+    }
+    if (k1) {
+      const double lv = (s1 - mx) - lse;
+      kl += exp(lv) * (lv - prev[u][1]);
+      la[lane + 64] = lv;
     }
     kl = wave_sum(kl);
     if (lane == 0) klp[((size_t)b * Hq + h) * K + j] = kl;
   }
-  (void)B;
 }
 
 // ---------------------------------------------------------------------------
@@ -425,73 +539,67 @@ __global__ __launch_bounds__(128) void ps_select_kernel(int L, int blk, int W, i
                                                         int32_t* __restrict__ idx, int32_t* __restrict__ n_out) {
   __shared__ double kl[16];
   __shared__ int sel[16];
-  __shared__ int flag[128];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ int cnt0;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int bs = bstart[b];
   const int ws = ps_window_start(bs, L, blk, W);
   const bool valid = wstart[b] == ws;
   if (tid < K) {
+    // mean over heads, heads added in order (loads issued 8 at a time)
     double acc = 0.0;
-    for (int h = 0; h < Hq; ++h) acc += klp[((size_t)b * Hq + h) * K + tid];
+    for (int h0 = 0; h0 < Hq; h0 += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = h0 + u < Hq ? klp[((size_t)b * Hq + h0 + u) * K + tid] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (h0 + u < Hq) acc += v[u];
+    }
     kl[tid] = valid ? acc / (double)Hq : 0.0;
     kl_out[(size_t)b * K + tid] = kl[tid];
   }
   __syncthreads();
   if (tid < K) {
     // rank of cluster tid by (drift desc, index asc)
-    int r = 0;
-    for (int j = 0; j < K; ++j) r += (kl[j] > kl[tid]) || (kl[j] == kl[tid] && j < tid);
-    sel[tid] = r < top;
+    int rk = 0;
+    for (int j = 0; j < K; ++j) rk += (kl[j] > kl[tid]) || (kl[j] == kl[tid] && j < tid);
+    sel[tid] = rk < top;
   }
   __syncthreads();
-  if (tid == 0) {
-    int c = 0;
-    for (int j = 0; j < K; ++j)
-      if (sel[j]) top_out[(size_t)b * top + c++] = j;
-    wstart[b] = ws;
+  if (tid < K && sel[tid]) {
+    int pos = 0;  // selected clusters listed in index order
+    for (int j = 0; j < tid; ++j) pos += sel[j];
+    top_out[(size_t)b * top + pos] = tid;
   }
-  if (tid < W) {
-    const int row = ws + tid;
-    flag[tid] = (row >= bs && row < bs + blk) || sel[assign[(size_t)b * W + tid]];
-  }
+  if (tid == 0) wstart[b] = ws;
+  // I = current block rows + members of the selected clusters, ascending
+  const int row = ws + tid;
+  const bool f = tid < W && ((row >= bs && row < bs + blk) || sel[assign[(size_t)b * W + tid]]);
+  const unsigned long long m = __ballot(f);
+  const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  if (tid == 0) cnt0 = __popcll(m);
   __syncthreads();
-  if (tid == 0) {
-    int c = 0;
-    for (int i = 0; i < W; ++i)
-      if (flag[i]) idx[(size_t)b * L + c++] = ws + i;
-    n_out[b] = c;
-  }
+  const int off = (tid >> 6) ? cnt0 : 0;
+  if (f) idx[(size_t)b * L + off + __popcll(m & below)] = row;
+  if (tid == 64) n_out[b] = cnt0 + __popcll(m);
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-int ps_gram_slices(int d) { return d / PS_SD; }
+int ps_gram_splits() { return PS_GRAM_SPLITS; }
 
 hipError_t launch_ps_gram(hipStream_t st, bool bf16m, int B, int L, int d, int blk, int W, const int32_t* bstart,
-                          const void* H, double* part, double* R) {
-  if (d % PS_SD || W > PS_WMAX || W < 1) return hipErrorInvalidValue;
-  const int nsl = d / PS_SD;
-  const size_t lds = (size_t)((W + 15) / 16) * 16 * (PS_SD + 1) * sizeof(double);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)ps_gram_kernel<bf16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(128 * (PS_SD + 1) * sizeof(double)));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)ps_gram_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(128 * (PS_SD + 1) * sizeof(double)));  // up to 8 tiles of 16 rows
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+                          const void* H, double* R) {
+  if (d % 32 || W > PS_WMAX || W < 1) return hipErrorInvalidValue;
+  const int TW = (W + 15) / 16;
+  const dim3 grid(TW * (TW + 1) / 2, B, PS_GRAM_SPLITS);
   if (bf16m)
-    hipLaunchKernelGGL(ps_gram_kernel<bf16>, dim3(nsl, B), dim3(256), lds, st, L, d, blk, W, bstart,
-                       (const bf16*)H, part);
+    hipLaunchKernelGGL(ps_gram_kernel<bf16>, grid, dim3(64 * PS_GRAM_WAVES), 0, st, L, d, blk, W, bstart,
+                       (const bf16*)H, R);
   else
-    hipLaunchKernelGGL(ps_gram_kernel<float>, dim3(nsl, B), dim3(256), lds, st, L, d, blk, W, bstart,
-                       (const float*)H, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ps_gram_reduce_kernel, dim3((W * W + 255) / 256, B), dim3(256), 0, st, W, nsl, part, R);
+    hipLaunchKernelGGL(ps_gram_kernel<float>, grid, dim3(64 * PS_GRAM_WAVES), 0, st, L, d, blk, W, bstart,
+                       (const float*)H, R);
   return hipGetLastError();
 }
 
@@ -516,10 +624,10 @@ hipError_t launch_ps_centroids(hipStream_t st, bool bf16m, int B, int L, int d, 
                                int MTt, const int32_t* bstart, const void* H, const double* coef,
                                const double* norms, const float* g1, double* cent, void* A) {
   if (bf16m)
-    hipLaunchKernelGGL(ps_centroid_kernel<bf16>, dim3(K, B), dim3(256), 0, st, L, d, blk, W, K, eps, MTt, bstart,
+    hipLaunchKernelGGL(ps_centroid_kernel<bf16>, dim3(K, B), dim3(PS_CENT_THREADS), 0, st, L, d, blk, W, K, eps, MTt, bstart,
                        (const bf16*)H, coef, norms, g1, cent, (bf16*)A);
   else
-    hipLaunchKernelGGL(ps_centroid_kernel<float>, dim3(K, B), dim3(256), 0, st, L, d, blk, W, K, eps, MTt, bstart,
+    hipLaunchKernelGGL(ps_centroid_kernel<float>, dim3(K, B), dim3(PS_CENT_THREADS), 0, st, L, d, blk, W, K, eps, MTt, bstart,
                        (const float*)H, coef, norms, g1, cent, (float*)A);
   return hipGetLastError();
 }
@@ -540,34 +648,24 @@ hipError_t launch_ps_queries(hipStream_t st, bool bf16m, int B, int L, int blk, 
                              int ldp, const int32_t* bstart, const float* part, const float* rc, const float* rs,
                              void* q) {
   const int M = B * K;
+  const dim3 grid(M, (Hq * (dh / 2) + 255) / 256);
   if (bf16m)
-    hipLaunchKernelGGL(ps_query_kernel<bf16>, dim3(M), dim3(256), 0, st, L, blk, W, K, Hq, dh, S, M, ldp, bstart, part,
+    hipLaunchKernelGGL(ps_query_kernel<bf16>, grid, dim3(256), 0, st, L, blk, W, K, Hq, dh, S, M, ldp, bstart, part,
                        rc, rs, (bf16*)q);
   else
-    hipLaunchKernelGGL(ps_query_kernel<float>, dim3(M), dim3(256), 0, st, L, blk, W, K, Hq, dh, S, M, ldp, bstart,
+    hipLaunchKernelGGL(ps_query_kernel<float>, grid, dim3(256), 0, st, L, blk, W, K, Hq, dh, S, M, ldp, bstart,
                        part, rc, rs, (float*)q);
   return hipGetLastError();
 }
 
 hipError_t launch_ps_attn_kl(hipStream_t st, bool bf16m, int B, int L, int blk, int W, int K, int Hq, int Hkv,
                              int dh, const int32_t* bstart, const void* q, const void* Kc, double* logA, double* klp) {
-  const size_t lds = ((size_t)K * dh + (size_t)W * (dh + 1) + (size_t)K * W) * sizeof(double);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)ps_attn_kl_kernel<bf16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)ps_attn_kl_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  if (W > PS_WMAX || W < 1 || K > 16 || K < 1 || dh % 32 || dh > 128) return hipErrorInvalidValue;
   if (bf16m)
-    hipLaunchKernelGGL(ps_attn_kl_kernel<bf16>, dim3(Hq, B), dim3(256), lds, st, L, blk, W, K, Hq, Hkv, dh, bstart,
+    hipLaunchKernelGGL(ps_attn_kl_kernel<bf16>, dim3(Hq, B), dim3(256), 0, st, L, blk, W, K, Hq, Hkv, dh, bstart,
                        (const bf16*)q, (const bf16*)Kc, logA, klp);
   else
-    hipLaunchKernelGGL(ps_attn_kl_kernel<float>, dim3(Hq, B), dim3(256), lds, st, L, blk, W, K, Hq, Hkv, dh, bstart,
+    hipLaunchKernelGGL(ps_attn_kl_kernel<float>, dim3(Hq, B), dim3(256), 0, st, L, blk, W, K, Hq, Hkv, dh, bstart,
                        (const float*)q, (const float*)Kc, logA, klp);
   return hipGetLastError();
 }
