@@ -129,7 +129,41 @@ WORKLOADS = {
 }
 
 
-def bench_config(name, steps, warmup):
+def class_table(prof, steps, achievable, ms_per_step):
+    """Per-phase figures from the library's per-class HIP events: ms per step,
+    launches, achieved algorithmic GB/s and TFLOP/s, and the fraction of the
+    HBM peak and of the measured streaming-read rate."""
+    out = {}
+    busy = 0.0
+    for k, v in prof.items():
+        if v["launches"] == 0:
+            continue
+        busy += v["ms"]
+        gbs = v["bytes"] / (v["ms"] * 1e-3) / 1e9 if v["ms"] > 0 else None
+        out[k] = {"ms_per_step": round(v["ms"] / steps, 4),
+                  "launches_per_step": round(v["launches"] / steps, 2),
+                  "GB_per_s": round(gbs, 1) if gbs is not None else None,
+                  "TFLOP_per_s": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] > 0 else None,
+                  "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4) if gbs is not None else None,
+                  "achievable_frac": round(gbs / achievable, 4) if gbs is not None and achievable else None}
+    # launch gaps, host work and any launch outside the classes
+    out["unprofiled"] = {"ms_per_step": round(ms_per_step - busy / steps, 4)}
+    return out
+
+
+def achievable_read_gbs():
+    """Best streaming-read rate of this device (dllm_stream_probe over 1 GiB)."""
+    import torch
+    from sparse_kv_cache_value_amd import binding as B
+    buf = torch.full((1 << 30,), 7, dtype=torch.uint8, device="cuda")
+    scratch = torch.zeros(1 << 13, dtype=torch.uint8, device="cuda")
+    gbs = B.dllm_stream_probe(buf, scratch, reps=3)
+    del buf, scratch
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def bench_config(name, steps, warmup, achievable=None):
     """Sparse steps of one of the other configs (the per-config figures of the
     scope table's measurement row): tokens/s, TPF, per-layer us, the kernel
     classes, and the GEMM class against its roofline (HBM, or the bf16 MFMA
@@ -147,24 +181,27 @@ def bench_config(name, steps, warmup):
     for _ in range(warmup):
         runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps)
     torch.cuda.synchronize()
-    nh = int(st.n_history.sum())
-    B.dllm_profile(model.h, True)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prof = B.dllm_profile_read(model.h)
-    B.dllm_profile(model.h, False)
-    tokens = int(st.n_history.sum()) - nh
+    def run(classes):
+        nh = int(st.n_history.sum())
+        B.dllm_profile(model.h, True, classes)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        prof = B.dllm_profile_read(model.h)
+        B.dllm_profile(model.h, False)
+        return wall, int(st.n_history.sum()) - nh, prof
+
+    # timed steps with events on the GEMM classes only, then the same number
+    # of steps with every class for the per-phase table
+    wall, tokens, prof = run(["gemm", "lm_head"])
+    wall_all, _, prof_all = run(None)
     model.close()
     del st, ps, model
     torch.cuda.empty_cache()
     ms = 1e3 * wall / steps
-    classes = {k: {"ms_per_step": round(v["ms"] / steps, 4),
-                   "GB_per_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] > 0 else None,
-                   "TFLOP_per_s": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] > 0 else None}
-               for k, v in prof.items() if v["launches"] > 0}
+    classes = class_table(prof_all, steps, achievable, 1e3 * wall_all / steps)
     g = prof["gemm"]
     gb = g["bytes"] / (g["ms"] * 1e-3) / 1e9 if g["ms"] > 0 else 0.0
     tf = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] > 0 else 0.0
@@ -175,7 +212,8 @@ def bench_config(name, steps, warmup):
                 "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gb / HBM_PEAK_GBS, 4)}
+                "frac": round(gb / HBM_PEAK_GBS, 4),
+                "frac_of_achievable": round(gb / achievable, 4) if achievable else None}
     roof["kernel"] = "layer GEMMs (gemm class)"
     lm_ms = prof["lm_head"]["ms"] / steps
     return {
@@ -216,10 +254,11 @@ def main():
 
     cfg = configs.C3
     masked = cfg.seq_len - cfg.prompt_len
-    if args.warmup + 2 * args.steps + args.full_steps + 1 > masked:
+    if args.warmup + 3 * args.steps + args.full_steps + 1 > masked:
         print("too many steps for 512 masked tokens", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    achievable = achievable_read_gbs()
     t_init = time.perf_counter()
     model = runtime.Model(cfg, "cuda")
     st = runtime.State(cfg)
@@ -244,9 +283,9 @@ def main():
     # Run B (headline): sparse refresh every step, gate disabled (tau = inf).
     # The library's per-class HIP events bracket every kernel launch on the
     # step's stream during the timed region.
-    def run_sparse(n, profile):
+    def run_sparse(n, profile, classes=None):
         nh = int(st.n_history.sum())
-        B.dllm_profile(model.h, profile)
+        B.dllm_profile(model.h, profile, classes)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -260,9 +299,12 @@ def main():
         B.dllm_profile(model.h, False)
         return wall, ev0.elapsed_time(ev1), int(st.n_history.sum()) - nh, prof
 
-    wall, gpu_ms, tokens, prof = run_sparse(args.steps, True)
+    # timed steps: events on the dominant class (layer GEMMs + LM head) only
+    wall, gpu_ms, tokens, prof = run_sparse(args.steps, True, ["gemm", "lm_head"])
     ms_per_step = 1e3 * wall / args.steps
-    # the same steps without the per-kernel events, for their overhead
+    # per-phase table: the same number of steps with events on every class
+    wall_all, _, _, prof_all = run_sparse(args.steps, True)
+    # and without any events, for their overhead
     wall_np, _, tokens_np, _ = run_sparse(args.steps, False)
 
     # Run A: gate as specified (tau = 2 nats, AUTO mode reads the flag each step)
@@ -281,11 +323,7 @@ def main():
     dom_launches = g["launches"] + lm["launches"]
     dom_bytes = g["bytes"] + lm["bytes"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else 0.0
-    per_step = {k: {"ms_per_step": round(v["ms"] / args.steps, 4),
-                    "launches_per_step": v["launches"] / args.steps,
-                    "GB_per_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] > 0 else None,
-                    "TFLOP_per_s": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] > 0 else None}
-                for k, v in prof.items()}
+    per_step = class_table(prof_all, args.steps, achievable, 1e3 * wall_all / args.steps)
     step_bytes = (g["bytes"] + lm["bytes"]) / args.steps
     out = {
         "metric": METRIC,
@@ -315,17 +353,19 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_of_achievable": round(achieved / achievable, 4),
             "traffic": gemm_traffic(),
             "launches": dom_launches,
             "avg_launch_us": round(1e3 * dom_ms / max(dom_launches, 1), 3),
             "algorithmic_bytes_per_launch": round(dom_bytes / max(dom_launches, 1), 1),
         },
+        "achievable_read_GB_per_s": round(achievable, 1),
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
         "ms_per_step_without_kernel_events": round(1e3 * wall_np / args.steps, 4),
         "tokens_per_s_without_kernel_events": round(tokens_np / wall_np, 3),
         "tokens_timed": tokens,
         "tpf": round(tokens / args.steps, 3),
-        "per_layer_sparse_us": round(1e3 * (ms_per_step - per_step["lm_head"]["ms_per_step"]) / cfg.n_layers, 2),
+        "per_layer_sparse_us": round(1e3 * (ms_per_step - lm["ms"] / args.steps) / cfg.n_layers, 2),
         "kernel_classes": per_step,
         "step_weight_bytes_GB": round(step_bytes / 1e9, 3),
         "run_full_gate": {"tau": cfg.tau, "ms_per_step": round(full_ms, 3),
@@ -340,7 +380,7 @@ def main():
         # the other configs of the scope table, a few sparse steps each
         out["other_configs"] = {}
         for name, n, w in (("C1", 20, 3), ("C2", 20, 3), ("C4", 8, 2), ("C5", 8, 2)):
-            out["other_configs"][name] = bench_config(name, n, w)
+            out["other_configs"][name] = bench_config(name, n, w, achievable)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

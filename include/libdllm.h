@@ -288,19 +288,40 @@ dllm_status dllm_step(dllm_model *m, dllm_state *s, const dllm_step_params *p,
  * (weights + activations read, outputs written; split-K partials are not
  * counted).  dllm_profile_read waits for the recorded events, writes
  * DLLM_PROF_N entries to stats_h and clears them. */
-enum { DLLM_PROF_GEMM = 0,    /* layer GEMMs (QKV, O, gate|up, down) */
-       DLLM_PROF_LMHEAD = 1,  /* LM-head GEMM */
-       DLLM_PROF_ATTN = 2,    /* attention */
-       DLLM_PROF_PROXY = 3,   /* value proxy + drift */
-       DLLM_PROF_N = 4 };
+enum { DLLM_PROF_GEMM = 0,      /* layer GEMMs (QKV, O, gate|up, down; Polestar centroid queries) */
+       DLLM_PROF_LMHEAD = 1,    /* LM-head GEMM */
+       DLLM_PROF_ATTN = 2,      /* attention */
+       DLLM_PROF_PROXY = 3,     /* value proxy + drift */
+       DLLM_PROF_SELECT = 4,    /* index-set selection (top-k, or Polestar cluster selection) */
+       DLLM_PROF_ROWS = 5,      /* row kernels: gather + RMSNorm, QKV / O / down epilogues, SwiGLU
+                                   (these count the split-K partials they read) */
+       DLLM_PROF_POLESTAR = 6,  /* Polestar drift path except its query GEMM */
+       DLLM_PROF_DECIDE = 7,    /* prep, embedding, LM-head gather and statistics, commit */
+       DLLM_PROF_N = 8 };
 typedef struct {
   int64_t launches;
   double ms;      /* sum of event-pair durations */
   double bytes;   /* sum of algorithmic bytes */
   double flops;   /* sum of algorithmic flops */
 } dllm_kernel_stats;
-dllm_status dllm_profile(dllm_model *m, int32_t enable);
+#define DLLM_PROF_ALL ((1 << DLLM_PROF_N) - 1)
+/* class_mask: bit c (1 << DLLM_PROF_c) records class c; 0 stops recording.
+ * Every recorded launch adds two stream markers, so time the step with only
+ * the classes needed. */
+dllm_status dllm_profile(dllm_model *m, int32_t class_mask);
 dllm_status dllm_profile_read(dllm_model *m, dllm_kernel_stats *stats_h);
+
+/* Diagnostics: achievable streaming-read bandwidth, the measured ceiling the
+ * kernels' algorithmic GB/s is also compared with (besides the published HBM
+ * peak).  Streams dev_buf (device memory, bytes >= 256 MiB; only the leading
+ * multiple of 64 MiB is read) with 16-byte nontemporal loads under four launch
+ * shapes (1024 or 2048 workgroups of 256 threads, 4 or 8 loads in flight per
+ * thread), each once untimed and then `reps` times between HIP events on
+ * `stream`, and stores the best shape's mean rate in *gbps_h (1e9 bytes/s).
+ * dev_scratch: device memory of at least 8 KiB (checksum words).  Waits for
+ * the stream.  Errors: DLLM_E_ARG (NULL pointer, reps < 1, bytes < 256 MiB). */
+dllm_status dllm_stream_probe(const void *dev_buf, size_t bytes, void *dev_scratch, int32_t reps, double *gbps_h,
+                              void *stream);
 
 #ifdef __cplusplus
 }

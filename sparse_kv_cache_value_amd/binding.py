@@ -62,8 +62,9 @@ class DllmStepResult(ctypes.Structure):
     _fields_ = [("n_full", _i32), ("n_committed", _i32), ("n_active", _i32), ("max_entropy", _f64)]
 
 
-DLLM_PROF_GEMM, DLLM_PROF_LMHEAD, DLLM_PROF_ATTN, DLLM_PROF_PROXY, DLLM_PROF_N = 0, 1, 2, 3, 4
-PROF_NAMES = ("gemm", "lm_head", "attention", "proxy")
+(DLLM_PROF_GEMM, DLLM_PROF_LMHEAD, DLLM_PROF_ATTN, DLLM_PROF_PROXY, DLLM_PROF_SELECT, DLLM_PROF_ROWS,
+ DLLM_PROF_POLESTAR, DLLM_PROF_DECIDE, DLLM_PROF_N) = range(9)
+PROF_NAMES = ("gemm", "lm_head", "attention", "proxy", "select", "rows", "polestar", "decide")
 
 
 class DllmKernelStats(ctypes.Structure):
@@ -92,6 +93,7 @@ SIGNATURES = {
                          ctypes.POINTER(DllmStepResult), _vp]),
     "dllm_profile": (_i32, [_vp, _i32]),
     "dllm_profile_read": (_i32, [_vp, ctypes.POINTER(DllmKernelStats)]),
+    "dllm_stream_probe": (_i32, [_vp, ctypes.c_size_t, _vp, _i32, ctypes.POINTER(_f64), _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -219,8 +221,27 @@ def dllm_step(m: int, state, mode: int, forced_rule: int, recent_k: int, tau: fl
     return res
 
 
-def dllm_profile(m: int, enable: bool):
-    _check(lib().dllm_profile(m, 1 if enable else 0))
+def dllm_profile(m: int, enable: bool, classes=None):
+    """Per-class event timing on (`classes`: names from PROF_NAMES, default
+    all) or off."""
+    if not enable:
+        mask = 0
+    elif classes is None:
+        mask = (1 << DLLM_PROF_N) - 1
+    else:
+        mask = 0
+        for c in classes:
+            mask |= 1 << PROF_NAMES.index(c)
+    _check(lib().dllm_profile(m, mask))
+
+
+def dllm_stream_probe(buf, scratch, reps: int = 3, stream=None) -> float:
+    """Achievable streaming-read GB/s over the device tensor `buf`
+    (>= 256 MiB); `scratch` is a device tensor of >= 8 KiB."""
+    out = _f64(0.0)
+    _check(lib().dllm_stream_probe(_p(buf), buf.numel() * buf.element_size(), _p(scratch), int(reps),
+                                   ctypes.byref(out), _stream(stream)))
+    return out.value
 
 
 def dllm_profile_read(m: int) -> dict:

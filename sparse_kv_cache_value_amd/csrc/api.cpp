@@ -114,6 +114,7 @@ struct dllm_model {
     double bytes, flops;
   };
   bool prof_on = false;
+  int32_t prof_mask = 0;  // bit c: class c records events
   std::vector<ProfRec> prof_pending;
   std::vector<hipEvent_t> ev_pool;
   std::vector<hipEvent_t> ev_all;
@@ -163,7 +164,7 @@ struct Prof {
   }
   Prof(dllm_model* m_, hipStream_t st_, int cls_, double bytes_, double flops_)
       : m(m_), st(st_), cls(cls_), bytes(bytes_), flops(flops_) {
-    if (m->prof_on) {
+    if (m->prof_on && ((m->prof_mask >> cls) & 1)) {
       a = get(m);
       if (a) (void)hipEventRecord(a, st);
     }
@@ -295,10 +296,19 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
   const LayerW& w = m->layers[layer];
   const void* Hin = hid(m, s, layer);
   int sp = 1;
-  HIPCHK(launch_gather_norm(st, m->bf16, max_rows, B, L, D, d.rms_eps, m->MTt, idx, n, Hin, w.attn_norm, m->A1));
+  const double Mr = max_rows, es = m->esize, nqkv = nq + 2 * nv;
+  {
+    Prof prof(m, st, DLLM_PROF_ROWS, 2.0 * Mr * D * es + D * 4.0, 4.0 * Mr * D);
+    HIPCHK(launch_gather_norm(st, m->bf16, max_rows, B, L, D, d.rms_eps, m->MTt, idx, n, Hin, w.attn_norm, m->A1));
+    prof.done();
+  }
   CHK(gemm(m, st, max_rows, B, D, nq + 2 * nv, m->A1, w.w_qkv, n, m->part, m->part_floats, &sp));
-  HIPCHK(launch_qkv_epilogue(st, m->bf16, max_rows, B, L, d.n_q_heads, d.n_kv_heads, d.head_dim, sp, idx, n,
-                             m->part, m->rope_cos, m->rope_sin, m->q, kcache(m, s, layer), vcache(m, s, layer)));
+  {
+    Prof prof(m, st, DLLM_PROF_ROWS, sp * Mr * nqkv * 4.0 + Mr * nqkv * es, Mr * nqkv * (sp + 3.0));
+    HIPCHK(launch_qkv_epilogue(st, m->bf16, max_rows, B, L, d.n_q_heads, d.n_kv_heads, d.head_dim, sp, idx, n,
+                               m->part, m->rope_cos, m->rope_sin, m->q, kcache(m, s, layer), vcache(m, s, layer)));
+    prof.done();
+  }
   {
     Prof prof(m, st, DLLM_PROF_ATTN,
               2.0 * B * L * nv * m->esize + 2.0 * max_rows * nq * m->esize,
@@ -308,27 +318,42 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
     prof.done();
   }
   CHK(gemm(m, st, max_rows, B, nq, D, m->attn_o, w.w_o, n, m->part, m->part_floats, &sp));
-  HIPCHK(launch_o_epilogue(st, m->bf16, max_rows, B, L, D, sp, d.rms_eps, m->MTt, idx, n, m->part, Hin,
-                           w.ffn_norm, m->hprime, m->A2));
+  {
+    Prof prof(m, st, DLLM_PROF_ROWS, sp * Mr * D * 4.0 + Mr * D * (2.0 * es + 4.0), Mr * D * (sp + 5.0));
+    HIPCHK(launch_o_epilogue(st, m->bf16, max_rows, B, L, D, sp, d.rms_eps, m->MTt, idx, n, m->part, Hin,
+                             w.ffn_norm, m->hprime, m->A2));
+    prof.done();
+  }
   if (m->bf16) {
     // SwiGLU fused into the gate|up GEMM
     CHK(gemm(m, st, max_rows, B, D, 2 * F, m->A2, w.w_gu, n, m->part, m->part_floats, &sp, DLLM_PROF_GEMM, m->MTt,
              m->act));
   } else {
     CHK(gemm(m, st, max_rows, B, D, 2 * F, m->A2, w.w_gu, n, m->part, m->part_floats, &sp));
+    Prof prof(m, st, DLLM_PROF_ROWS, sp * Mr * 2.0 * F * 4.0 + Mr * F * es, Mr * F * (2.0 * sp + 4.0));
     HIPCHK(launch_swiglu(st, m->bf16, max_rows, B, F, sp, n, m->part, m->act));
+    prof.done();
   }
   CHK(gemm(m, st, max_rows, B, F, D, m->act, w.w_down, n, m->part, m->part_floats, &sp));
-  HIPCHK(launch_down_epilogue(st, m->bf16, max_rows, B, L, D, d.proxy_rank, sp, idx, n, m->part, m->hprime,
-                              hid(m, s, layer + 1), pcur(m, s, layer), pref(m, s, layer), score(m, s, layer)));
+  {
+    Prof prof(m, st, DLLM_PROF_ROWS,
+              sp * Mr * D * 4.0 + Mr * D * (4.0 + es) + Mr * d.proxy_rank * 16.0 + Mr * 8.0, Mr * D * sp);
+    HIPCHK(launch_down_epilogue(st, m->bf16, max_rows, B, L, D, d.proxy_rank, sp, idx, n, m->part, m->hprime,
+                                hid(m, s, layer + 1), pcur(m, s, layer), pref(m, s, layer), score(m, s, layer)));
+    prof.done();
+  }
   return DLLM_OK;
 }
 
 dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st) {
   const dllm_dims& d = m->d;
   const int B = s->batch, blk = d.block_len;
-  HIPCHK(launch_lm_gather(st, m->bf16, B, d.seq_len, blk, d.d_model, d.rms_eps, m->lm_MTt, s->block_start,
-                          hid(m, s, d.n_layers), m->final_norm, m->A_lm, m->lm_rows));
+  {
+    Prof prof(m, st, DLLM_PROF_DECIDE, 2.0 * B * blk * d.d_model * m->esize, 4.0 * B * blk * d.d_model);
+    HIPCHK(launch_lm_gather(st, m->bf16, B, d.seq_len, blk, d.d_model, d.rms_eps, m->lm_MTt, s->block_start,
+                            hid(m, s, d.n_layers), m->final_norm, m->A_lm, m->lm_rows));
+    prof.done();
+  }
   int sp = 1;
   const size_t cap = (size_t)d.max_batch * blk * d.vocab;
   if (m->bf16) {
@@ -342,15 +367,19 @@ dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st) {
     CHK(gemm(m, st, B * blk, 1, d.d_model, d.vocab, m->A_lm, m->lm_head, m->lm_rows, m->logits, cap, &sp,
              DLLM_PROF_LMHEAD));
   }
+  Prof prof(m, st, DLLM_PROF_DECIDE, 4.0 * B * blk * d.vocab, 4.0 * B * blk * d.vocab);
   HIPCHK(launch_lm_stats(st, B * blk, d.vocab, m->logits, m->lm_part, m->lm_stats, m->lm_slabs));
+  prof.done();
   return DLLM_OK;
 }
 
 dllm_status do_commit(dllm_model* m, dllm_state* s, double thr, double tau, hipStream_t st) {
   CHK(do_lm_head(m, s, st));
   const dllm_dims& d = m->d;
+  Prof prof(m, st, DLLM_PROF_DECIDE, (double)s->batch * d.block_len * (32.0 + 4.0 + 1.0), 0.0);
   HIPCHK(launch_commit(st, s->batch, d.seq_len, d.block_len, thr, tau, m->lm_stats, s->tokens, s->committed,
                        s->history, s->n_history, s->n_new, s->block_start, s->full_next, s->max_entropy));
+  prof.done();
   return DLLM_OK;
 }
 
@@ -395,12 +424,19 @@ dllm_status do_polestar_drift(dllm_model* m, int layer, const dllm_state* s, dll
   const int W = p->window_blocks * blk, K = p->n_clusters, Hq = d.n_q_heads, dh = d.head_dim;
   const LayerW& w = m->layers[layer];
   void* H = hid(m, const_cast<dllm_state*>(s), layer);
+  const double es = m->esize, Bw = (double)B * W;
+  // window rows read by the Gram, the centroids and the codes; centroids
+  // (fp64 and packed) and codes written
+  Prof prof(m, st, DLLM_PROF_POLESTAR,
+            3.0 * Bw * D * es + (double)B * K * D * (8.0 + es) + (double)B * K * D * 8.0 + Bw * (D / 2.0 + D / 16.0),
+            2.0 * Bw * W * D + 2.0 * Bw * D);
   HIPCHK(launch_ps_gram(st, m->bf16, B, L, D, blk, W, s->block_start, H, m->ps_R));
   HIPCHK(launch_ps_kmeans(st, B, W, K, p->kmeans_iters, m->ps_R, ps->assign, ps->norms, m->ps_coef, m->ps_nsel));
   HIPCHK(launch_ps_centroids(st, m->bf16, B, L, D, blk, W, K, d.rms_eps, m->ps_MTt, s->block_start, H, m->ps_coef,
                              ps->norms, w.attn_norm, ps->centroids, m->ps_A));
   HIPCHK(launch_ps_codes(st, m->bf16, B, L, D, blk, W, K, s->block_start, H, ps->norms, ps->assign, ps->centroids,
                          ps->codes, ps->scales));
+  prof.done();
   // centroid queries through the layer's query projection (the first
   // n_q_heads*head_dim columns of the packed QKV weight; fp32 models use the
   // whole row-major QKV weight and read the query columns)
@@ -408,11 +444,18 @@ dllm_status do_polestar_drift(dllm_model* m, int layer, const dllm_state* s, dll
   int sp = 1;
   CHK(gemm(m, st, B * K, B, D, N, m->ps_A, w.w_qkv, m->ps_nsel, m->part, m->part_floats, &sp, DLLM_PROF_GEMM,
            m->ps_MTt));
+  // query partials read, queries written, window keys per head, log-attention
+  // read and written
+  Prof prof2(m, st, DLLM_PROF_POLESTAR,
+             (double)sp * B * K * Hq * dh * 4.0 + (double)B * K * Hq * dh * es + Bw * Hq * dh * es +
+                 (double)B * K * Hq * W * 16.0,
+             2.0 * B * K * (double)Hq * W * dh);
   HIPCHK(launch_ps_queries(st, m->bf16, B, L, blk, W, K, Hq, dh, sp, N, s->block_start, m->part, m->rope_cos,
                            m->rope_sin, ps->queries));
   double* la = ps->log_attn + (size_t)layer * B * K * Hq * W;
   HIPCHK(launch_ps_attn_kl(st, m->bf16, B, L, blk, W, K, Hq, d.n_kv_heads, dh, s->block_start, ps->queries,
                            kcache(m, const_cast<dllm_state*>(s), layer), la, m->ps_klp));
+  prof2.done();
   return DLLM_OK;
 }
 
@@ -420,9 +463,11 @@ dllm_status do_polestar_select(dllm_model* m, int layer, const dllm_state* s, dl
                                const dllm_polestar_params* p, int32_t* idx, int32_t* n, hipStream_t st) {
   const dllm_dims& d = m->d;
   const int B = s->batch, W = p->window_blocks * d.block_len;
+  Prof prof(m, st, DLLM_PROF_SELECT, (double)B * d.n_q_heads * p->n_clusters * 8.0 + (double)B * W * 8.0, 0.0);
   HIPCHK(launch_ps_select(st, B, d.seq_len, d.block_len, W, p->n_clusters, d.n_q_heads, p->top_clusters,
                           s->block_start, ps->assign, m->ps_klp, ps->win_start + (size_t)layer * B, ps->kl, ps->top,
                           idx, n));
+  prof.done();
   return DLLM_OK;
 }
 
@@ -756,13 +801,17 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
   }
   const int fmax = p->forced_rule == DLLM_FORCED_NONE ? 0
                    : (p->forced_rule == DLLM_FORCED_BLOCK ? d.block_len : d.block_len + p->recent_k);
-  HIPCHK(launch_prep(st, B, L, d.block_len, p->forced_rule, p->recent_k, p->mode, s->history, s->n_history, s->n_new,
-                     s->block_start, s->full_next, m->forced, m->step_full, m->idx0, m->n0));
   int prev_max = any_full ? B * L : B * std::min(L, d.block_len);
+  {
+    Prof prof(m, st, DLLM_PROF_DECIDE, (double)B * L * 6.0 + 2.0 * prev_max * d.d_model * m->esize, 0.0);
+    HIPCHK(launch_prep(st, B, L, d.block_len, p->forced_rule, p->recent_k, p->mode, s->history, s->n_history,
+                       s->n_new, s->block_start, s->full_next, m->forced, m->step_full, m->idx0, m->n0));
+    HIPCHK(launch_embed(st, m->bf16, prev_max, B, L, d.d_model, d.vocab, m->idx0, m->n0, s->tokens, m->embed,
+                        hid(m, s, 0)));
+    prof.done();
+  }
   const int32_t* prev_idx = m->idx0;
   const int32_t* prev_n = m->n0;
-  HIPCHK(launch_embed(st, m->bf16, prev_max, B, L, d.d_model, d.vocab, prev_idx, prev_n, s->tokens, m->embed,
-                      hid(m, s, 0)));
   if (polestar && !any_full) {
     // Polestar-Cache: the cluster drift path picks the rows of every layer
     const int W = p->polestar->window_blocks * d.block_len;
@@ -782,7 +831,11 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     const int k = kf > (double)L ? L : (int)kf;
     int32_t* idx = m->idx[l & 1];
     int32_t* n = m->nsel[l & 1];
-    HIPCHK(launch_select(st, B, L, k, score(m, s, l), m->forced, m->step_full, idx, n));
+    {
+      Prof prof(m, st, DLLM_PROF_SELECT, (double)B * L * 13.0, 0.0);
+      HIPCHK(launch_select(st, B, L, k, score(m, s, l), m->forced, m->step_full, idx, n));
+      prof.done();
+    }
     const int rows = any_full ? B * L : B * std::min(L, std::max(k, fmax));
     CHK(do_sparse(m, l, s, idx, n, rows, st));
     prev_idx = idx;
@@ -793,9 +846,45 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
   return finish_step(m, s, res_h, st);
 }
 
-dllm_status dllm_profile(dllm_model* m, int32_t enable) {
+dllm_status dllm_stream_probe(const void* dev_buf, size_t bytes, void* dev_scratch, int32_t reps, double* gbps_h,
+                              void* stream) {
+  if (!dev_buf || !dev_scratch || !gbps_h) return fail(DLLM_E_ARG, "stream probe: NULL pointer");
+  if (reps < 1) return fail(DLLM_E_ARG, "stream probe: reps < 1");
+  if (bytes < ((size_t)256 << 20)) return fail(DLLM_E_ARG, "stream probe: need at least 256 MiB");
+  const size_t use = bytes / ((size_t)64 << 20) * ((size_t)64 << 20);
+  hipStream_t st = S(stream);
+  hipEvent_t a = nullptr, b = nullptr;
+  HIPCHK(hipEventCreate(&a));
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return fail(DLLM_E_HIP, "hipEventCreate failed");
+  }
+  double best = 0.0;
+  hipError_t e = hipSuccess;
+  const int grids[2] = {1024, 2048}, depths[2] = {4, 8};
+  for (int gi = 0; gi < 2 && e == hipSuccess; ++gi)
+    for (int di = 0; di < 2 && e == hipSuccess; ++di) {
+      e = launch_stream_probe(st, grids[gi], depths[di], dev_buf, use, (unsigned*)dev_scratch);
+      if (e == hipSuccess) e = hipEventRecord(a, st);
+      for (int r = 0; r < reps && e == hipSuccess; ++r)
+        e = launch_stream_probe(st, grids[gi], depths[di], dev_buf, use, (unsigned*)dev_scratch);
+      if (e == hipSuccess) e = hipEventRecord(b, st);
+      if (e == hipSuccess) e = hipEventSynchronize(b);
+      float ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+      if (e == hipSuccess && ms > 0.f) best = std::max(best, (double)use * reps / (ms * 1e-3) / 1e9);
+    }
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  if (e != hipSuccess) return fail(DLLM_E_HIP, "stream probe: %s", hipGetErrorString(e));
+  *gbps_h = best;
+  return DLLM_OK;
+}
+
+dllm_status dllm_profile(dllm_model* m, int32_t class_mask) {
   CHK(check_model(m));
-  m->prof_on = enable != 0;
+  m->prof_mask = class_mask & ((1 << DLLM_PROF_N) - 1);
+  m->prof_on = m->prof_mask != 0;
   return DLLM_OK;
 }
 

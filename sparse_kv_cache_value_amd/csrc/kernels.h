@@ -134,4 +134,10 @@ hipError_t launch_ps_select(hipStream_t st, int B, int L, int blk, int W, int K,
                             const int32_t* bstart, const int32_t* assign, const double* klp, int32_t* wstart,
                             double* kl, int32_t* top_out, int32_t* idx, int32_t* n);
 
+// ---- diagnostics (probe.hip) ----
+// bytes must be a positive multiple of stream_probe_quantum(grid, depth);
+// depth is 4 or 8 loads of 16 bytes in flight per thread; out holds grid words.
+size_t stream_probe_quantum(int grid, int depth);
+hipError_t launch_stream_probe(hipStream_t st, int grid, int depth, const void* buf, size_t bytes, unsigned* out);
+
 }  // namespace dllm
