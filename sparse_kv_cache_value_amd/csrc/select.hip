@@ -8,7 +8,9 @@
 // bit patterns (non-negative doubles order like their unsigned bits), stopping
 // as soon as the bucket holding the cut is taken whole; rows equal to the
 // threshold on the resolved bits are ranked by an index-order scan, and the
-// selected rows are compacted in ascending order by a second scan.
+// selected rows are compacted in ascending order by a second scan.  When no
+// more candidates have a non-zero score than are needed (zero drift marks rows
+// whose input did not change), the cut is zero and no radix pass runs.
 #include "common.h"
 #include "kernels.h"
 
@@ -45,7 +47,7 @@ __device__ __forceinline__ uint64_t score_key(double s) {
   return (u >> 63) ? 0ull : u;  // -0.0 (and negatives, which drift never yields) rank as +0
 }
 
-// EM: rows held per thread, the smallest of 8/16/32 that covers ceil(L/256).
+// EM: rows held per thread, the smallest of 4/8/16/32 that covers ceil(L/256).
 template <int EM>
 __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const double* __restrict__ score,
                                                        const uint8_t* __restrict__ forced,
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
 
   uint64_t key[EM];
   int cls[EM];  // 0 = candidate, 1 = forced, 2 = past the end
-  int nf = 0;
+  int nf = 0, nz = 0;
 #pragma unroll
   for (int e = 0; e < EM; ++e) {
     const int i = i0 + e;
@@ -72,10 +74,14 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
       cls[e] = (fr && fr[i]) ? 1 : 0;
       key[e] = score_key(s[i]);
       nf += cls[e] == 1;
+      nz += cls[e] == 0 && key[e] != 0;
     }
   }
-  int nF;
-  (void)block_excl_scan(nf, wsum, &nF);
+  // forced rows (low 16 bits) and candidates of non-zero score (high bits),
+  // both <= L <= 8192, in one scan
+  int packed;
+  (void)block_excl_scan(nf | (nz << 16), wsum, &packed);
+  const int nF = packed & 0xFFFF, nnz = packed >> 16;
   const bool all_rows = full && full[b];
   const int keff = all_rows ? L : min(max(k, nF), L);
   const int need = keff - nF;       // rows to take by score
@@ -84,7 +90,11 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
   const int mode = need <= 0 ? 0 : (need >= ncand ? 1 : 2);
   uint64_t thr = 0;
   int take_eq = 0;
-  if (mode == 2) {
+  if (mode == 2 && need >= nnz) {
+    // the cut falls among the zero scores (rows whose input did not change):
+    // every non-zero candidate is taken, then zeros by index
+    take_eq = need - nnz;
+  } else if (mode == 2) {
     uint64_t prefix = 0, pmask = 0;
     int rem = need;
     for (int pass = 0; pass < 8; ++pass) {
@@ -190,7 +200,9 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
 hipError_t launch_select(hipStream_t st, int B, int L, int k, const double* score, const uint8_t* forced,
                          const uint8_t* full, int32_t* idx, int32_t* n) {
   if (L > SEL_T * SEL_EMAX) return hipErrorInvalidValue;
-  if (L <= SEL_T * 8)
+  if (L <= SEL_T * 4)
+    hipLaunchKernelGGL(select_kernel<4>, dim3(B), dim3(SEL_T), 0, st, L, k, score, forced, full, idx, n);
+  else if (L <= SEL_T * 8)
     hipLaunchKernelGGL(select_kernel<8>, dim3(B), dim3(SEL_T), 0, st, L, k, score, forced, full, idx, n);
   else if (L <= SEL_T * 16)
     hipLaunchKernelGGL(select_kernel<16>, dim3(B), dim3(SEL_T), 0, st, L, k, score, forced, full, idx, n);
