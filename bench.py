@@ -126,7 +126,12 @@ WORKLOADS = {
           "forced = block + recent 32, gate disabled",
     "C5": "Polestar drift path on the LLaDA-8B layer shape: 32 layers, batch 4, L=4096 (2048 + 2048 masked), "
           "window 96, 16 spherical k-means centroids x 10 iterations, NVFP4 residual codes, top-4 clusters",
+    "C5-commit": "C5 with Polestar-Commit (drift-delta rule, alpha = 1, tau_s = 0.9, suffix-block commit): "
+                 "LM head over the current and next block",
 }
+
+# the config object behind each name
+CONFIG_OF = {"C5-commit": lambda c: c.C5.with_(polestar_commit=True, commit_alpha=1.0)}
 
 
 def class_table(prof, steps, achievable, ms_per_step):
@@ -172,7 +177,7 @@ def bench_config(name, steps, warmup, achievable=None):
     from sparse_kv_cache_value_amd import binding as B
     from sparse_kv_cache_value_amd import configs, runtime
 
-    cfg = getattr(configs, name)
+    cfg = CONFIG_OF[name](configs) if name in CONFIG_OF else getattr(configs, name)
     model = runtime.Model(cfg, "cuda")
     st = runtime.State(cfg)
     ps = runtime.PolestarState(cfg) if cfg.score == configs.SCORE_POLESTAR else None
@@ -379,7 +384,7 @@ def main():
     if not args.no_other_configs:
         # the other configs of the scope table, a few sparse steps each
         out["other_configs"] = {}
-        for name, n, w in (("C1", 20, 3), ("C2", 20, 3), ("C4", 8, 2), ("C5", 8, 2)):
+        for name, n, w in (("C1", 20, 3), ("C2", 20, 3), ("C4", 8, 2), ("C5", 8, 2), ("C5-commit", 8, 2)):
             out["other_configs"][name] = bench_config(name, n, w, achievable)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

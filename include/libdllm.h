@@ -129,6 +129,9 @@ typedef struct {
   int32_t kmeans_iters;  /* assign/update iterations before the final assignment (10) */
   int32_t top_clusters;  /* clusters refreshed per layer and step (4), <= n_clusters */
   int32_t window_blocks; /* prefix, current and suffix block: 3 */
+  int32_t drift_commit;  /* 1: dllm_step commits with Polestar-Commit (dllm_polestar_commit);
+                            0: the static threshold commit */
+  double commit_alpha;   /* Polestar-Commit alpha (>= 0; +inf disables the drift rule) */
 } dllm_polestar_params;
 
 /* Caller-owned Polestar state (K = n_clusters, Hq = n_q_heads, W as above).
@@ -146,6 +149,11 @@ typedef struct {
   void *queries;         /* [B][K][n_q_heads*head_dim] centroid queries (storage dtype) */
   double *kl;            /* [B][K] cluster drift (mean over heads of KL(A_t || A_t-1)) */
   int32_t *top;          /* [B][top_clusters] refreshed clusters, ascending */
+  /* Polestar-Commit (initialise to zero): */
+  double *drift_sum;     /* [B][block_len] sum of the current block rows' drifts at earlier steps */
+  int32_t *drift_cnt;    /* [B][block_len] number of drifts in drift_sum */
+  int32_t *drift_valid;  /* [B] 1 when the last dllm_polestar_select found the cluster drift
+                            defined (window unchanged); the Polestar commit clears it */
 } dllm_polestar_state;
 
 typedef struct {
@@ -264,6 +272,26 @@ dllm_status dllm_polestar_drift(dllm_model *m, int32_t layer, const dllm_state *
  * with dllm_sparse_layer(max_rows = batch * W). */
 dllm_status dllm_polestar_select(dllm_model *m, int32_t layer, const dllm_state *s, dllm_polestar_state *ps,
                                  const dllm_polestar_params *p, int32_t *idx, int32_t *n_sel, void *stream);
+
+/* Polestar-Commit (Polestar, section 2B) of one step, in place of dllm_commit
+ * for callers of the Polestar drift path.  The LM-head statistics are taken
+ * for the current block and the next one (rows past seq_len are skipped).
+ * Uses the cluster drift, assignment and top clusters that the last
+ * dllm_polestar_drift / dllm_polestar_select left in ps (the last layer's),
+ * when ps->drift_valid says they are defined.  For each still-masked row j of
+ * the current block with confidence c_j: commit if c_j >= conf_threshold (tau_s),
+ * or if its drift D_j (its cluster's drift) exceeds the mean of its earlier
+ * drifts in this block by more than alpha (tau_s - c_j)^2 (strictly; no
+ * earlier drift: no drift commit).  If none commits, the most confident
+ * masked row does (lowest position on ties).  If a top cluster has a member
+ * among the window rows after the current block, the next block's masked
+ * rows with c >= tau_s commit too.  Commits are appended to the history in
+ * ascending position order; the entropy gate and block advance are those of
+ * dllm_commit.  Then D_j is added to drift_sum/drift_cnt (both cleared when
+ * the block advances) and drift_valid is cleared. */
+dllm_status dllm_polestar_commit(dllm_model *m, dllm_state *s, dllm_polestar_state *ps,
+                                 const dllm_polestar_params *p, double conf_threshold, double tau,
+                                 void *stream);
 
 /* Forced rows for the next step, forced[b][i] in {0,1} ([B][L]):
  * DLLM_FORCED_BLOCK marks the current block, DLLM_FORCED_BLOCK_RECENT also the

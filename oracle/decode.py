@@ -15,6 +15,9 @@ Readings (where the pages leave the step open):
 * Forced sets: "block+recent" = every row of the current block plus the last
   ``recent_k`` entries of the decode history (EntropyCache); "block" = the
   current block (Polestar); "none" = drift alone (SPA-Cache).
+* Commit rule: "threshold" (static confidence threshold) or "polestar"
+  (Polestar section 2B, see ``polestar.drift_commit``; it needs the Polestar
+  drift path and uses its last layer's cluster drift).
 """
 
 from __future__ import annotations
@@ -38,6 +41,8 @@ class Policy:
     conf_threshold: float = 0.9
     score: str = "spa_cos"          # or "polestar_kl" (Polestar section 2A drift path)
     polestar: polestar.PolestarParams = dataclasses.field(default_factory=polestar.PolestarParams)
+    commit: str = "threshold"       # or "polestar" (Polestar section 2B)
+    commit_alpha: float = 1.0       # Polestar-Commit alpha
 
 
 class SeqState:
@@ -58,6 +63,9 @@ class SeqState:
         self.full_next = True
         self.n_new = 0
         self.ps = [polestar.PolestarLayerState() for _ in range(N)]
+        # Polestar-Commit: sum and count of the current block rows' past drifts
+        self.drift_sum = np.zeros(spec.block_len, np.float64)
+        self.drift_cnt = np.zeros(spec.block_len, np.int64)
 
     def advance_block(self):
         L, b = self.spec.seq_len, self.spec.block_len
@@ -120,7 +128,10 @@ def step(st: SeqState, layers, head, spec: Spec, pol: Policy, force_mode: Option
         sets.append(I)
         scores.append(s)
     info = {"full": full, "sets": sets, "scores": scores, "forced": forced, "polestar": ps_info}
-    info.update(commit_block(st, head, spec, pol))
+    if pol.commit == "polestar":
+        info.update(commit_block_polestar(st, head, spec, pol, ps_info[-1] if ps_info else None))
+    else:
+        info.update(commit_block(st, head, spec, pol))
     return info
 
 
@@ -141,3 +152,41 @@ def commit_block(st: SeqState, head, spec: Spec, pol: Policy):
     st.advance_block()
     st.full_next = emax > pol.tau
     return {"rows": rows, "stats": stats, "pos": pos, "tok": tok, "emax": emax}
+
+
+def commit_block_polestar(st: SeqState, head, spec: Spec, pol: Policy, last):
+    """Polestar-Commit of one step; ``last`` is the last layer's drift-path
+    result of this step (None in a full step)."""
+    L, blk = spec.seq_len, spec.block_len
+    rows = st.block_rows()
+    if rows.size == 0:
+        st.n_new = 0
+        st.full_next = False
+        return {"rows": rows, "stats": None, "pos": [], "tok": [], "emax": 0.0}
+    bs = st.block_start
+    srows = np.arange(bs + blk, min(bs + 2 * blk, L))
+    both = np.concatenate([rows, srows])
+    stats = lm_stats(st.H[spec.n_layers][both], head["final_norm"], head["lm_head"], spec)
+    n = rows.size
+    cur = {k: stats[k][:n] for k in ("conf", "argmax", "entropy")}
+    suf = {k: stats[k][n:] for k in ("conf", "argmax", "entropy")}
+    valid = last is not None and last["valid"]
+    D = polestar.token_drift(rows, last["wstart"], last["assign"], last["kl"]) if valid else None
+    hit = valid and polestar.suffix_hit(bs, blk, last["wstart"], last["assign"], last["top"])
+    pos, tok, emax, _ = polestar.drift_commit(rows, cur, srows, suf, st.committed, pol.conf_threshold,
+                                              pol.commit_alpha, D, st.drift_sum[:n], st.drift_cnt[:n], hit)
+    if D is not None:
+        st.drift_sum[:n] += D
+        st.drift_cnt[:n] += 1
+    for p, t in zip(pos, tok):
+        st.tokens[p] = t
+        st.committed[p] = True
+        st.history.append(p)
+    st.n_new = len(pos)
+    st.advance_block()
+    if st.block_start != bs:
+        st.drift_sum[:] = 0.0
+        st.drift_cnt[:] = 0
+    st.full_next = emax > pol.tau
+    return {"rows": rows, "srows": srows, "stats": stats, "pos": pos, "tok": tok, "emax": emax, "D": D,
+            "hit": hit}

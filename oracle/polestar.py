@@ -266,7 +266,8 @@ def drift_and_select(x, K, block_start: int, W, spec: Spec, pp: PolestarParams, 
     pos = ws + stride * np.arange(pp.n_clusters)
     q = centroid_queries(C, pos, W, spec)
     logA = proxy_log_attention(q, np.asarray(K)[ws:ws + Wn])
-    if prev.logA is not None and prev.wstart == ws:
+    valid = prev.logA is not None and prev.wstart == ws
+    if valid:
         kl = cluster_kl(logA, prev.logA)
     else:
         kl = np.zeros(pp.n_clusters)
@@ -275,4 +276,91 @@ def drift_and_select(x, K, block_start: int, W, spec: Spec, pp: PolestarParams, 
     rows = np.arange(block_start, min(block_start + blk, L))
     I = select_rows(rows, ws, a, top)
     return {"wstart": ws, "Xh": Xh, "C": C, "assign": a, "obj": obj, "dots": D, "codes": codes,
-            "scales": scales, "q": q, "logA": logA, "kl": kl, "top": top, "I": I}
+            "scales": scales, "q": q, "logA": logA, "kl": kl, "valid": valid, "top": top, "I": I}
+
+
+# ---------------------------------------------------------------------------
+# Polestar-Commit (Polestar page, section 2B).
+#
+# What the page states:
+# - For the current block it tracks each token's drift delta: the token's
+#   drift minus the historical mean of its drift.  A sharp positive delta
+#   signals fast context integration.
+# - A token commits when its delta exceeds a confidence-dependent threshold
+#   alpha (tau_s - c)^2, so a low-confidence token with a strong convergence
+#   signal can still commit.
+# - The last layer's update packet is also inspected: when a centroid of the
+#   suffix window is among the top drift clusters, suffix tokens commit, but
+#   only at the high confidence threshold (>= tau_s).
+#
+# Readings (the page gives no values or definitions beyond these):
+# - tau_s is the static confidence threshold of the threshold commit, and a
+#   token that clears it commits as before; the drift rule adds commits.
+# - A token's drift D_j is the cluster drift (mean over heads of the proxy
+#   attention KL) of its cluster at the last layer.  It is defined only when
+#   that layer's drift is (the window did not move since the previous step).
+# - The historical mean is the mean of D_j over the earlier steps of the
+#   current block at which it was defined; with no earlier value there is no
+#   delta and no drift commit.  The history restarts when the block advances.
+# - "A suffix centroid among the top clusters": a top cluster of the last
+#   layer has a member among the window rows after the current block.  The
+#   suffix tokens considered are the masked rows of the next block.
+# - If nothing commits in the current block, the most confident masked row of
+#   the block commits (lowest position on ties), as in the threshold commit.
+# - Commits are appended to the decode history in ascending position order
+#   (current block, then suffix); the entropy gate takes the maximum entropy
+#   over all of them.
+# ---------------------------------------------------------------------------
+def token_drift(rows, wstart: int, assign, kl):
+    """D_j of window rows ``rows``: the drift of the cluster each belongs to."""
+    a = np.asarray(assign)
+    return np.array([float(kl[a[int(r) - wstart]]) for r in rows], np.float64)
+
+
+def suffix_hit(block_start: int, blk: int, wstart: int, assign, top) -> bool:
+    """Whether a top cluster has a member among the window rows after the
+    current block."""
+    a = np.asarray(assign)
+    first = block_start + blk - wstart  # first window index after the block
+    return any(int(a[r]) in set(int(t) for t in top) for r in range(max(first, 0), a.size))
+
+
+def drift_commit(cur_rows, cur, suf_rows, suf, committed, tau_s: float, alpha: float, D, hist_sum, hist_cnt,
+                 hit: bool):
+    """One Polestar-Commit decision.
+
+    cur_rows / suf_rows: positions of the current and the next block; cur /
+    suf: their LM statistics (dicts with conf, argmax, entropy); committed:
+    bool [L] (not modified); D: drift of the current block rows, or None when
+    undefined this step; hist_sum / hist_cnt: sum and count of their earlier
+    drifts (read only here).  Returns (positions in ascending order, tokens,
+    max entropy, pick flags of the current rows)."""
+    n = len(cur_rows)
+    cand = [j for j in range(n) if not committed[cur_rows[j]]]
+    pick = []
+    for j in cand:
+        c = float(cur["conf"][j])
+        if c >= tau_s:
+            pick.append(j)
+        elif D is not None and hist_cnt[j] > 0:
+            delta = float(D[j]) - float(hist_sum[j]) / float(hist_cnt[j])
+            t = tau_s - c
+            if delta > alpha * (t * t):
+                pick.append(j)
+    if not pick and cand:
+        best = cand[0]
+        for j in cand[1:]:
+            if cur["conf"][j] > cur["conf"][best]:
+                best = j
+        pick = [best]
+    pick.sort()
+    spick = []
+    if hit:
+        spick = [j for j in range(len(suf_rows))
+                 if not committed[suf_rows[j]] and float(suf["conf"][j]) >= tau_s]
+    pos = [int(cur_rows[j]) for j in pick] + [int(suf_rows[j]) for j in spick]
+    tok = [int(cur["argmax"][j]) for j in pick] + [int(suf["argmax"][j]) for j in spick]
+    ents = [float(cur["entropy"][j]) for j in pick] + [float(suf["entropy"][j]) for j in spick]
+    flags = np.zeros(n, bool)
+    flags[pick] = True
+    return pos, tok, max(ents, default=0.0), flags

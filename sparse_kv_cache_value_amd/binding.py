@@ -43,12 +43,14 @@ class DllmState(ctypes.Structure):
 
 
 class DllmPolestarParams(ctypes.Structure):
-    _fields_ = [("n_clusters", _i32), ("kmeans_iters", _i32), ("top_clusters", _i32), ("window_blocks", _i32)]
+    _fields_ = [("n_clusters", _i32), ("kmeans_iters", _i32), ("top_clusters", _i32), ("window_blocks", _i32),
+                ("drift_commit", _i32), ("commit_alpha", _f64)]
 
 
 class DllmPolestarState(ctypes.Structure):
     _fields_ = [(n, _vp) for n in (
-        "log_attn", "win_start", "centroids", "norms", "assign", "codes", "scales", "queries", "kl", "top")]
+        "log_attn", "win_start", "centroids", "norms", "assign", "codes", "scales", "queries", "kl", "top",
+        "drift_sum", "drift_cnt", "drift_valid")]
 
 
 class DllmStepParams(ctypes.Structure):
@@ -89,6 +91,8 @@ SIGNATURES = {
                                    ctypes.POINTER(DllmPolestarParams), _vp]),
     "dllm_polestar_select": (_i32, [_vp, _i32, ctypes.POINTER(DllmState), ctypes.POINTER(DllmPolestarState),
                                     ctypes.POINTER(DllmPolestarParams), _vp, _vp, _vp]),
+    "dllm_polestar_commit": (_i32, [_vp, ctypes.POINTER(DllmState), ctypes.POINTER(DllmPolestarState),
+                                    ctypes.POINTER(DllmPolestarParams), _f64, _f64, _vp]),
     "dllm_step": (_i32, [_vp, ctypes.POINTER(DllmState), ctypes.POINTER(DllmStepParams),
                          ctypes.POINTER(DllmStepResult), _vp]),
     "dllm_profile": (_i32, [_vp, _i32]),
@@ -205,6 +209,12 @@ def dllm_polestar_drift(m: int, layer: int, state, ps, params: DllmPolestarParam
 def dllm_polestar_select(m: int, layer: int, state, ps, params: DllmPolestarParams, idx, n_sel, stream=None):
     _check(lib().dllm_polestar_select(m, layer, ctypes.byref(state.c), ctypes.byref(ps.c), ctypes.byref(params),
                                       _p(idx), _p(n_sel), _stream(stream)))
+
+
+def dllm_polestar_commit(m: int, state, ps, params: DllmPolestarParams, conf_threshold: float, tau: float,
+                         stream=None):
+    _check(lib().dllm_polestar_commit(m, ctypes.byref(state.c), ctypes.byref(ps.c), ctypes.byref(params),
+                                      float(conf_threshold), float(tau), _stream(stream)))
 
 
 def dllm_step(m: int, state, mode: int, forced_rule: int, recent_k: int, tau: float, conf_threshold: float,

@@ -87,6 +87,8 @@ class Config:
     n_clusters: int = 16
     kmeans_iters: int = 10
     top_clusters: int = 4
+    polestar_commit: bool = False   # Polestar-Commit (Polestar section 2B) instead of the threshold commit
+    commit_alpha: float = 1.0
     # C2-style stale cache
     stale_frac: float = 0.0
     stale_std: float = 0.0

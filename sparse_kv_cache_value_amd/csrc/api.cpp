@@ -345,9 +345,11 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
   return DLLM_OK;
 }
 
-dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st) {
+// LM-head statistics of the first nblk blocks from each sequence's block
+// start (nblk = 1: the current block; 2: also the next one).
+dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int nblk = 1) {
   const dllm_dims& d = m->d;
-  const int B = s->batch, blk = d.block_len;
+  const int B = s->batch, blk = d.block_len * nblk;
   {
     Prof prof(m, st, DLLM_PROF_DECIDE, 2.0 * B * blk * d.d_model * m->esize, 4.0 * B * blk * d.d_model);
     HIPCHK(launch_lm_gather(st, m->bf16, B, d.seq_len, blk, d.d_model, d.rms_eps, m->lm_MTt, s->block_start,
@@ -355,7 +357,7 @@ dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st) {
     prof.done();
   }
   int sp = 1;
-  const size_t cap = (size_t)d.max_batch * blk * d.vocab;
+  const size_t cap = (size_t)d.max_batch * 2 * d.block_len * d.vocab;
   if (m->bf16) {
     Prof prof(m, st, DLLM_PROF_LMHEAD,
               (double)d.d_model * d.vocab * 2.0 + (double)B * blk * d.d_model * 2.0 + (double)B * blk * d.vocab * 4.0,
@@ -383,6 +385,20 @@ dllm_status do_commit(dllm_model* m, dllm_state* s, double thr, double tau, hipS
   return DLLM_OK;
 }
 
+dllm_status do_polestar_commit(dllm_model* m, dllm_state* s, dllm_polestar_state* ps, const dllm_polestar_params* p,
+                               double thr, double tau, hipStream_t st) {
+  CHK(do_lm_head(m, s, st, 2));
+  const dllm_dims& d = m->d;
+  const int W = p->window_blocks * d.block_len;
+  Prof prof(m, st, DLLM_PROF_DECIDE, (double)s->batch * d.block_len * 2.0 * (32.0 + 4.0 + 1.0 + 12.0), 0.0);
+  HIPCHK(launch_ps_commit(st, s->batch, d.seq_len, d.block_len, W, p->n_clusters, p->top_clusters, thr,
+                          p->commit_alpha, tau, m->lm_stats, ps->kl, ps->assign, ps->top, ps->drift_valid,
+                          ps->drift_sum, ps->drift_cnt, s->tokens, s->committed, s->history, s->n_history, s->n_new,
+                          s->block_start, s->full_next, s->max_entropy));
+  prof.done();
+  return DLLM_OK;
+}
+
 dllm_status finish_step(dllm_model* m, dllm_state* s, dllm_step_result* res_h, hipStream_t st) {
   if (!res_h) return DLLM_OK;
   const int B = s->batch, L = m->d.seq_len;
@@ -402,8 +418,10 @@ dllm_status check_polestar(const dllm_model* m, const dllm_state* s, const dllm_
   const dllm_dims& d = m->d;
   if (!ps || !p) return fail(DLLM_E_ARG, "polestar state/params is NULL");
   if (!ps->log_attn || !ps->win_start || !ps->centroids || !ps->norms || !ps->assign || !ps->codes || !ps->scales ||
-      !ps->queries || !ps->kl || !ps->top)
+      !ps->queries || !ps->kl || !ps->top || !ps->drift_sum || !ps->drift_cnt || !ps->drift_valid)
     return fail(DLLM_E_ARG, "polestar state has a NULL buffer");
+  if (p->drift_commit && !(p->commit_alpha >= 0.0)) return fail(DLLM_E_ARG, "commit_alpha must be >= 0");
+  if (d.block_len > 64) return fail(DLLM_E_UNSUPPORTED, "the Polestar path needs block_len <= 64");
   if (!m->ps_R) return fail(DLLM_E_UNSUPPORTED, "the Polestar path needs d_model %% 128 == 0");
   const int W = p->window_blocks * d.block_len;
   if (p->n_clusters < 1 || p->n_clusters > 16) return fail(DLLM_E_ARG, "n_clusters must be in [1, 16]");
@@ -466,7 +484,7 @@ dllm_status do_polestar_select(dllm_model* m, int layer, const dllm_state* s, dl
   Prof prof(m, st, DLLM_PROF_SELECT, (double)B * d.n_q_heads * p->n_clusters * 8.0 + (double)B * W * 8.0, 0.0);
   HIPCHK(launch_ps_select(st, B, d.seq_len, d.block_len, W, p->n_clusters, d.n_q_heads, p->top_clusters,
                           s->block_start, ps->assign, m->ps_klp, ps->win_start + (size_t)layer * B, ps->kl, ps->top,
-                          idx, n));
+                          idx, n, ps->drift_valid));
   prof.done();
   return DLLM_OK;
 }
@@ -552,7 +570,7 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   ALLOC(m->n0, (size_t)d.max_batch * 4);
   ALLOC(m->forced, (size_t)m->M_cap);
   ALLOC(m->step_full, (size_t)d.max_batch);
-  const int lm_rows_cap = d.max_batch * d.block_len;
+  const int lm_rows_cap = d.max_batch * 2 * d.block_len;  // current and next block (Polestar-Commit)
   m->lm_MTt = (lm_rows_cap + 31) / 32 + 1;
   ALLOC(m->A_lm, (size_t)m->lm_MTt * 32 * D * es + gemm_pad_elems(m->lm_MTt) * es);
   ALLOC(m->logits, (size_t)lm_rows_cap * d.vocab * 4);
@@ -740,6 +758,17 @@ dllm_status dllm_commit(dllm_model* m, dllm_state* s, double conf_threshold, dou
   return do_commit(m, s, conf_threshold, tau, S(stream));
 }
 
+dllm_status dllm_polestar_commit(dllm_model* m, dllm_state* s, dllm_polestar_state* ps,
+                                 const dllm_polestar_params* p, double conf_threshold, double tau, void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s, false));
+  CHK(check_polestar(m, s, ps, p));
+  if (!m->head_ready) return fail(DLLM_E_STATE, "head weights not initialised");
+  if (std::isnan(conf_threshold) || std::isnan(tau)) return fail(DLLM_E_ARG, "threshold is NaN");
+  if (!(p->commit_alpha >= 0.0)) return fail(DLLM_E_ARG, "commit_alpha must be >= 0");
+  return do_polestar_commit(m, s, ps, p, conf_threshold, tau, S(stream));
+}
+
 dllm_status dllm_polestar_drift(dllm_model* m, int32_t layer, const dllm_state* s, dllm_polestar_state* ps,
                                 const dllm_polestar_params* p, void* stream) {
   CHK(check_model(m));
@@ -822,7 +851,10 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
       CHK(do_polestar_select(m, l, s, p->polestar_state, p->polestar, idx, n, st));
       CHK(do_sparse(m, l, s, idx, n, B * W, st));
     }
-    CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
+    if (p->polestar->drift_commit)
+      CHK(do_polestar_commit(m, s, p->polestar_state, p->polestar, p->conf_threshold, p->tau, st));
+    else
+      CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
     return finish_step(m, s, res_h, st);
   }
   for (int l = 0; l < d.n_layers; ++l) {
@@ -842,7 +874,10 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     prev_n = n;
     prev_max = rows;
   }
-  CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
+  if (polestar && p->polestar->drift_commit)
+    CHK(do_polestar_commit(m, s, p->polestar_state, p->polestar, p->conf_threshold, p->tau, st));
+  else
+    CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
   return finish_step(m, s, res_h, st);
 }
 

@@ -132,7 +132,13 @@ hipError_t launch_ps_attn_kl(hipStream_t st, bool bf16, int B, int L, int blk, i
                              int dh, const int32_t* bstart, const void* q, const void* Kc, double* logA, double* klp);
 hipError_t launch_ps_select(hipStream_t st, int B, int L, int blk, int W, int K, int Hq, int top,
                             const int32_t* bstart, const int32_t* assign, const double* klp, int32_t* wstart,
-                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n);
+                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n, int32_t* valid);
+// Polestar-Commit; stats [B][2 blk][4] (current and next block), blk <= 64.
+hipError_t launch_ps_commit(hipStream_t st, int B, int L, int blk, int W, int K, int top, double thr, double alpha,
+                            double tau, const double* stats, const double* kl, const int32_t* assign,
+                            const int32_t* top_c, int32_t* drift_valid, double* dsum, int32_t* dcnt,
+                            int32_t* tokens, uint8_t* committed, int32_t* history, int32_t* n_history,
+                            int32_t* n_new, int32_t* block_start, uint8_t* full_next, double* max_entropy);
 
 // ---- diagnostics (probe.hip) ----
 // bytes must be a positive multiple of stream_probe_quantum(grid, depth);

@@ -536,7 +536,8 @@ __global__ __launch_bounds__(128) void ps_select_kernel(int L, int blk, int W, i
                                                         const int32_t* __restrict__ assign,
                                                         const double* __restrict__ klp, int32_t* __restrict__ wstart,
                                                         double* __restrict__ kl_out, int32_t* __restrict__ top_out,
-                                                        int32_t* __restrict__ idx, int32_t* __restrict__ n_out) {
+                                                        int32_t* __restrict__ idx, int32_t* __restrict__ n_out,
+                                                        int32_t* __restrict__ valid_out) {
   __shared__ double kl[16];
   __shared__ int sel[16];
   __shared__ int cnt0;
@@ -571,7 +572,10 @@ __global__ __launch_bounds__(128) void ps_select_kernel(int L, int blk, int W, i
     for (int j = 0; j < tid; ++j) pos += sel[j];
     top_out[(size_t)b * top + pos] = tid;
   }
-  if (tid == 0) wstart[b] = ws;
+  if (tid == 0) {
+    wstart[b] = ws;
+    valid_out[b] = valid ? 1 : 0;
+  }
   // I = current block rows + members of the selected clusters, ascending
   const int row = ws + tid;
   const bool f = tid < W && ((row >= bs && row < bs + blk) || sel[assign[(size_t)b * W + tid]]);
@@ -582,6 +586,162 @@ __global__ __launch_bounds__(128) void ps_select_kernel(int L, int blk, int W, i
   const int off = (tid >> 6) ? cnt0 : 0;
   if (f) idx[(size_t)b * L + off + __popcll(m & below)] = row;
   if (tid == 64) n_out[b] = cnt0 + __popcll(m);
+}
+
+// ---------------------------------------------------------------------------
+// Polestar-Commit (Polestar page, section 2B), one workgroup per sequence:
+// wave 0 holds the current block's rows, wave 1 the next block's.  stats:
+// [B][2 blk][4] LM-head statistics of both blocks.  A masked current row
+// commits at conf >= thr, or when its drift D (its cluster's drift at the last
+// layer, defined when drift_valid) exceeds the mean of its earlier drifts in
+// this block by more than alpha (thr - conf)^2; if none commits, the most
+// confident masked row (lowest position on ties).  When a top cluster has a
+// member among the window rows after the block, the next block's masked rows
+// with conf >= thr commit too.  History gets the current block's commits then
+// the next block's, ascending; entropy gate and block advance as in the
+// threshold commit.  Then D is added to the drift history (cleared when the
+// block advances) and drift_valid is cleared.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void ps_commit_kernel(
+    int L, int blk, int W, int K, int top, double thr, double alpha, double tau, const double* __restrict__ stats,
+    const double* __restrict__ kl, const int32_t* __restrict__ assign, const int32_t* __restrict__ top_c,
+    int32_t* __restrict__ drift_valid, double* __restrict__ dsum, int32_t* __restrict__ dcnt,
+    int32_t* __restrict__ tokens, uint8_t* __restrict__ committed, int32_t* __restrict__ history,
+    int32_t* __restrict__ n_history, int32_t* __restrict__ n_new, int32_t* __restrict__ block_start,
+    uint8_t* __restrict__ full_next, double* __restrict__ max_entropy) {
+  __shared__ int s_hit, s_cnt[2], s_nbs;
+  __shared__ double s_e[2];
+  __shared__ uint8_t done_row[128];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int bs = block_start[b];
+  const bool active = bs < L;
+  const int ws = ps_window_start(active ? bs : 0, L, blk, W);
+  const bool valid = active && drift_valid[b] != 0;
+  uint8_t* cm = committed + (size_t)b * L;
+  if (wv == 1) {
+    // suffix hit: a top cluster among the window rows after the current block
+    unsigned tmask = 0u;
+    for (int t = 0; t < top; ++t) tmask |= 1u << top_c[(size_t)b * top + t];
+    const int first = bs + blk - ws;
+    bool h = false;
+    for (int r = lane; r < W; r += 64)
+      if (r >= first && ((tmask >> assign[(size_t)b * W + r]) & 1u)) h = true;
+    const bool any = __ballot(h) != 0ull;
+    if (lane == 0) s_hit = (valid && any) ? 1 : 0;
+  }
+  const int row = bs + wv * blk + lane;
+  const bool rv = active && lane < blk && row < L;
+  double conf = 0.0, ent = 0.0, D = 0.0;
+  int tok = 0;
+  bool cand = false;
+  if (rv) {
+    const double* p = stats + ((size_t)b * 2 * blk + wv * blk + lane) * 4;
+    conf = 1.0 / p[2];
+    ent = log(p[2]) - p[3] / p[2];
+    tok = (int)p[1];
+    cand = cm[row] == 0;
+  }
+  bool pick = false;
+  if (wv == 0) {
+    int cnt = 0;
+    double sm = 0.0;
+    if (rv) {
+      cnt = dcnt[(size_t)b * blk + lane];
+      sm = dsum[(size_t)b * blk + lane];
+      if (valid) D = kl[(size_t)b * K + assign[(size_t)b * W + (row - ws)]];
+    }
+    if (cand) {
+      if (conf >= thr) {
+        pick = true;
+      } else if (valid && cnt > 0) {
+        const double delta = D - sm / (double)cnt;
+        const double t = thr - conf;
+        pick = delta > alpha * (t * t);
+      }
+    }
+    const uint64_t any_pick = __ballot(pick);
+    const uint64_t any_cand = __ballot(cand);
+    if (any_pick == 0ull && any_cand != 0ull) {
+      // most confident candidate, lowest position on ties
+      double bc = cand ? conf : -1.0;
+      int br = cand ? row : 0x7fffffff;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const double oc = __shfl_xor(bc, o, 64);
+        const int orr = __shfl_xor(br, o, 64);
+        if (oc > bc || (oc == bc && orr < br)) {
+          bc = oc;
+          br = orr;
+        }
+      }
+      pick = cand && row == br;
+    }
+  }
+  __syncthreads();
+  if (wv == 1) pick = s_hit != 0 && cand && conf >= thr;
+  const uint64_t mask = __ballot(pick);
+  double e = pick ? ent : 0.0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) e = fmax(e, __shfl_xor(e, o, 64));
+  if (lane == 0) {
+    s_cnt[wv] = __popcll(mask);
+    s_e[wv] = e;
+  }
+  // rows of both blocks committed after this step (rows past L count as done)
+  if (lane < blk) done_row[wv * blk + lane] = (!rv || !cand || pick) ? 1 : 0;
+  __syncthreads();
+  const int nh = n_history[b];
+  if (pick) {
+    const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+    tokens[(size_t)b * L + row] = tok;
+    cm[row] = 1;
+    history[(size_t)b * L + nh + (wv ? s_cnt[0] : 0) + rank] = row;
+  }
+  if (tid == 0) {
+    int nbs = bs;
+    if (active) {
+      bool cur_done = true;
+      for (int j = 0; j < blk; ++j) cur_done = cur_done && done_row[j];
+      if (cur_done) {
+        nbs = bs + blk;
+        if (nbs < L) {
+          bool nxt_done = true;
+          for (int j = 0; j < blk; ++j) nxt_done = nxt_done && done_row[blk + j];
+          if (nxt_done) {
+            nbs += blk;
+            // later blocks are untouched by this step
+            while (nbs < L) {
+              bool c = true;
+              for (int j = 0; j < blk && nbs + j < L; ++j) c = c && cm[nbs + j] != 0;
+              if (!c) break;
+              nbs += blk;
+            }
+          }
+        }
+      }
+    }
+    s_nbs = nbs;
+    const int cnt = s_cnt[0] + s_cnt[1];
+    const double em = fmax(s_e[0], s_e[1]);
+    n_history[b] = nh + cnt;
+    n_new[b] = cnt;
+    max_entropy[b] = em;
+    full_next[b] = em > tau ? 1 : 0;
+    block_start[b] = nbs;
+    drift_valid[b] = 0;
+  }
+  __syncthreads();
+  if (wv == 0 && lane < blk && active) {
+    double* sp = dsum + (size_t)b * blk + lane;
+    int32_t* cp = dcnt + (size_t)b * blk + lane;
+    if (s_nbs != bs) {
+      *sp = 0.0;
+      *cp = 0;
+    } else if (valid && rv) {
+      *sp = *sp + D;
+      *cp = *cp + 1;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -672,10 +832,22 @@ hipError_t launch_ps_attn_kl(hipStream_t st, bool bf16m, int B, int L, int blk, 
 
 hipError_t launch_ps_select(hipStream_t st, int B, int L, int blk, int W, int K, int Hq, int top,
                             const int32_t* bstart, const int32_t* assign, const double* klp, int32_t* wstart,
-                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n) {
+                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n, int32_t* valid) {
   if (W > PS_WMAX || K > 16) return hipErrorInvalidValue;
   hipLaunchKernelGGL(ps_select_kernel, dim3(B), dim3(128), 0, st, L, blk, W, K, Hq, top, bstart, assign, klp, wstart,
-                     kl, top_out, idx, n);
+                     kl, top_out, idx, n, valid);
+  return hipGetLastError();
+}
+
+hipError_t launch_ps_commit(hipStream_t st, int B, int L, int blk, int W, int K, int top, double thr, double alpha,
+                            double tau, const double* stats, const double* kl, const int32_t* assign,
+                            const int32_t* top_c, int32_t* drift_valid, double* dsum, int32_t* dcnt,
+                            int32_t* tokens, uint8_t* committed, int32_t* history, int32_t* n_history,
+                            int32_t* n_new, int32_t* block_start, uint8_t* full_next, double* max_entropy) {
+  if (W > PS_WMAX || K > 16 || blk > 64 || top > K) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ps_commit_kernel, dim3(B), dim3(128), 0, st, L, blk, W, K, top, thr, alpha, tau, stats, kl,
+                     assign, top_c, drift_valid, dsum, dcnt, tokens, committed, history, n_history, n_new,
+                     block_start, full_next, max_entropy);
   return hipGetLastError();
 }
 

@@ -113,7 +113,8 @@ class State:
 
 
 def polestar_params(cfg: Config) -> B.DllmPolestarParams:
-    return B.DllmPolestarParams(cfg.n_clusters, cfg.kmeans_iters, cfg.top_clusters, cfg.window_blocks)
+    return B.DllmPolestarParams(cfg.n_clusters, cfg.kmeans_iters, cfg.top_clusters, cfg.window_blocks,
+                                1 if cfg.polestar_commit else 0, float(cfg.commit_alpha))
 
 
 class PolestarState:
@@ -135,9 +136,12 @@ class PolestarState:
         self.queries = torch.zeros((Bn, K, cfg.n_q), dtype=inputs.storage_dtype(cfg), device=dev)
         self.kl = torch.zeros((Bn, K), dtype=torch.float64, device=dev)
         self.top = torch.zeros((Bn, cfg.top_clusters), dtype=torch.int32, device=dev)
+        self.drift_sum = torch.zeros((Bn, cfg.block_len), dtype=torch.float64, device=dev)
+        self.drift_cnt = torch.zeros((Bn, cfg.block_len), dtype=torch.int32, device=dev)
+        self.drift_valid = torch.zeros(Bn, dtype=torch.int32, device=dev)
         self.c = B.DllmPolestarState(*[t.data_ptr() for t in (
             self.log_attn, self.win_start, self.centroids, self.norms, self.assign, self.codes, self.scales,
-            self.queries, self.kl, self.top)])
+            self.queries, self.kl, self.top, self.drift_sum, self.drift_cnt, self.drift_valid)])
 
 
 def step(model: Model, state: State, mode: int = B.DLLM_MODE_AUTO, want_result: bool = True, stream=None,

@@ -496,11 +496,115 @@ def check_polestar_selection():
     assert r4["wstart"] == 0 and np.all(r4["kl"] > 0.0)
 
 
+def check_polestar_commit():
+    """P15, Polestar-Commit (Polestar section 2B).
+
+    - Worked example in exact binary fractions: tau_s = 0.75, c = 0.25, alpha = 2
+      gives a threshold 2 (0.75 - 0.25)^2 = 0.5; past drifts 0.75 and 1.25 give
+      a mean of 1; a drift of 1.5 (delta 0.5) does not commit (strict), 1.5625
+      (delta 0.5625) does.
+    - Without a defined drift, or with an infinite alpha, it is the static
+      threshold commit (same positions, tokens and entropy).
+    - alpha = 0 commits exactly the masked rows with a positive delta (and the
+      ones over tau_s); a row with no earlier drift never commits by drift.
+    - Suffix rows commit only on a hit and only at conf >= tau_s.
+    - Raising alpha never adds a commit.
+    - suffix_hit and token_drift on hand-built window assignments.
+    - Decode: the drift history accumulates while the block stays and restarts
+      when it advances."""
+    from oracle import polestar as ps
+    from oracle.model import commit as thr_commit
+
+    def stats(conf, ent=None, tok=None):
+        conf = np.asarray(conf, np.float64)
+        n = conf.size
+        return {"conf": conf, "entropy": np.asarray(ent if ent is not None else np.arange(n) + 0.5, np.float64),
+                "argmax": np.asarray(tok if tok is not None else np.arange(n) + 100, np.int64)}
+
+    L = 16
+    committed = np.zeros(L, bool)
+    rows, srows = np.arange(4, 8), np.arange(8, 12)
+    cur = stats([0.25, 0.25, 0.25, 0.25])
+    suf = stats([0.9, 0.5, 0.75, 0.1])
+    hs, hc = np.full(4, 2.0), np.full(4, 2)
+    D = np.array([1.5, 1.5625, 0.0, 1.5625])
+    committed[7] = True  # row 7 is no candidate
+    pos, tok, emax, fl = ps.drift_commit(rows, cur, srows, suf, committed, 0.75, 2.0, D, hs, hc, False)
+    assert pos == [5] and tok == [101] and emax == 1.5 and fl.tolist() == [False, True, False, False]
+    # a hit adds the suffix rows at conf >= tau_s (rows 8 and 10), after the block
+    pos, tok, emax, _ = ps.drift_commit(rows, cur, srows, suf, committed, 0.75, 2.0, D, hs, hc, True)
+    assert pos == [5, 8, 10] and tok == [101, 100, 102] and emax == 2.5
+    # no drift, or alpha = inf: the threshold commit
+    rng = np.random.default_rng(15)
+    for trial in range(20):
+        conf = rng.random(4) * 0.9
+        if trial % 3 == 0:
+            conf[rng.integers(0, 4)] = 0.95
+        c2 = np.zeros(L, bool)
+        c2[rows[rng.random(4) < 0.3]] = True
+        if c2[rows].all():
+            c2[rows[0]] = False
+        st_ = stats(conf, rng.random(4) * 3, rng.integers(0, 50, 4))
+        want = thr_commit(rows, st_["conf"], st_["argmax"], st_["entropy"], c2, 0.9)
+        Dr = rng.random(4) * 5
+        for d_, alpha in ((None, 1.0), (Dr, math.inf)):
+            got = ps.drift_commit(rows, st_, srows, suf, c2, 0.9, alpha, d_, np.ones(4), np.ones(4, np.int64),
+                                  False)
+            assert (got[0], got[1], got[2]) == (list(want[0]), list(want[1]), want[2])
+        # alpha = 0: exactly the positive deltas among the masked rows (or the fallback)
+        hsum, hcnt = rng.random(4) * 4, np.array([2, 0, 1, 3])
+        got = ps.drift_commit(rows, st_, srows, suf, c2, 0.9, 0.0, Dr, hsum, hcnt, False)
+        exp_ = [int(rows[j]) for j in range(4) if not c2[rows[j]] and
+                (st_["conf"][j] >= 0.9 or (hcnt[j] > 0 and Dr[j] - hsum[j] / hcnt[j] > 0.0))]
+        if exp_:
+            assert got[0] == exp_
+        else:
+            assert got[0] == list(want[0])
+        # raising alpha never adds a commit
+        prev_set = set(got[0])
+        for alpha in (0.5, 2.0, 10.0, 1e6):
+            g2 = ps.drift_commit(rows, st_, srows, suf, c2, 0.9, alpha, Dr, hsum, hcnt, False)
+            if len(g2[0]) > 1 or not exp_:
+                assert set(g2[0]) <= prev_set | set(want[0])
+            prev_set = set(g2[0]) if g2[0] else prev_set
+    # suffix hit: window [10, 22), block [14, 18): rows 18.. are the suffix part
+    a = np.array([0, 1, 2, 0, 1, 2, 3, 3, 1, 2, 3, 0])
+    assert ps.suffix_hit(14, 4, 10, a, [3]) is True      # rows 18..21 -> clusters 1, 2, 3, 0
+    assert ps.suffix_hit(14, 4, 10, a, [1]) is True
+    assert ps.suffix_hit(14, 4, 10, a[:8], [3]) is False  # no row after the block
+    assert ps.suffix_hit(14, 4, 10, np.array([0, 0, 0, 0, 3, 3, 3, 3, 0, 0, 0, 0]), [3]) is False
+    assert ps.token_drift([14, 15], 10, a, np.array([1.0, 2.0, 3.0, 4.0])).tolist() == [2.0, 3.0]
+    # decode: history accumulates within a block and restarts when it advances
+    from oracle.decode import Policy, SeqState, commit_block_polestar
+    from sparse_kv_cache_value_amd import configs
+    from helpers import spec_of as _spec
+    cfg = configs.C1.with_(seq_len=64, prompt_len=32, block_len=16, d_model=32, n_q_heads=2, n_kv_heads=2,
+                           head_dim=16, d_ffn=64, vocab=32, proxy_rank=8, n_layers=1)
+    spec = _spec(cfg, gemm64=True)
+    _, head = model_np(cfg, gain_std=0.2)
+    toks = np.zeros(64, np.int64)
+    cm = np.zeros(64, bool)
+    cm[:32] = True
+    sq = SeqState(spec, toks, cm)
+    sq.H[1] = rng.standard_normal((64, 32))
+    pol = Policy(rho=(0.5,), conf_threshold=2.0, commit="polestar", commit_alpha=1e9)
+    last = {"valid": True, "wstart": 16, "assign": np.zeros(48, np.int64), "kl": np.full(16, 0.25),
+            "top": np.array([1])}
+    r = commit_block_polestar(sq, head, spec, pol, last)
+    assert len(r["pos"]) == 1 and sq.block_start == 32 and sq.drift_cnt[:16].tolist() == [1] * 16
+    assert np.all(sq.drift_sum[:16] == 0.25) and not r["hit"]
+    r = commit_block_polestar(sq, head, spec, pol, None)  # a full step: no drift, no history change
+    assert r["D"] is None and sq.drift_cnt[:16].tolist() == [1] * 16
+    for _ in range(14):
+        commit_block_polestar(sq, head, spec, pol, last)
+    assert sq.block_start == 48 and np.all(sq.drift_cnt == 0) and np.all(sq.drift_sum == 0.0)
+
+
 ALL_CHECKS = [
     check_brute_layer, check_brute_decisions, check_all_rows_equals_dense,
     check_empty_set_noop, check_fixed_point, check_drift_closed_forms,
     check_entropy_closed_forms, check_proxy_basis, check_gqa_is_repeated_mha,
     check_permutation_equivariance, check_selection_structure, check_budget_table,
     check_decode_structure, check_fp8_fp4_codecs, check_spherical_kmeans, check_proxy_attention_and_kl,
-    check_polestar_selection,
+    check_polestar_selection, check_polestar_commit,
 ]

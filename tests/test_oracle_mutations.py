@@ -219,8 +219,74 @@ def m_top_clusters_high_ties(monkeypatch):
     monkeypatch.setattr(ops, "top_clusters", bad)
 
 
+def _drift_commit_variant(monkeypatch, rule):
+    """Replace the drift test of Polestar-Commit by ``rule(delta, c, tau_s,
+    alpha)``; everything else as in the oracle."""
+    orig = ops.drift_commit
+
+    def bad(cur_rows, cur, suf_rows, suf, committed, tau_s, alpha, D, hist_sum, hist_cnt, hit):
+        n = len(cur_rows)
+        cand = [j for j in range(n) if not committed[cur_rows[j]]]
+        pick = []
+        for j in cand:
+            c = float(cur["conf"][j])
+            if c >= tau_s:
+                pick.append(j)
+            elif D is not None and hist_cnt[j] > 0:
+                if rule(float(D[j]) - float(hist_sum[j]) / float(hist_cnt[j]), c, tau_s, alpha):
+                    pick.append(j)
+        if not pick:
+            return orig(cur_rows, cur, suf_rows, suf, committed, tau_s, alpha, None, hist_sum, hist_cnt, hit)
+        pick.sort()
+        spick = [j for j in range(len(suf_rows)) if hit and not committed[suf_rows[j]] and suf["conf"][j] >= tau_s]
+        pos = [int(cur_rows[j]) for j in pick] + [int(suf_rows[j]) for j in spick]
+        tok = [int(cur["argmax"][j]) for j in pick] + [int(suf["argmax"][j]) for j in spick]
+        ents = [float(cur["entropy"][j]) for j in pick] + [float(suf["entropy"][j]) for j in spick]
+        fl = np.zeros(n, bool)
+        fl[pick] = True
+        return pos, tok, max(ents, default=0.0), fl
+    monkeypatch.setattr(ops, "drift_commit", bad)
+
+
+def m_commit_threshold_not_squared(monkeypatch):
+    _drift_commit_variant(monkeypatch, lambda dl, c, ts, a: dl > a * (ts - c))
+
+
+def m_commit_nonstrict(monkeypatch):
+    _drift_commit_variant(monkeypatch, lambda dl, c, ts, a: dl >= a * (ts - c) ** 2)
+
+
+def m_commit_raw_drift(monkeypatch):
+    # the drift itself instead of its deviation from the historical mean
+    orig = ops.drift_commit
+
+    def bad(cur_rows, cur, suf_rows, suf, committed, tau_s, alpha, D, hist_sum, hist_cnt, hit):
+        return orig(cur_rows, cur, suf_rows, suf, committed, tau_s, alpha, D, np.zeros_like(hist_sum),
+                    hist_cnt, hit)
+    monkeypatch.setattr(ops, "drift_commit", bad)
+
+
+def m_suffix_any_conf(monkeypatch):
+    orig = ops.drift_commit
+
+    def bad(cur_rows, cur, suf_rows, suf, committed, tau_s, alpha, D, hist_sum, hist_cnt, hit):
+        s2 = dict(suf)
+        s2["conf"] = np.maximum(np.asarray(suf["conf"], np.float64), tau_s)
+        return orig(cur_rows, cur, suf_rows, s2, committed, tau_s, alpha, D, hist_sum, hist_cnt, hit)
+    monkeypatch.setattr(ops, "drift_commit", bad)
+
+
+def m_suffix_hit_includes_block(monkeypatch):
+    def bad(block_start, blk, wstart, assign, top):
+        a = np.asarray(assign)
+        first = block_start - wstart  # the current block counted as suffix
+        return any(int(a[r]) in set(int(t) for t in top) for r in range(max(first, 0), a.size))
+    monkeypatch.setattr(ops, "suffix_hit", bad)
+
+
 MUTATIONS += [m_fp_ties_up, m_kmeans_mean_not_normalised, m_kl_reversed, m_window_unclamped,
-              m_proxy_attention_unscaled, m_top_clusters_high_ties]
+              m_proxy_attention_unscaled, m_top_clusters_high_ties, m_commit_threshold_not_squared,
+              m_commit_nonstrict, m_commit_raw_drift, m_suffix_any_conf, m_suffix_hit_includes_block]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
