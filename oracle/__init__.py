@@ -24,4 +24,4 @@ function's docstring.
 """
 
 from .model import *  # noqa: F401,F403
-from . import model, decode, brute, budget, polestar  # noqa: F401
+from . import model, decode, brute, budget, polestar, extrapolation  # noqa: F401

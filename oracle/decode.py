@@ -15,6 +15,8 @@ Readings (where the pages leave the step open):
 * Forced sets: "block+recent" = every row of the current block plus the last
   ``recent_k`` entries of the decode history (EntropyCache); "block" = the
   current block (Polestar); "none" = drift alone (SPA-Cache).
+* Confidence Extrapolation (TSPD + CE page, section 2) optionally adds early
+  commits to the threshold commit (``extrapolation.ce_commit``).
 * Commit rule: "threshold" (static confidence threshold) or "polestar"
   (Polestar section 2B, see ``polestar.drift_commit``; it needs the Polestar
   drift path and uses its last layer's cluster drift).
@@ -29,7 +31,7 @@ import numpy as np
 
 from .model import (Spec, budget_k, commit, drift, lm_stats, proxy, select,
                     sparse_layer)
-from . import polestar
+from . import extrapolation, polestar
 
 
 @dataclasses.dataclass
@@ -43,6 +45,7 @@ class Policy:
     polestar: polestar.PolestarParams = dataclasses.field(default_factory=polestar.PolestarParams)
     commit: str = "threshold"       # or "polestar" (Polestar section 2B)
     commit_alpha: float = 1.0       # Polestar-Commit alpha
+    ce: Optional[extrapolation.CEParams] = None  # Confidence Extrapolation on the threshold commit
 
 
 class SeqState:
@@ -66,6 +69,8 @@ class SeqState:
         # Polestar-Commit: sum and count of the current block rows' past drifts
         self.drift_sum = np.zeros(spec.block_len, np.float64)
         self.drift_cnt = np.zeros(spec.block_len, np.int64)
+        # Confidence Extrapolation: filter state per current block position
+        self.ce_states = [None] * spec.block_len
 
     def advance_block(self):
         L, b = self.spec.seq_len, self.spec.block_len
@@ -142,16 +147,24 @@ def commit_block(st: SeqState, head, spec: Spec, pol: Policy):
         st.full_next = False
         return {"rows": rows, "stats": None, "pos": [], "tok": [], "emax": 0.0}
     stats = lm_stats(st.H[spec.n_layers][rows], head["final_norm"], head["lm_head"], spec)
-    pos, tok, emax = commit(rows, stats["conf"], stats["argmax"], stats["entropy"],
-                            st.committed, pol.conf_threshold)
+    early = None
+    if pol.ce is not None:
+        pos, tok, emax, early = extrapolation.ce_commit(rows, stats["conf"], stats["argmax"], stats["entropy"],
+                                                        st.committed, pol.conf_threshold, st.ce_states, pol.ce)
+    else:
+        pos, tok, emax = commit(rows, stats["conf"], stats["argmax"], stats["entropy"],
+                                st.committed, pol.conf_threshold)
+    bs = st.block_start
     for p, t in zip(pos, tok):
         st.tokens[p] = t
         st.committed[p] = True
         st.history.append(p)
     st.n_new = len(pos)
     st.advance_block()
+    if st.block_start != bs:
+        st.ce_states = [None] * spec.block_len
     st.full_next = emax > pol.tau
-    return {"rows": rows, "stats": stats, "pos": pos, "tok": tok, "emax": emax}
+    return {"rows": rows, "stats": stats, "pos": pos, "tok": tok, "emax": emax, "early": early}
 
 
 def commit_block_polestar(st: SeqState, head, spec: Spec, pol: Policy, last):

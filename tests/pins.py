@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import math
 import os
+from dataclasses import replace as dataclasses_replace
 
 import numpy as np
 
@@ -600,11 +601,116 @@ def check_polestar_commit():
     assert sq.block_start == 48 and np.all(sq.drift_cnt == 0) and np.all(sq.drift_sum == 0.0)
 
 
+def check_confidence_extrapolation():
+    """P16, Confidence Extrapolation (TSPD + CE page, method section 2).
+
+    - The expanded predict / update / forecast arithmetic equals the matrix
+      form of the Kalman filter (F P F^T + Q; K = P H^T (H P H^T + r)^-1,
+      P = (I - K H) P; F^h P F^hT + sum_k F^k Q F^kT) on random states.
+    - With no velocity (p_v0 = 0, q = 0) the level is the running mean of the
+      observations.
+    - With q = 0 the filter equals the Bayesian least-squares line fit with a
+      N(0, p_v0) prior on the slope (solved by numpy.linalg.solve).
+    - ce_commit reduces to the threshold commit when kappa = inf or
+      gamma > 1; a linear trend 0.6, 0.7, 0.8 commits early at threshold
+      0.95 (forecast 1.0 at h = 2) but not at 1.05; coverage counts the
+      committed block positions to the left."""
+    from oracle import extrapolation as ce
+    from oracle.model import commit as thr_commit
+    rng = np.random.default_rng(16)
+    F = np.array([[1.0, 1.0], [0.0, 1.0]])
+    H = np.array([[1.0, 0.0]])
+    for _ in range(20):
+        p = ce.CEParams(horizon=3, q=float(rng.random() * 1e-2), r=float(rng.random() * 1e-2 + 1e-4))
+        Q = p.q * np.array([[0.25, 0.5], [0.5, 1.0]])
+        A = rng.standard_normal((2, 2)) * 0.1
+        P = A @ A.T + np.eye(2) * 1e-3
+        st = [float(rng.random()), float(rng.standard_normal() * 0.05), P[0, 0], P[0, 1], P[1, 1]]
+        x = np.array(st[:2])
+        Pp = F @ P @ F.T + Q
+        got = ce.kf_predict(st, p)
+        assert np.allclose(got[:2], F @ x, rtol=1e-14, atol=1e-16)
+        assert np.allclose([got[2], got[3], got[4]], [Pp[0, 0], Pp[0, 1], Pp[1, 1]], rtol=1e-13, atol=1e-18)
+        c = float(rng.random())
+        up = ce.kf_update(got, c, p)
+        K = Pp @ H.T / (H @ Pp @ H.T + p.r)
+        xu = F @ x + (K * (c - (F @ x)[0])).ravel()
+        Pu = (np.eye(2) - K @ H) @ Pp
+        assert np.allclose(up[:2], xu, rtol=1e-12, atol=1e-15)
+        assert np.allclose([up[2], up[3], up[4]], [Pu[0, 0], Pu[0, 1], Pu[1, 1]], rtol=1e-11, atol=1e-18)
+        lb = ce.forecast_bounds(up, dataclasses_replace(p, kappa=1.5))
+        xs, Ps = np.array(up[:2]), np.array([[up[2], up[3]], [up[3], up[4]]])
+        for h in range(1, 4):
+            Fh = np.linalg.matrix_power(F, h)
+            Vh = Fh @ Ps @ Fh.T + sum(np.linalg.matrix_power(F, k) @ Q @ np.linalg.matrix_power(F, k).T
+                                      for k in range(h))
+            want = (Fh @ xs)[0] - 1.5 * math.sqrt(Vh[0, 0])
+            assert abs(lb[h - 1] - want) <= 1e-12 * max(1.0, abs(want))
+    # running mean
+    p0 = ce.CEParams(q=0.0, r=1e-3, p_v0=0.0)
+    obs = rng.random(12)
+    s_ = None
+    for t, c in enumerate(obs):
+        s_ = ce.kf_observe(s_, c, p0)
+        assert abs(s_[0] - obs[:t + 1].mean()) <= 1e-13 and s_[1] == 0.0
+    # q = 0: Bayesian least-squares line with a N(0, p_v0) slope prior
+    p1 = ce.CEParams(q=0.0, r=2e-3, p_v0=5e-2)
+    obs = 0.3 + 0.05 * np.arange(10) + rng.standard_normal(10) * 0.03
+    s_ = None
+    for t, c in enumerate(obs):
+        s_ = ce.kf_observe(s_, c, p1)
+        i = np.arange(t + 1, dtype=np.float64)
+        X = np.stack([np.ones_like(i), i], axis=1)
+        N = X.T @ X / p1.r + np.diag([0.0, 1.0 / p1.p_v0])
+        beta = np.linalg.solve(N, X.T @ obs[:t + 1] / p1.r)
+        cov = np.linalg.inv(N)
+        lvl = beta[0] + t * beta[1]
+        var = cov[0, 0] + 2 * t * cov[0, 1] + t * t * cov[1, 1]
+        if t >= 1:
+            assert abs(s_[0] - lvl) <= 1e-10 and abs(s_[1] - beta[1]) <= 1e-10, (t, s_, lvl, beta)
+            assert abs(s_[2] - var) <= 1e-10 * max(var, 1e-12)
+    # commit rule
+    rows = np.arange(8, 12)
+    L = 16
+    for trial in range(20):
+        conf = rng.random(4) * 0.9
+        committed = np.zeros(L, bool)
+        committed[rows[rng.random(4) < 0.3]] = True
+        if committed[rows].all():
+            committed[rows[0]] = False
+        ent, am = rng.random(4), rng.integers(0, 40, 4)
+        want = thr_commit(rows, conf, am, ent, committed, 0.5)
+        for pp in (ce.CEParams(kappa=math.inf), ce.CEParams(gamma=1.5)):
+            states = [None] * 4
+            got = ce.ce_commit(rows, conf, am, ent, committed, 0.5, states, pp)
+            assert (got[0], got[1], got[2]) == (list(want[0]), list(want[1]), want[2]) and not got[3].any()
+    pl = ce.CEParams(horizon=2, q=0.0, r=1e-9, p_v0=10.0, kappa=0.0, gamma=0.5)
+    for thr, want_early in ((0.95, True), (1.05, False)):
+        states = [None] * 4
+        committed = np.zeros(L, bool)
+        committed[8] = True  # row 9 then has coverage 1
+        for c in (0.6, 0.7):
+            ce.ce_commit(rows, np.array([0.0, c, 0.0, 0.0]), np.arange(4), np.zeros(4), committed, thr, states, pl)
+        pos, _, _, early = ce.ce_commit(rows, np.array([0.0, 0.8, 0.1, 0.0]), np.arange(4), np.zeros(4),
+                                        committed, thr, states, pl)
+        assert abs(states[1][0] - 0.8) < 1e-6 and abs(states[1][1] - 0.1) < 1e-6
+        assert bool(early[1]) == want_early and pos == ([9] if want_early else [9])
+        assert (9 in pos)  # early, or the fallback (most confident)
+    # coverage: rows 8, 9 committed; row 11 has 2 of 3 left committed, row 10 has 2 of 2
+    committed = np.zeros(L, bool)
+    committed[[8, 9]] = True
+    states = [None, None, [0.2, 0.5, 1e-9, 0.0, 1e-9], [0.2, 0.5, 1e-9, 0.0, 1e-9]]
+    pc = ce.CEParams(horizon=1, q=0.0, r=1e-9, p_v0=1e-9, kappa=0.0, gamma=0.7)
+    pos, _, _, early = ce.ce_commit(rows, np.array([1.0, 1.0, 0.2, 0.2]), np.arange(4), np.zeros(4), committed, 0.6,
+                                    states, pc)
+    assert early.tolist() == [False, False, True, False] and pos == [10]
+
+
 ALL_CHECKS = [
     check_brute_layer, check_brute_decisions, check_all_rows_equals_dense,
     check_empty_set_noop, check_fixed_point, check_drift_closed_forms,
     check_entropy_closed_forms, check_proxy_basis, check_gqa_is_repeated_mha,
     check_permutation_equivariance, check_selection_structure, check_budget_table,
     check_decode_structure, check_fp8_fp4_codecs, check_spherical_kmeans, check_proxy_attention_and_kl,
-    check_polestar_selection, check_polestar_commit,
+    check_polestar_selection, check_polestar_commit, check_confidence_extrapolation,
 ]

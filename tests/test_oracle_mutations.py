@@ -293,3 +293,69 @@ MUTATIONS += [m_fp_ties_up, m_kmeans_mean_not_normalised, m_kl_reversed, m_windo
 def test_mutation_is_caught(monkeypatch, mutation):
     mutation(monkeypatch)
     assert _fails(pins.ALL_CHECKS), f"no pin catches {mutation.__name__}"
+
+
+# ---- Confidence Extrapolation ----
+import oracle.extrapolation as oce  # noqa: E402
+
+
+def m_ce_predict_drops_quarter_q(monkeypatch):
+    def bad(s, p):
+        x0, x1, a, b, d = s
+        return [x0 + x1, x1, a + 2.0 * b + d, b + d + p.q / 2.0, d + p.q]
+    monkeypatch.setattr(oce, "kf_predict", bad)
+
+
+def m_ce_gain_swapped(monkeypatch):
+    def bad(s, c, p):
+        x0, x1, a, b, d = s
+        S = a + p.r
+        k0, k1 = b / S, a / S
+        y = float(c) - x0
+        return [x0 + k0 * y, x1 + k1 * y, a - k0 * a, b - k0 * b, d - k1 * b]
+    monkeypatch.setattr(oce, "kf_update", bad)
+
+
+def m_ce_forecast_not_propagated(monkeypatch):
+    def bad(s, p):
+        x0, x1, a, b, d = s
+        return [x0 + h * x1 - p.kappa * math.sqrt(a) for h in range(1, p.horizon + 1)]
+    monkeypatch.setattr(oce, "forecast_bounds", bad)
+
+
+def m_ce_coverage_counts_self(monkeypatch):
+    orig = oce.ce_commit
+
+    def bad(rows, conf, argmax, entropy, committed, threshold, states, p):
+        # coverage over the positions up to and including the token
+        n = len(rows)
+        cand = [j for j in range(n) if not committed[rows[j]]]
+        for j in cand:
+            states[j] = oce.kf_observe(states[j], conf[j], p)
+        early = np.zeros(n, bool)
+        pick = []
+        for j in cand:
+            if conf[j] >= threshold:
+                pick.append(j)
+                continue
+            cov = sum(1 for i in range(j) if committed[rows[i]]) / (j + 1)
+            if cov >= p.gamma and max(oce.forecast_bounds(states[j], p)) >= threshold:
+                pick.append(j)
+                early[j] = True
+        if not pick and cand:
+            best = max(cand, key=lambda j: (conf[j], -j))
+            pick = [best]
+        pick.sort()
+        return ([int(rows[j]) for j in pick], [int(argmax[j]) for j in pick],
+                max((float(entropy[j]) for j in pick), default=0.0), early)
+    monkeypatch.setattr(oce, "ce_commit", bad)
+
+
+CE_MUTATIONS = [m_ce_predict_drops_quarter_q, m_ce_gain_swapped, m_ce_forecast_not_propagated,
+                m_ce_coverage_counts_self]
+
+
+@pytest.mark.parametrize("mutation", CE_MUTATIONS, ids=lambda f: f.__name__)
+def test_ce_mutation_is_caught(monkeypatch, mutation):
+    mutation(monkeypatch)
+    assert _fails(pins.ALL_CHECKS), f"no pin catches {mutation.__name__}"
