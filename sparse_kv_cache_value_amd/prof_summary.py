@@ -39,8 +39,9 @@ def _name(s: str) -> str:
 
 
 def _steps(rows, key_start, key_end, name_key, nsteps):
+    # a step ends with its commit kernel
     ks = sorted(rows, key=lambda r: int(r[key_start]))
-    ends = [i for i, r in enumerate(ks) if "lm_merge" in r[name_key]]
+    ends = [i for i, r in enumerate(ks) if "commit_kernel" in r[name_key]]
     if len(ends) < nsteps + 1:
         raise SystemExit(f"trace has {len(ends)} steps, need {nsteps + 1}")
     sel = ends[-nsteps - 1:]
@@ -59,7 +60,9 @@ def kernels(path: str, nsteps: int = 10) -> str:
             agg[n][0] += 1
             agg[n][1] += d
             busy += d
-    span = (int(ks[sel[-1]]["End_Timestamp"]) - int(ks[sel[0]]["End_Timestamp"])) / 1e3
+    # from the first kernel of the first selected step (the host work between
+    # bench passes before it is not part of the steps)
+    span = (int(ks[sel[-1]]["End_Timestamp"]) - int(ks[sel[0] + 1]["Start_Timestamp"])) / 1e3
     out = [f"steps {nsteps}: span/step {span / nsteps:.1f} us, kernel busy/step {busy / nsteps:.1f} us, "
            f"gaps/step {(span - busy) / nsteps:.1f} us",
            f"{'kernel':64s} {'launches/step':>13s} {'avg_us':>8s} {'us/step':>9s}"]
@@ -100,7 +103,14 @@ def traffic(fetch_csv: str, write_csv: str, nsteps: int = 3) -> dict:
         rec[counter] = {"kib_per_launch": sum(vals) / len(vals), "launches": len(vals), "copy_factor": factor}
     fetch = rec["FETCH_SIZE"]["kib_per_launch"] * 1024 / rec["FETCH_SIZE"]["copy_factor"]
     write = rec["WRITE_SIZE"]["kib_per_launch"] * 1024 / rec["WRITE_SIZE"]["copy_factor"]
-    return {"kernel_class": "gemm (layer GEMMs + LM head)", "steps": nsteps, "counters": rec,
+    run = ("rocprofv3 --pmc {c} --kernel-include-regex 'gemm|lm_merge|elementwise' --output-format csv "
+           "-d <out_{c}> -o run -- python3 bench.py --steps 3 --warmup 1 --full-steps 0 --no-cpu-baseline "
+           "--no-other-configs --copy-calibration")
+    cmds = [run.format(c="FETCH_SIZE"), run.format(c="WRITE_SIZE"),
+            "python -m sparse_kv_cache_value_amd.prof_summary traffic <out_FETCH_SIZE>/run_counter_collection.csv "
+            "<out_WRITE_SIZE>/run_counter_collection.csv 3"]
+    return {"commands (from /tmp, TMPDIR=/tmp)": cmds,
+            "kernel_class": "gemm (layer GEMMs + LM head)", "steps": nsteps, "counters": rec,
             "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
             "traffic_bytes_per_launch": round(fetch + write), "source_hash": gemm_source_hash()}
 
