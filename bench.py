@@ -130,8 +130,12 @@ WORKLOADS = {
                  "LM head over the current and next block",
 }
 
+WORKLOADS["C2-ce"] = ("C2 with Confidence Extrapolation on the threshold commit (horizon 2, q = 1e-4, r = 1e-3, "
+                      "p_v0 = 1e-2, kappa = 2, gamma = 0.5)")
+
 # the config object behind each name
-CONFIG_OF = {"C5-commit": lambda c: c.C5.with_(polestar_commit=True, commit_alpha=1.0)}
+CONFIG_OF = {"C5-commit": lambda c: c.C5.with_(polestar_commit=True, commit_alpha=1.0),
+             "C2-ce": lambda c: c.C2.with_(ce_horizon=2)}
 
 
 def class_table(prof, steps, achievable, ms_per_step):
@@ -181,17 +185,18 @@ def bench_config(name, steps, warmup, achievable=None):
     model = runtime.Model(cfg, "cuda")
     st = runtime.State(cfg)
     ps = runtime.PolestarState(cfg) if cfg.score == configs.SCORE_POLESTAR else None
+    cs = runtime.CEState(cfg) if cfg.ce_horizon > 0 else None
     stream = torch.cuda.current_stream()
-    runtime.step(model, st, mode=B.DLLM_MODE_FULL, polestar_state=ps)
+    runtime.step(model, st, mode=B.DLLM_MODE_FULL, polestar_state=ps, ce_state=cs)
     for _ in range(warmup):
-        runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps)
+        runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps, ce_state=cs)
     torch.cuda.synchronize()
     def run(classes):
         nh = int(st.n_history.sum())
         B.dllm_profile(model.h, True, classes)
         t0 = time.perf_counter()
         for _ in range(steps):
-            runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps)
+            runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False, polestar_state=ps, ce_state=cs)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         prof = B.dllm_profile_read(model.h)
@@ -203,7 +208,7 @@ def bench_config(name, steps, warmup, achievable=None):
     wall, tokens, prof = run(["gemm", "lm_head"])
     wall_all, _, prof_all = run(None)
     model.close()
-    del st, ps, model
+    del st, ps, cs, model
     torch.cuda.empty_cache()
     ms = 1e3 * wall / steps
     classes = class_table(prof_all, steps, achievable, 1e3 * wall_all / steps)
@@ -384,7 +389,8 @@ def main():
     if not args.no_other_configs:
         # the other configs of the scope table, a few sparse steps each
         out["other_configs"] = {}
-        for name, n, w in (("C1", 20, 3), ("C2", 20, 3), ("C4", 8, 2), ("C5", 8, 2), ("C5-commit", 8, 2)):
+        for name, n, w in (("C1", 20, 3), ("C2", 20, 3), ("C2-ce", 20, 3), ("C4", 8, 2), ("C5", 8, 2),
+                           ("C5-commit", 8, 2)):
             out["other_configs"][name] = bench_config(name, n, w, achievable)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -156,6 +156,31 @@ typedef struct {
                             defined (window unchanged); the Polestar commit clears it */
 } dllm_polestar_state;
 
+/* Confidence Extrapolation (TSPD + CE page, method section 2) on top of the
+ * threshold commit: a constant-velocity Kalman filter (fp64) on each masked
+ * current-block row's top-1 confidence, state (level, velocity), transition
+ * [[1,1],[0,1]] per step, process noise q [[1/4,1/2],[1/2,1]], observation
+ * noise r; first observation: state (c, 0), covariance diag(r, p_v0).  A
+ * masked row commits early when its left-context coverage (share of the
+ * block rows to its left committed before this step; 1 for the block's first
+ * row) is >= gamma and, for some h in 1..horizon, the forecast level minus
+ * kappa standard deviations is >= the commit threshold. */
+typedef struct {
+  int32_t horizon;       /* look-ahead steps H, 1..64 */
+  double q;              /* process noise scale (>= 0) */
+  double r;              /* observation noise variance (> 0) */
+  double p_v0;           /* initial velocity variance (>= 0) */
+  double kappa;          /* lower bound = mean - kappa * sd (>= 0, +inf: no early commit) */
+  double gamma;          /* minimum left-context coverage */
+} dllm_ce_params;
+
+/* Caller-owned filter state of the current block's rows (initialise to zero;
+ * a block's states are dropped when it advances). */
+typedef struct {
+  double *kf;            /* [B][block_len][5] level, velocity, P00, P01, P11 */
+  int32_t *has;          /* [B][block_len] 1 when kf holds a state */
+} dllm_ce_state;
+
 typedef struct {
   int32_t mode;          /* DLLM_MODE_*; AUTO reads state.full_next (one host wait) */
   int32_t forced_rule;   /* DLLM_FORCED_* */
@@ -166,6 +191,9 @@ typedef struct {
   int32_t score;         /* DLLM_SCORE_* */
   const dllm_polestar_params *polestar;   /* host; DLLM_SCORE_POLESTAR_KL only */
   dllm_polestar_state *polestar_state;    /* DLLM_SCORE_POLESTAR_KL only */
+  const dllm_ce_params *ce;               /* host; non-NULL: commit with Confidence Extrapolation
+                                             (dllm_commit_ce); not with Polestar-Commit */
+  dllm_ce_state *ce_state;                /* with ce */
 } dllm_step_params;
 
 typedef struct {
@@ -248,6 +276,16 @@ dllm_status dllm_lm_head(dllm_model *m, const dllm_state *s, double *stats_out,
  * advances block_start past fully committed blocks. */
 dllm_status dllm_commit(dllm_model *m, dllm_state *s, double conf_threshold, double tau,
                         void *stream);
+
+/* dllm_commit with Confidence Extrapolation (see dllm_ce_params): the LM-head
+ * statistics of the current block, the filter update of its masked rows, then
+ * a masked row commits at conf >= conf_threshold or early by extrapolation;
+ * if none does, the most confident masked row (lowest position on ties).
+ * History, entropy gate and block advance as in dllm_commit.  Errors:
+ * DLLM_E_ARG for NULL pointers, NaN thresholds, horizon outside 1..64, r <= 0,
+ * or a negative q, p_v0 or kappa. */
+dllm_status dllm_commit_ce(dllm_model *m, dllm_state *s, const dllm_ce_params *ce, dllm_ce_state *ce_state,
+                           double conf_threshold, double tau, void *stream);
 
 /* Polestar-Cache drift path at `layer` (Polestar, section 2A), per sequence:
  * window rows [ws, ws + W), ws = clamp(block_start - block_len, 0, L - W);

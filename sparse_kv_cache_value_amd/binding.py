@@ -53,11 +53,20 @@ class DllmPolestarState(ctypes.Structure):
         "drift_sum", "drift_cnt", "drift_valid")]
 
 
+class DllmCEParams(ctypes.Structure):
+    _fields_ = [("horizon", _i32), ("q", _f64), ("r", _f64), ("p_v0", _f64), ("kappa", _f64), ("gamma", _f64)]
+
+
+class DllmCEState(ctypes.Structure):
+    _fields_ = [("kf", _vp), ("has", _vp)]
+
+
 class DllmStepParams(ctypes.Structure):
     _fields_ = [("mode", _i32), ("forced_rule", _i32), ("recent_k", _i32), ("tau", _f64),
                 ("conf_threshold", _f64), ("rho_h", ctypes.POINTER(_f64)), ("score", _i32),
                 ("polestar", ctypes.POINTER(DllmPolestarParams)),
-                ("polestar_state", ctypes.POINTER(DllmPolestarState))]
+                ("polestar_state", ctypes.POINTER(DllmPolestarState)),
+                ("ce", ctypes.POINTER(DllmCEParams)), ("ce_state", ctypes.POINTER(DllmCEState))]
 
 
 class DllmStepResult(ctypes.Structure):
@@ -86,6 +95,8 @@ SIGNATURES = {
     "dllm_sparse_layer": (_i32, [_vp, _i32, ctypes.POINTER(DllmState), _vp, _vp, _i32, _vp]),
     "dllm_lm_head": (_i32, [_vp, ctypes.POINTER(DllmState), _vp, _vp, _vp]),
     "dllm_commit": (_i32, [_vp, ctypes.POINTER(DllmState), _f64, _f64, _vp]),
+    "dllm_commit_ce": (_i32, [_vp, ctypes.POINTER(DllmState), ctypes.POINTER(DllmCEParams),
+                              ctypes.POINTER(DllmCEState), _f64, _f64, _vp]),
     "dllm_forced_set": (_i32, [_vp, ctypes.POINTER(DllmState), _i32, _i32, _vp, _vp]),
     "dllm_polestar_drift": (_i32, [_vp, _i32, ctypes.POINTER(DllmState), ctypes.POINTER(DllmPolestarState),
                                    ctypes.POINTER(DllmPolestarParams), _vp]),
@@ -197,6 +208,11 @@ def dllm_commit(m: int, state, conf_threshold: float, tau: float, stream=None):
     _check(lib().dllm_commit(m, ctypes.byref(state.c), float(conf_threshold), float(tau), _stream(stream)))
 
 
+def dllm_commit_ce(m: int, state, ce: DllmCEParams, ce_state, conf_threshold: float, tau: float, stream=None):
+    _check(lib().dllm_commit_ce(m, ctypes.byref(state.c), ctypes.byref(ce), ctypes.byref(ce_state.c),
+                                float(conf_threshold), float(tau), _stream(stream)))
+
+
 def dllm_forced_set(m: int, state, rule: int, recent_k: int, forced, stream=None):
     _check(lib().dllm_forced_set(m, ctypes.byref(state.c), rule, recent_k, _p(forced), _stream(stream)))
 
@@ -219,12 +235,15 @@ def dllm_polestar_commit(m: int, state, ps, params: DllmPolestarParams, conf_thr
 
 def dllm_step(m: int, state, mode: int, forced_rule: int, recent_k: int, tau: float, conf_threshold: float,
               rho, want_result: bool = True, stream=None, score: int = DLLM_SCORE_SPA_COS,
-              polestar: Optional[DllmPolestarParams] = None, polestar_state=None) -> Optional[DllmStepResult]:
+              polestar: Optional[DllmPolestarParams] = None, polestar_state=None,
+              ce: Optional[DllmCEParams] = None, ce_state=None) -> Optional[DllmStepResult]:
     rho_arr = (_f64 * len(rho))(*[float(r) for r in rho])
     p = DllmStepParams(mode, forced_rule, recent_k, float(tau), float(conf_threshold),
                        ctypes.cast(rho_arr, ctypes.POINTER(_f64)), score,
                        ctypes.pointer(polestar) if polestar is not None else None,
-                       ctypes.pointer(polestar_state.c) if polestar_state is not None else None)
+                       ctypes.pointer(polestar_state.c) if polestar_state is not None else None,
+                       ctypes.pointer(ce) if ce is not None else None,
+                       ctypes.pointer(ce_state.c) if ce_state is not None else None)
     res = DllmStepResult() if want_result else None
     _check(lib().dllm_step(m, ctypes.byref(state.c), ctypes.byref(p),
                            ctypes.byref(res) if res is not None else None, _stream(stream)))

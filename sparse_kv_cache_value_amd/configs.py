@@ -89,6 +89,13 @@ class Config:
     top_clusters: int = 4
     polestar_commit: bool = False   # Polestar-Commit (Polestar section 2B) instead of the threshold commit
     commit_alpha: float = 1.0
+    # Confidence Extrapolation (TSPD + CE section 2) on the threshold commit; horizon 0 = off
+    ce_horizon: int = 0
+    ce_q: float = 1e-4
+    ce_r: float = 1e-3
+    ce_p_v0: float = 1e-2
+    ce_kappa: float = 2.0
+    ce_gamma: float = 0.5
     # C2-style stale cache
     stale_frac: float = 0.0
     stale_std: float = 0.0

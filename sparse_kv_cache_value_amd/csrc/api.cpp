@@ -385,6 +385,27 @@ dllm_status do_commit(dllm_model* m, dllm_state* s, double thr, double tau, hipS
   return DLLM_OK;
 }
 
+dllm_status check_ce(const dllm_model* m, const dllm_ce_params* ce, const dllm_ce_state* cs) {
+  if (!ce || !cs || !cs->kf || !cs->has) return fail(DLLM_E_ARG, "CE params/state is NULL");
+  if (ce->horizon < 1 || ce->horizon > 64) return fail(DLLM_E_ARG, "CE horizon must be in [1, 64]");
+  if (!(ce->r > 0.0) || !(ce->q >= 0.0) || !(ce->p_v0 >= 0.0) || !(ce->kappa >= 0.0) || std::isnan(ce->gamma))
+    return fail(DLLM_E_ARG, "CE needs r > 0, q, p_v0, kappa >= 0 and a gamma");
+  if (m->d.block_len > 64) return fail(DLLM_E_UNSUPPORTED, "CE needs block_len <= 64");
+  return DLLM_OK;
+}
+
+dllm_status do_commit_ce(dllm_model* m, dllm_state* s, const dllm_ce_params* ce, dllm_ce_state* cs, double thr,
+                         double tau, hipStream_t st) {
+  CHK(do_lm_head(m, s, st));
+  const dllm_dims& d = m->d;
+  Prof prof(m, st, DLLM_PROF_DECIDE, (double)s->batch * d.block_len * (32.0 + 4.0 + 1.0 + 44.0), 0.0);
+  HIPCHK(launch_ce_commit(st, s->batch, d.seq_len, d.block_len, thr, tau, ce->horizon, ce->q, ce->r, ce->p_v0,
+                          ce->kappa, ce->gamma, m->lm_stats, cs->kf, cs->has, s->tokens, s->committed, s->history,
+                          s->n_history, s->n_new, s->block_start, s->full_next, s->max_entropy));
+  prof.done();
+  return DLLM_OK;
+}
+
 dllm_status do_polestar_commit(dllm_model* m, dllm_state* s, dllm_polestar_state* ps, const dllm_polestar_params* p,
                                double thr, double tau, hipStream_t st) {
   CHK(do_lm_head(m, s, st, 2));
@@ -758,6 +779,16 @@ dllm_status dllm_commit(dllm_model* m, dllm_state* s, double conf_threshold, dou
   return do_commit(m, s, conf_threshold, tau, S(stream));
 }
 
+dllm_status dllm_commit_ce(dllm_model* m, dllm_state* s, const dllm_ce_params* ce, dllm_ce_state* ce_state,
+                           double conf_threshold, double tau, void* stream) {
+  CHK(check_model(m));
+  CHK(check_state(m, s, false));
+  CHK(check_ce(m, ce, ce_state));
+  if (!m->head_ready) return fail(DLLM_E_STATE, "head weights not initialised");
+  if (std::isnan(conf_threshold) || std::isnan(tau)) return fail(DLLM_E_ARG, "threshold is NaN");
+  return do_commit_ce(m, s, ce, ce_state, conf_threshold, tau, S(stream));
+}
+
 dllm_status dllm_polestar_commit(dllm_model* m, dllm_state* s, dllm_polestar_state* ps,
                                  const dllm_polestar_params* p, double conf_threshold, double tau, void* stream) {
   CHK(check_model(m));
@@ -814,6 +845,11 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     return fail(DLLM_E_ARG, "unknown score %d", p->score);
   const bool polestar = p->score == DLLM_SCORE_POLESTAR_KL;
   if (polestar) CHK(check_polestar(m, s, p->polestar_state, p->polestar));
+  if (p->ce) {
+    CHK(check_ce(m, p->ce, p->ce_state));
+    if (polestar && p->polestar->drift_commit)
+      return fail(DLLM_E_ARG, "Confidence Extrapolation and Polestar-Commit are exclusive");
+  }
   const dllm_dims& d = m->d;
   for (int l = 0; l < d.n_layers; ++l) {
     CHK(check_layer(m, l));
@@ -853,6 +889,8 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     }
     if (p->polestar->drift_commit)
       CHK(do_polestar_commit(m, s, p->polestar_state, p->polestar, p->conf_threshold, p->tau, st));
+    else if (p->ce)
+      CHK(do_commit_ce(m, s, p->ce, p->ce_state, p->conf_threshold, p->tau, st));
     else
       CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
     return finish_step(m, s, res_h, st);
@@ -876,6 +914,8 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
   }
   if (polestar && p->polestar->drift_commit)
     CHK(do_polestar_commit(m, s, p->polestar_state, p->polestar, p->conf_threshold, p->tau, st));
+  else if (p->ce)
+    CHK(do_commit_ce(m, s, p->ce, p->ce_state, p->conf_threshold, p->tau, st));
   else
     CHK(do_commit(m, s, p->conf_threshold, p->tau, st));
   return finish_step(m, s, res_h, st);

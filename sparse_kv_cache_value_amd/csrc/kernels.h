@@ -108,6 +108,11 @@ hipError_t launch_commit(hipStream_t st, int B, int L, int blk, double thr, doub
                          const double* stats, int32_t* tokens, uint8_t* committed, int32_t* history,
                          int32_t* n_history, int32_t* n_new, int32_t* block_start, uint8_t* full_next,
                          double* max_entropy);
+// Threshold commit with Confidence Extrapolation; kf [B][blk][5], has [B][blk].
+hipError_t launch_ce_commit(hipStream_t st, int B, int L, int blk, double thr, double tau, int horizon, double q,
+                            double r, double p_v0, double kappa, double gamma, const double* stats, double* kf,
+                            int32_t* has, int32_t* tokens, uint8_t* committed, int32_t* history, int32_t* n_history,
+                            int32_t* n_new, int32_t* block_start, uint8_t* full_next, double* max_entropy);
 // out: {n_full, n_committed, n_active, pad} int32 then max entropy as double (24 bytes).
 hipError_t launch_step_result(hipStream_t st, int B, const uint8_t* step_full, const int32_t* n_new,
                               const int32_t* block_start, const double* max_entropy, int L, void* out);

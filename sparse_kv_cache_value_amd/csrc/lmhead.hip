@@ -241,6 +241,169 @@ hipError_t launch_commit(hipStream_t st, int B, int L, int blk, double thr, doub
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Threshold commit with Confidence Extrapolation (TSPD + CE page, method
+// section 2).  Lane j is block row j.  Each still-masked row's confidence
+// feeds a constant-velocity Kalman filter (fp64; first observation: state
+// (c, 0), covariance diag(r, p_v0); later: predict with
+// F = [[1,1],[0,1]], Q = q [[1/4,1/2],[1/2,1]], then update with H = [1,0]
+// and noise r).  A masked row commits at conf >= thr, or early when its
+// left-context coverage (share of the block rows to its left committed
+// before this step; 1 for the first row) is >= gamma and for some
+// h = 1..horizon the forecast mean - kappa sd (covariance propagated h steps)
+// is >= thr.  Fallback, history, entropy gate and block advance as in
+// commit_kernel; the block's filter states are dropped when it advances.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void ce_commit_kernel(int L, int blk, double thr, double tau, int horizon, double q,
+                                                       double r, double p_v0, double kappa, double gamma,
+                                                       const double* __restrict__ stats, double* __restrict__ kf,
+                                                       int32_t* __restrict__ has, int32_t* __restrict__ tokens,
+                                                       uint8_t* __restrict__ committed, int32_t* __restrict__ history,
+                                                       int32_t* __restrict__ n_history, int32_t* __restrict__ n_new,
+                                                       int32_t* __restrict__ block_start,
+                                                       uint8_t* __restrict__ full_next,
+                                                       double* __restrict__ max_entropy) {
+  // every product and sum rounded on its own, in the order written (no fused
+  // multiply-add), as the filter equations are stated
+#pragma clang fp contract(off)
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int bs = block_start[b];
+  const int row = bs + lane;
+  const bool valid = bs < L && lane < blk && row < L;
+  uint8_t* cm = committed + (size_t)b * L;
+  double conf = 0.0, ent = 0.0;
+  int tok = 0;
+  bool cand = false;
+  if (valid) {
+    const double* p = stats + ((size_t)b * blk + lane) * 4;
+    conf = 1.0 / p[2];
+    ent = log(p[2]) - p[3] / p[2];
+    tok = (int)p[1];
+    cand = cm[row] == 0;
+  }
+  // filter update of the masked rows
+  double* ks = kf + ((size_t)b * blk + lane) * 5;
+  int32_t* hs = has + (size_t)b * blk + lane;
+  double x0 = 0.0, x1 = 0.0, a = 0.0, bb = 0.0, d = 0.0;
+  if (cand) {
+    if (*hs == 0) {
+      x0 = conf;
+      x1 = 0.0;
+      a = r;
+      bb = 0.0;
+      d = p_v0;
+    } else {
+      x0 = ks[0];
+      x1 = ks[1];
+      a = ks[2];
+      bb = ks[3];
+      d = ks[4];
+      // predict
+      x0 = x0 + x1;
+      a = a + 2.0 * bb + d + q / 4.0;
+      bb = bb + d + q / 2.0;
+      d = d + q;
+      // update
+      const double S = a + r;
+      const double k0 = a / S, k1 = bb / S;
+      const double y = conf - x0;
+      x0 = x0 + k0 * y;
+      x1 = x1 + k1 * y;
+      const double a2 = a - k0 * a, b2 = bb - k0 * bb, d2 = d - k1 * bb;
+      a = a2;
+      bb = b2;
+      d = d2;
+    }
+    ks[0] = x0;
+    ks[1] = x1;
+    ks[2] = a;
+    ks[3] = bb;
+    ks[4] = d;
+    *hs = 1;
+  }
+  // left-context coverage from the rows committed before this step
+  const uint64_t before = __ballot(valid && !cand);
+  const int left = __popcll(before & ((1ull << lane) - 1ull));
+  const double coverage = lane == 0 ? 1.0 : (double)left / (double)lane;
+  bool pick = false;
+  if (cand) {
+    if (conf >= thr) {
+      pick = true;
+    } else if (coverage >= gamma) {
+      double pa = a, pb = bb, pd = d;
+      for (int h = 1; h <= horizon; ++h) {
+        const double na = pa + 2.0 * pb + pd + q / 4.0, nb = pb + pd + q / 2.0, nd = pd + q;
+        pa = na;
+        pb = nb;
+        pd = nd;
+        if (x0 + (double)h * x1 - kappa * sqrt(pa) >= thr) pick = true;
+      }
+    }
+  }
+  const uint64_t any_pick = __ballot(pick);
+  const uint64_t any_cand = __ballot(cand);
+  if (any_pick == 0 && any_cand != 0) {
+    double bc = cand ? conf : -1.0;
+    int br = cand ? row : 0x7fffffff;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double oc = __shfl_xor(bc, o, 64);
+      const int orr = __shfl_xor(br, o, 64);
+      if (oc > bc || (oc == bc && orr < br)) {
+        bc = oc;
+        br = orr;
+      }
+    }
+    pick = cand && row == br;
+  }
+  const uint64_t mask = __ballot(pick);
+  const int cnt = __popcll(mask);
+  const int nh = n_history[b];
+  if (pick) {
+    const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+    tokens[(size_t)b * L + row] = tok;
+    cm[row] = 1;
+    history[(size_t)b * L + nh + rank] = row;
+  }
+  double e = pick ? ent : 0.0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) e = fmax(e, __shfl_xor(e, o, 64));
+  const bool done_row = !valid || !cand || pick;
+  const uint64_t full_mask = __ballot(lane < blk ? done_row : true);
+  int nbs = bs;
+  if (bs < L && full_mask == ~0ull) {
+    nbs = bs + blk;
+    while (nbs < L) {
+      bool c = true;
+      for (int jj = lane; jj < blk; jj += 64) {
+        const int rr = nbs + jj;
+        if (rr < L && cm[rr] == 0) c = false;
+      }
+      if (__ballot(!c) != 0) break;
+      nbs += blk;
+    }
+  }
+  if (nbs != bs && lane < blk) *hs = 0;  // the block's filter states end with it
+  if (lane == 0) {
+    n_history[b] = nh + cnt;
+    n_new[b] = cnt;
+    max_entropy[b] = e;
+    full_next[b] = e > tau ? 1 : 0;
+    block_start[b] = nbs;
+  }
+}
+
+hipError_t launch_ce_commit(hipStream_t st, int B, int L, int blk, double thr, double tau, int horizon, double q,
+                            double r, double p_v0, double kappa, double gamma, const double* stats, double* kf,
+                            int32_t* has, int32_t* tokens, uint8_t* committed, int32_t* history, int32_t* n_history,
+                            int32_t* n_new, int32_t* block_start, uint8_t* full_next, double* max_entropy) {
+  if (blk > 64 || horizon < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ce_commit_kernel, dim3(B), dim3(64), 0, st, L, blk, thr, tau, horizon, q, r, p_v0, kappa, gamma,
+                     stats, kf, has, tokens, committed, history, n_history, n_new, block_start, full_next,
+                     max_entropy);
+  return hipGetLastError();
+}
+
 // out = {sequences run full, tokens committed, sequences still active, 0} then the max entropy.
 __global__ void step_result_kernel(int B, int L, const uint8_t* __restrict__ step_full,
                                    const int32_t* __restrict__ n_new, const int32_t* __restrict__ block_start,

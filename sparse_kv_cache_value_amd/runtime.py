@@ -144,14 +144,37 @@ class PolestarState:
             self.queries, self.kl, self.top, self.drift_sum, self.drift_cnt, self.drift_valid)])
 
 
+def ce_params(cfg: Config) -> B.DllmCEParams:
+    return B.DllmCEParams(cfg.ce_horizon, cfg.ce_q, cfg.ce_r, cfg.ce_p_v0, cfg.ce_kappa, cfg.ce_gamma)
+
+
+class CEState:
+    """Caller-owned Confidence Extrapolation state (include/libdllm.h, dllm_ce_state)."""
+
+    def __init__(self, cfg: Config, batch: Optional[int] = None, device="cuda"):
+        Bn = batch or cfg.batch
+        self.kf = torch.zeros((Bn, cfg.block_len, 5), dtype=torch.float64, device=device)
+        self.has = torch.zeros((Bn, cfg.block_len), dtype=torch.int32, device=device)
+        self.c = B.DllmCEState(self.kf.data_ptr(), self.has.data_ptr())
+
+
 def step(model: Model, state: State, mode: int = B.DLLM_MODE_AUTO, want_result: bool = True, stream=None,
-         tau: Optional[float] = None, polestar_state: Optional[PolestarState] = None):
+         tau: Optional[float] = None, polestar_state: Optional[PolestarState] = None,
+         ce_state: Optional[CEState] = None):
+    """One dllm_step; a config with ce_horizon > 0 commits with Confidence
+    Extrapolation and needs a CEState."""
     cfg = model.cfg
+    ce = None
+    if cfg.ce_horizon > 0:
+        if ce_state is None:
+            raise ValueError("Confidence Extrapolation needs a CEState")
+        ce = ce_params(cfg)
     if cfg.score == SCORE_POLESTAR:
         if polestar_state is None:
             raise ValueError("the Polestar score needs a PolestarState")
         return B.dllm_step(model.h, state, mode, FORCED_RULE[cfg.forced], cfg.recent_k,
                            cfg.tau if tau is None else tau, cfg.conf_threshold, cfg.rho, want_result, stream,
-                           B.DLLM_SCORE_POLESTAR_KL, polestar_params(cfg), polestar_state)
+                           B.DLLM_SCORE_POLESTAR_KL, polestar_params(cfg), polestar_state, ce, ce_state)
     return B.dllm_step(model.h, state, mode, FORCED_RULE[cfg.forced], cfg.recent_k,
-                       cfg.tau if tau is None else tau, cfg.conf_threshold, cfg.rho, want_result, stream)
+                       cfg.tau if tau is None else tau, cfg.conf_threshold, cfg.rho, want_result, stream,
+                       ce=ce, ce_state=ce_state)

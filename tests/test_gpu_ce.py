@@ -1,0 +1,156 @@
+"""Confidence Extrapolation (TSPD + CE page, method section 2) on the GPU
+against the oracle.  After each step, the GPU's own LM-head statistics of
+the step's block are read back (dllm_lm_head on the step's block start: the
+same deterministic kernels the commit ran), and the oracle's filter and
+commit rule run on them from the GPU's filter state before the step.  The
+filter is computed without fused multiply-adds in the order the equations
+are written, so the states and every decision must agree exactly.  The
+config (threshold above every confidence, 64-step horizon, near-noiseless
+filter) makes early commits fire next to the most-confident fallback.  Also:
+dllm_step with CE is bit-for-bit the composition of the entry points, and bad
+parameters are rejected."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import extrapolation as oce
+from gpu_common import Snap, build, medium_cfg, say
+from sparse_kv_cache_value_amd import binding as B
+from sparse_kv_cache_value_amd import runtime
+
+pytestmark = pytest.mark.gpu
+
+CE = medium_cfg(name="medium-ce", seed=41, batch=2, tau=math.inf, conf_threshold=1.3e-3, ce_horizon=64,
+                ce_q=1e-12, ce_r=1e-12, ce_p_v0=1.0, ce_kappa=0.0, ce_gamma=0.0, n_steps=10)
+CE_COV = CE.with_(name="medium-ce-coverage", conf_threshold=1.2e-3, ce_horizon=32, ce_gamma=0.75, ce_kappa=0.5,
+                  ce_q=1e-12, n_steps=16)
+
+
+def _params(cfg):
+    return oce.CEParams(horizon=cfg.ce_horizon, q=cfg.ce_q, r=cfg.ce_r, p_v0=cfg.ce_p_v0, kappa=cfg.ce_kappa,
+                        gamma=cfg.ce_gamma)
+
+
+@pytest.mark.parametrize("cfg", [CE, CE_COV], ids=lambda c: c.name)
+def test_ce_decode_matches_oracle(cfg):
+    model, _, _ = build(cfg)
+    st, cs = runtime.State(cfg), runtime.CEState(cfg)
+    runtime.step(model, st, mode=B.DLLM_MODE_FULL, ce_state=cs)
+    p = _params(cfg)
+    Bn, L, blk = cfg.batch, cfg.seq_len, cfg.block_len
+    stats = torch.zeros((Bn * blk, 4), dtype=torch.float64, device="cuda")
+    n_early = n_blocked = 0
+    for t in range(cfg.n_steps):
+        before = Snap(st)
+        kf0, has0 = cs.kf.cpu().numpy().copy(), cs.has.cpu().numpy().copy()
+        runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, ce_state=cs)
+        after = Snap(st)
+        # the statistics the commit used: LM head on the step's block start
+        bs_after = st.block_start.clone()
+        st.block_start.copy_(torch.from_numpy(before.block_start).cuda())
+        B.dllm_lm_head(model.h, st, stats)
+        st.block_start.copy_(bs_after)
+        S_ = stats.cpu().numpy().reshape(Bn, blk, 4)
+        kf1, has1 = cs.kf.cpu().numpy(), cs.has.cpu().numpy()
+        for b in range(Bn):
+            bs = int(before.block_start[b])
+            if bs >= L:
+                assert after.n_new[b] == 0
+                continue
+            rows = np.arange(bs, min(bs + blk, L))
+            n = rows.size
+            conf = 1.0 / S_[b, :n, 2]
+            ent = np.log(S_[b, :n, 2]) - S_[b, :n, 3] / S_[b, :n, 2]
+            am = S_[b, :n, 1].astype(np.int64)
+            states = [list(kf0[b, j]) if has0[b, j] else None for j in range(blk)]
+            pos, tok, emax, early = oce.ce_commit(rows, conf, am, ent, before.committed[b], cfg.conf_threshold,
+                                                  states, p)
+            got = [int(x) for x in after.history[b][before.n_history[b]:after.n_history[b]]]
+            assert got == pos, f"t={t} b={b}: committed {got} vs oracle {pos}"
+            assert [int(after.tokens[b][x]) for x in pos] == tok
+            assert abs(after.max_entropy[b] - emax) <= 1e-12 * max(1.0, emax)
+            n_early += int(early.sum())
+            # rows whose forecast cleared the threshold but whose coverage did not
+            for j in range(n):
+                if (not before.committed[b][rows[j]]) and conf[j] < cfg.conf_threshold and states[j] is not None:
+                    left = sum(1 for i in range(j) if before.committed[b][rows[i]])
+                    cov = 1.0 if j == 0 else left / j
+                    if cov < p.gamma and max(oce.forecast_bounds(states[j], p)) >= cfg.conf_threshold:
+                        n_blocked += 1
+            nbs = int(after.block_start[b])
+            if nbs != bs:
+                assert not has1[b].any(), f"t={t} b={b}: filter states kept after the block advanced"
+            else:
+                for j in range(n):
+                    if states[j] is None:
+                        assert has1[b, j] == 0
+                    else:
+                        assert has1[b, j] == 1
+                        assert np.array_equal(kf1[b, j], np.array(states[j])), \
+                            f"t={t} b={b} row {rows[j]}: filter {kf1[b, j]} vs {states[j]}"
+            say(f"{cfg.name} t={t} b={b}: committed {pos}, early {np.nonzero(early)[0].tolist()}")
+    say(f"{cfg.name}: {n_early} early commits, {n_blocked} held back by coverage")
+    assert n_early > 0, "no early commit fired"
+    if cfg is CE_COV:
+        assert n_blocked > 0, "coverage never held a commit back"
+    model.close()
+
+
+def test_ce_step_equals_entry_points():
+    cfg = CE
+    model, _, _ = build(cfg)
+    from sparse_kv_cache_value_amd.runtime import FORCED_RULE
+    Bn, L, N = cfg.batch, cfg.seq_len, cfg.n_layers
+    a, ca = runtime.State(cfg), runtime.CEState(cfg)
+    runtime.step(model, a, mode=B.DLLM_MODE_FULL, ce_state=ca)
+    b_, cb = runtime.State(cfg), runtime.CEState(cfg)
+    for k, v in a.tensors().items():
+        getattr(b_, k).copy_(v)
+    cb.kf.copy_(ca.kf)
+    cb.has.copy_(ca.has)
+    dev = "cuda"
+    idx = [torch.zeros((Bn, L), dtype=torch.int32, device=dev) for _ in range(2)]
+    n = [torch.zeros(Bn, dtype=torch.int32, device=dev) for _ in range(2)]
+    forced = torch.zeros((Bn, L), dtype=torch.uint8, device=dev)
+    fmax = cfg.block_len + cfg.recent_k
+    for t in range(3):
+        runtime.step(model, a, mode=B.DLLM_MODE_SPARSE, ce_state=ca)
+        S0 = Snap(b_)
+        B.dllm_forced_set(model.h, b_, FORCED_RULE[cfg.forced], cfg.recent_k, forced)
+        rows0 = torch.zeros((Bn, L), dtype=torch.int32)
+        n0 = torch.zeros(Bn, dtype=torch.int32)
+        for bb in range(Bn):
+            nh, nn = S0.n_history[bb], S0.n_new[bb]
+            rows0[bb, :nn] = torch.from_numpy(S0.history[bb][nh - nn:nh].copy())
+            n0[bb] = nn
+        pi, pn, pmax = rows0.to(dev), n0.to(dev), Bn * min(L, cfg.block_len)
+        B.dllm_embed(model.h, b_, pi, pn)
+        for l in range(N):
+            B.dllm_drift_score(model.h, l, b_, pi, pn, pmax)
+            k = oracle.budget_k(cfg.rho[l], L)
+            B.dllm_select(model.h, l, b_, forced, None, cfg.rho[l], idx[l & 1], n[l & 1])
+            rmax = Bn * min(L, max(k, fmax))
+            B.dllm_sparse_layer(model.h, l, b_, idx[l & 1], n[l & 1], rmax)
+            pi, pn, pmax = idx[l & 1], n[l & 1], rmax
+        B.dllm_commit_ce(model.h, b_, runtime.ce_params(cfg), cb, cfg.conf_threshold, cfg.tau)
+        torch.cuda.synchronize()
+        for k2, v in a.tensors().items():
+            assert torch.equal(v, getattr(b_, k2)), f"t={t}: {k2} differs"
+        assert torch.equal(ca.kf, cb.kf) and torch.equal(ca.has, cb.has), f"t={t}: filter state differs"
+    model.close()
+
+
+def test_ce_rejects_bad_params():
+    cfg = CE
+    model, _, _ = build(cfg)
+    st, cs = runtime.State(cfg), runtime.CEState(cfg)
+    for bad in (dict(ce_horizon=0), dict(ce_horizon=65), dict(ce_r=0.0), dict(ce_q=-1.0), dict(ce_kappa=-1.0)):
+        with pytest.raises(B.DllmError):
+            B.dllm_commit_ce(model.h, st, runtime.ce_params(cfg.with_(**bad)), cs, cfg.conf_threshold, cfg.tau)
+    model.close()
