@@ -71,6 +71,8 @@ class SeqState:
         self.drift_cnt = np.zeros(spec.block_len, np.int64)
         # Confidence Extrapolation: filter state per current block position
         self.ce_states = [None] * spec.block_len
+        # Polestar schedule: steps since the last full pass
+        self.steps_since_full = 0
 
     def advance_block(self):
         L, b = self.spec.seq_len, self.spec.block_len
@@ -114,6 +116,10 @@ def step(st: SeqState, layers, head, spec: Spec, pol: Policy, force_mode: Option
     overrides.  Returns a dict with the per-layer index sets and scores, the
     block statistics and the commits."""
     full = st.full_next if force_mode is None else (force_mode == "full")
+    fp = pol.polestar.full_period if pol.score == "polestar_kl" else 0
+    if force_mode is None and fp > 0 and st.steps_since_full + 1 >= fp:
+        full = True  # periodic full pass (Polestar section 2A, schedule)
+    st.steps_since_full = 0 if full else st.steps_since_full + 1
     st.H[0] = np.asarray(head["embed"], spec.wd)[st.tokens]
     forced = st.forced_set(pol)
     sets, scores, ps_info = [], [], []
@@ -121,7 +127,7 @@ def step(st: SeqState, layers, head, spec: Spec, pol: Policy, force_mode: Option
         if pol.score == "polestar_kl" and not full:
             # Polestar: the drift path picks the rows; no value proxy involved
             r = polestar.drift_and_select(st.H[l], st.K[l], st.block_start, layers[l], spec, pol.polestar,
-                                          st.ps[l])
+                                          st.ps[l], len(st.history))
             sparse_layer(st.H[l], st.K[l], st.V[l], st.H[l + 1], r["I"], layers[l], spec)
             sets.append(r["I"])
             scores.append(r["kl"])

@@ -63,6 +63,8 @@ class PolestarParams:
     iters: int = 10
     top: int = 4
     window_blocks: int = 3
+    tau_upd: int = 0        # drift refresh once this many tokens were decoded since the last (0: every step)
+    full_period: int = 0    # a full pass every this many steps (0: never)
 
 
 def window_start(block_start: int, L: int, blk: int, wblocks: int = 3) -> int:
@@ -245,17 +247,34 @@ def select_rows(block_rows, wstart: int, assign, clusters):
 
 @dataclasses.dataclass
 class PolestarLayerState:
-    """Per layer and sequence: the previous step's proxy log-attention and the
-    window it belongs to."""
+    """Per layer and sequence: the proxy log-attention of the last drift
+    refresh, the window it belongs to, and the number of decoded tokens at
+    that refresh."""
     logA: Optional[np.ndarray] = None
     wstart: int = -1
+    hist_at_update: int = 0
 
 
-def drift_and_select(x, K, block_start: int, W, spec: Spec, pp: PolestarParams, prev: PolestarLayerState):
+def refresh_due(prev: PolestarLayerState, ws: int, n_decoded: int, pp: PolestarParams) -> bool:
+    """Schedule of the drift refresh (Polestar section 2A, schedule).  The page
+    triggers updates once the decoded context has moved enough, e.g. after
+    tau_upd decoded tokens.  Reading: a layer's refresh runs when tau_upd <= 0
+    (every step), on a window's first step (no stored attention, or the window
+    moved), or once at least tau_upd tokens were decoded since its last
+    refresh.  Full passes do not reset the count."""
+    if pp.tau_upd <= 0 or prev.logA is None or prev.wstart != ws:
+        return True
+    return n_decoded - prev.hist_at_update >= pp.tau_upd
+
+
+def drift_and_select(x, K, block_start: int, W, spec: Spec, pp: PolestarParams, prev: PolestarLayerState,
+                     n_decoded: int = 0):
     """The whole drift path of one layer and one sequence: window, k-means,
     NVFP4 codes, centroid queries, proxy attention, cluster drift, top
     clusters and the index set I.  Updates ``prev``; returns a dict of every
-    intermediate."""
+    intermediate.  ``n_decoded``: tokens decoded before this step (for the
+    refresh schedule).  Without a due refresh (``refresh_due``) the step
+    refreshes only the current block, keeps ``prev`` and has no drift."""
     L, blk = spec.seq_len, spec.block_len
     Wn = pp.window_blocks * blk
     ws = window_start(block_start, L, blk, pp.window_blocks)
@@ -266,17 +285,22 @@ def drift_and_select(x, K, block_start: int, W, spec: Spec, pp: PolestarParams, 
     pos = ws + stride * np.arange(pp.n_clusters)
     q = centroid_queries(C, pos, W, spec)
     logA = proxy_log_attention(q, np.asarray(K)[ws:ws + Wn])
-    valid = prev.logA is not None and prev.wstart == ws
+    rows = np.arange(block_start, min(block_start + blk, L))
+    update = refresh_due(prev, ws, n_decoded, pp)
+    valid = update and prev.logA is not None and prev.wstart == ws
     if valid:
         kl = cluster_kl(logA, prev.logA)
     else:
         kl = np.zeros(pp.n_clusters)
-    prev.logA, prev.wstart = logA, ws
     top = top_clusters(kl, pp.top)
-    rows = np.arange(block_start, min(block_start + blk, L))
-    I = select_rows(rows, ws, a, top)
+    if update:
+        prev.logA, prev.wstart, prev.hist_at_update = logA, ws, n_decoded
+        I = select_rows(rows, ws, a, top)
+    else:
+        I = rows.astype(np.int64)
     return {"wstart": ws, "Xh": Xh, "C": C, "assign": a, "obj": obj, "dots": D, "codes": codes,
-            "scales": scales, "q": q, "logA": logA, "kl": kl, "valid": valid, "top": top, "I": I}
+            "scales": scales, "q": q, "logA": logA, "kl": kl, "valid": valid, "update": update, "top": top,
+            "I": I}
 
 
 # ---------------------------------------------------------------------------

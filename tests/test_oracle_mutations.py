@@ -359,3 +359,26 @@ CE_MUTATIONS = [m_ce_predict_drops_quarter_q, m_ce_gain_swapped, m_ce_forecast_n
 def test_ce_mutation_is_caught(monkeypatch, mutation):
     mutation(monkeypatch)
     assert _fails(pins.ALL_CHECKS), f"no pin catches {mutation.__name__}"
+
+
+# ---- Polestar refresh schedule ----
+def m_refresh_strict(monkeypatch):
+    def bad(prev, ws, n_decoded, pp):
+        if pp.tau_upd <= 0 or prev.logA is None or prev.wstart != ws:
+            return True
+        return n_decoded - prev.hist_at_update > pp.tau_upd
+    monkeypatch.setattr(ops, "refresh_due", bad)
+
+
+def m_refresh_ignores_window(monkeypatch):
+    def bad(prev, ws, n_decoded, pp):
+        if pp.tau_upd <= 0 or prev.logA is None:
+            return True
+        return n_decoded - prev.hist_at_update >= pp.tau_upd
+    monkeypatch.setattr(ops, "refresh_due", bad)
+
+
+@pytest.mark.parametrize("mutation", [m_refresh_strict, m_refresh_ignores_window], ids=lambda f: f.__name__)
+def test_schedule_mutation_is_caught(monkeypatch, mutation):
+    mutation(monkeypatch)
+    assert _fails(pins.ALL_CHECKS), f"no pin catches {mutation.__name__}"
