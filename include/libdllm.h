@@ -132,6 +132,11 @@ typedef struct {
   int32_t drift_commit;  /* 1: dllm_step commits with Polestar-Commit (dllm_polestar_commit);
                             0: the static threshold commit */
   double commit_alpha;   /* Polestar-Commit alpha (>= 0; +inf disables the drift rule) */
+  int32_t tau_upd;       /* schedule: a layer's drift refresh runs on a window's first step or once
+                            this many tokens were decoded since its last one (0: every step);
+                            otherwise the step refreshes only the current block */
+  int32_t full_period;   /* schedule: dllm_step in AUTO mode runs a full pass every this many steps
+                            (0: never) */
 } dllm_polestar_params;
 
 /* Caller-owned Polestar state (K = n_clusters, Hq = n_q_heads, W as above).
@@ -154,6 +159,8 @@ typedef struct {
   int32_t *drift_cnt;    /* [B][block_len] number of drifts in drift_sum */
   int32_t *drift_valid;  /* [B] 1 when the last dllm_polestar_select found the cluster drift
                             defined (window unchanged); the Polestar commit clears it */
+  int32_t *upd_hist;     /* [N][B] state.n_history at the layer's last drift refresh (initialise to 0) */
+  int32_t steps_since_full; /* host value: steps since the last full pass (dllm_step keeps it) */
 } dllm_polestar_state;
 
 /* Confidence Extrapolation (TSPD + CE page, method section 2) on top of the

@@ -116,10 +116,13 @@ def step(st: SeqState, layers, head, spec: Spec, pol: Policy, force_mode: Option
     overrides.  Returns a dict with the per-layer index sets and scores, the
     block statistics and the commits."""
     full = st.full_next if force_mode is None else (force_mode == "full")
+    # periodic full pass (Polestar section 2A, schedule): counted in steps
+    # since the last periodic or explicitly requested full pass, apart from
+    # the entropy gate
     fp = pol.polestar.full_period if pol.score == "polestar_kl" else 0
-    if force_mode is None and fp > 0 and st.steps_since_full + 1 >= fp:
-        full = True  # periodic full pass (Polestar section 2A, schedule)
-    st.steps_since_full = 0 if full else st.steps_since_full + 1
+    periodic = force_mode is None and fp > 0 and st.steps_since_full + 1 >= fp
+    full = full or periodic
+    st.steps_since_full = 0 if (periodic or force_mode == "full") else st.steps_since_full + 1
     st.H[0] = np.asarray(head["embed"], spec.wd)[st.tokens]
     forced = st.forced_set(pol)
     sets, scores, ps_info = [], [], []

@@ -44,13 +44,13 @@ class DllmState(ctypes.Structure):
 
 class DllmPolestarParams(ctypes.Structure):
     _fields_ = [("n_clusters", _i32), ("kmeans_iters", _i32), ("top_clusters", _i32), ("window_blocks", _i32),
-                ("drift_commit", _i32), ("commit_alpha", _f64)]
+                ("drift_commit", _i32), ("commit_alpha", _f64), ("tau_upd", _i32), ("full_period", _i32)]
 
 
 class DllmPolestarState(ctypes.Structure):
     _fields_ = [(n, _vp) for n in (
         "log_attn", "win_start", "centroids", "norms", "assign", "codes", "scales", "queries", "kl", "top",
-        "drift_sum", "drift_cnt", "drift_valid")]
+        "drift_sum", "drift_cnt", "drift_valid", "upd_hist")] + [("steps_since_full", _i32)]
 
 
 class DllmCEParams(ctypes.Structure):

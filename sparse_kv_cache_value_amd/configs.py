@@ -87,6 +87,8 @@ class Config:
     n_clusters: int = 16
     kmeans_iters: int = 10
     top_clusters: int = 4
+    tau_upd: int = 0                # drift refresh every this many decoded tokens (0: every step)
+    full_period: int = 0            # AUTO mode: a full pass every this many steps (0: never)
     polestar_commit: bool = False   # Polestar-Commit (Polestar section 2B) instead of the threshold commit
     commit_alpha: float = 1.0
     # Confidence Extrapolation (TSPD + CE section 2) on the threshold commit; horizon 0 = off

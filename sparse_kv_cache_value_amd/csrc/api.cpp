@@ -443,9 +443,10 @@ dllm_status check_polestar(const dllm_model* m, const dllm_state* s, const dllm_
   const dllm_dims& d = m->d;
   if (!ps || !p) return fail(DLLM_E_ARG, "polestar state/params is NULL");
   if (!ps->log_attn || !ps->win_start || !ps->centroids || !ps->norms || !ps->assign || !ps->codes || !ps->scales ||
-      !ps->queries || !ps->kl || !ps->top || !ps->drift_sum || !ps->drift_cnt || !ps->drift_valid)
+      !ps->queries || !ps->kl || !ps->top || !ps->drift_sum || !ps->drift_cnt || !ps->drift_valid || !ps->upd_hist)
     return fail(DLLM_E_ARG, "polestar state has a NULL buffer");
   if (p->drift_commit && !(p->commit_alpha >= 0.0)) return fail(DLLM_E_ARG, "commit_alpha must be >= 0");
+  if (p->tau_upd < 0 || p->full_period < 0) return fail(DLLM_E_ARG, "tau_upd and full_period must be >= 0");
   if (d.block_len > 64) return fail(DLLM_E_UNSUPPORTED, "the Polestar path needs block_len <= 64");
   if (!m->ps_R) return fail(DLLM_E_UNSUPPORTED, "the Polestar path needs d_model %% 128 == 0");
   const int W = p->window_blocks * d.block_len;
@@ -502,7 +503,8 @@ dllm_status do_polestar_drift(dllm_model* m, int layer, const dllm_state* s, dll
                            m->rope_sin, ps->queries));
   double* la = ps->log_attn + (size_t)layer * B * K * Hq * W;
   HIPCHK(launch_ps_attn_kl(st, m->bf16, B, L, blk, W, K, Hq, d.n_kv_heads, dh, s->block_start, ps->queries,
-                           kcache(m, const_cast<dllm_state*>(s), layer), la, m->ps_klp));
+                           kcache(m, const_cast<dllm_state*>(s), layer), la, m->ps_klp, p->tau_upd,
+                           ps->win_start + (size_t)layer * B, s->n_history, ps->upd_hist + (size_t)layer * B));
   prof2.done();
   HIPCHK(hipStreamWaitEvent(st, m->ev_join, 0));
   return DLLM_OK;
@@ -515,7 +517,7 @@ dllm_status do_polestar_select(dllm_model* m, int layer, const dllm_state* s, dl
   Prof prof(m, st, DLLM_PROF_SELECT, (double)B * d.n_q_heads * p->n_clusters * 8.0 + (double)B * W * 8.0, 0.0);
   HIPCHK(launch_ps_select(st, B, d.seq_len, d.block_len, W, p->n_clusters, d.n_q_heads, p->top_clusters,
                           s->block_start, ps->assign, m->ps_klp, ps->win_start + (size_t)layer * B, ps->kl, ps->top,
-                          idx, n, ps->drift_valid));
+                          idx, n, ps->drift_valid, p->tau_upd, s->n_history, ps->upd_hist + (size_t)layer * B));
   prof.done();
   return DLLM_OK;
 }
@@ -876,17 +878,28 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
   hipStream_t st = S(stream);
   const int B = s->batch, L = d.seq_len;
   bool any_full = p->mode == DLLM_MODE_FULL;
+  int mode = p->mode;
   if (p->mode == DLLM_MODE_AUTO) {
     HIPCHK(hipMemcpyAsync(m->full_host, s->full_next, (size_t)B, hipMemcpyDeviceToHost, st));
     HIPCHK(hipStreamSynchronize(st));
     for (int b = 0; b < B; ++b) any_full = any_full || m->full_host[b] != 0;
+    // Polestar schedule: a periodic full pass of every sequence
+    const int fp = polestar ? p->polestar->full_period : 0;
+    if (fp > 0 && p->polestar_state->steps_since_full + 1 >= fp) {
+      any_full = true;
+      mode = DLLM_MODE_FULL;
+    }
+  }
+  if (polestar) {
+    // the step is a full pass for every sequence exactly when mode is FULL
+    p->polestar_state->steps_since_full = mode == DLLM_MODE_FULL ? 0 : p->polestar_state->steps_since_full + 1;
   }
   const int fmax = p->forced_rule == DLLM_FORCED_NONE ? 0
                    : (p->forced_rule == DLLM_FORCED_BLOCK ? d.block_len : d.block_len + p->recent_k);
   int prev_max = any_full ? B * L : B * std::min(L, d.block_len);
   {
     Prof prof(m, st, DLLM_PROF_DECIDE, (double)B * L * 6.0 + 2.0 * prev_max * d.d_model * m->esize, 0.0);
-    HIPCHK(launch_prep(st, B, L, d.block_len, p->forced_rule, p->recent_k, p->mode, s->history, s->n_history,
+    HIPCHK(launch_prep(st, B, L, d.block_len, p->forced_rule, p->recent_k, mode, s->history, s->n_history,
                        s->n_new, s->block_start, s->full_next, m->forced, m->step_full, m->idx0, m->n0));
     HIPCHK(launch_embed(st, m->bf16, prev_max, B, L, d.d_model, d.vocab, m->idx0, m->n0, s->tokens, m->embed,
                         hid(m, s, 0)));

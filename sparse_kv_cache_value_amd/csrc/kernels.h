@@ -133,11 +133,15 @@ hipError_t launch_ps_codes(hipStream_t st, bool bf16, int B, int L, int d, int b
 hipError_t launch_ps_queries(hipStream_t st, bool bf16, int B, int L, int blk, int W, int K, int Hq, int dh, int S,
                              int ldp, const int32_t* bstart, const float* part, const float* rc, const float* rs,
                              void* q);
+// logA is replaced only for sequences whose drift refresh is due (tau_upd,
+// the layer's window start and n_history at its last refresh).
 hipError_t launch_ps_attn_kl(hipStream_t st, bool bf16, int B, int L, int blk, int W, int K, int Hq, int Hkv,
-                             int dh, const int32_t* bstart, const void* q, const void* Kc, double* logA, double* klp);
+                             int dh, const int32_t* bstart, const void* q, const void* Kc, double* logA, double* klp,
+                             int tau_upd, const int32_t* wstart, const int32_t* n_hist, const int32_t* upd_hist);
 hipError_t launch_ps_select(hipStream_t st, int B, int L, int blk, int W, int K, int Hq, int top,
                             const int32_t* bstart, const int32_t* assign, const double* klp, int32_t* wstart,
-                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n, int32_t* valid);
+                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n, int32_t* valid, int tau_upd,
+                            const int32_t* n_hist, int32_t* upd_hist);
 // Polestar-Commit; stats [B][2 blk][4] (current and next block), blk <= 64.
 hipError_t launch_ps_commit(hipStream_t st, int B, int L, int blk, int W, int K, int top, double thr, double alpha,
                             double tau, const double* stats, const double* kl, const int32_t* assign,

@@ -437,16 +437,30 @@ __global__ __launch_bounds__(256) void ps_query_kernel(int L, int blk, int W, in
 // l feeds query/key row l%16 and the dims (dh/4)*(l/16) .. +dh/4, one per
 // MFMA, in the same order for both operands.
 // ---------------------------------------------------------------------------
+// Whether sequence b's drift refresh at this layer is due: every step at
+// tau_upd <= 0, on a window's first step, or once tau_upd tokens were decoded
+// since the layer's last refresh.
+__device__ __forceinline__ bool ps_refresh_due(int b, int ws, int tau_upd, const int32_t* __restrict__ wstart,
+                                               const int32_t* __restrict__ n_hist,
+                                               const int32_t* __restrict__ upd_hist) {
+  return tau_upd <= 0 || wstart[b] != ws || n_hist[b] - upd_hist[b] >= tau_upd;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void ps_attn_kl_kernel(int L, int blk, int W, int K, int Hq, int Hkv, int dh,
                                                          const int32_t* __restrict__ bstart,
                                                          const T* __restrict__ q, const T* __restrict__ Kc,
-                                                         double* __restrict__ logA, double* __restrict__ klp) {
+                                                         double* __restrict__ logA, double* __restrict__ klp,
+                                                         int tau_upd, const int32_t* __restrict__ wstart,
+                                                         const int32_t* __restrict__ n_hist,
+                                                         const int32_t* __restrict__ upd_hist) {
   __shared__ double sc[16 * PS_WMAX];  // [K][W]
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int g = (h * Hkv) / Hq;
   const int ws = ps_window_start(bstart[b], L, blk, W);
+  // without a due refresh the stored attention stays (the KL is not used)
+  const bool store = ps_refresh_due(b, ws, tau_upd, wstart, n_hist, upd_hist);
   const int nq = Hq * dh, kq = dh / 4;
   const int r = lane & 15, slot = lane >> 4;
   const T* qrow = q + ((size_t)b * K + min(r, K - 1)) * nq + h * dh + slot * kq;
@@ -514,12 +528,12 @@ __global__ __launch_bounds__(256) void ps_attn_kl_kernel(int L, int blk, int W, 
     if (k0) {
       const double lv = (s0 - mx) - lse;
       kl += exp(lv) * (lv - prev[u][0]);
-      la[lane] = lv;
+      if (store) la[lane] = lv;
     }
     if (k1) {
       const double lv = (s1 - mx) - lse;
       kl += exp(lv) * (lv - prev[u][1]);
-      la[lane + 64] = lv;
+      if (store) la[lane + 64] = lv;
     }
     kl = wave_sum(kl);
     if (lane == 0) klp[((size_t)b * Hq + h) * K + j] = kl;
@@ -537,14 +551,17 @@ __global__ __launch_bounds__(128) void ps_select_kernel(int L, int blk, int W, i
                                                         const double* __restrict__ klp, int32_t* __restrict__ wstart,
                                                         double* __restrict__ kl_out, int32_t* __restrict__ top_out,
                                                         int32_t* __restrict__ idx, int32_t* __restrict__ n_out,
-                                                        int32_t* __restrict__ valid_out) {
+                                                        int32_t* __restrict__ valid_out, int tau_upd,
+                                                        const int32_t* __restrict__ n_hist,
+                                                        int32_t* __restrict__ upd_hist) {
   __shared__ double kl[16];
   __shared__ int sel[16];
   __shared__ int cnt0;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int bs = bstart[b];
   const int ws = ps_window_start(bs, L, blk, W);
-  const bool valid = wstart[b] == ws;
+  const bool upd = ps_refresh_due(b, ws, tau_upd, wstart, n_hist, upd_hist);
+  const bool valid = upd && wstart[b] == ws;
   if (tid < K) {
     // mean over heads, heads added in order (loads issued 8 at a time)
     double acc = 0.0;
@@ -573,12 +590,15 @@ __global__ __launch_bounds__(128) void ps_select_kernel(int L, int blk, int W, i
     top_out[(size_t)b * top + pos] = tid;
   }
   if (tid == 0) {
-    wstart[b] = ws;
+    if (upd) {
+      wstart[b] = ws;
+      upd_hist[b] = n_hist[b];
+    }
     valid_out[b] = valid ? 1 : 0;
   }
   // I = current block rows + members of the selected clusters, ascending
   const int row = ws + tid;
-  const bool f = tid < W && ((row >= bs && row < bs + blk) || sel[assign[(size_t)b * W + tid]]);
+  const bool f = tid < W && ((row >= bs && row < bs + blk) || (upd && sel[assign[(size_t)b * W + tid]]));
   const unsigned long long m = __ballot(f);
   const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
   if (tid == 0) cnt0 = __popcll(m);
@@ -819,23 +839,25 @@ hipError_t launch_ps_queries(hipStream_t st, bool bf16m, int B, int L, int blk, 
 }
 
 hipError_t launch_ps_attn_kl(hipStream_t st, bool bf16m, int B, int L, int blk, int W, int K, int Hq, int Hkv,
-                             int dh, const int32_t* bstart, const void* q, const void* Kc, double* logA, double* klp) {
+                             int dh, const int32_t* bstart, const void* q, const void* Kc, double* logA, double* klp,
+                             int tau_upd, const int32_t* wstart, const int32_t* n_hist, const int32_t* upd_hist) {
   if (W > PS_WMAX || W < 1 || K > 16 || K < 1 || dh % 32 || dh > 128) return hipErrorInvalidValue;
   if (bf16m)
     hipLaunchKernelGGL(ps_attn_kl_kernel<bf16>, dim3(Hq, B), dim3(256), 0, st, L, blk, W, K, Hq, Hkv, dh, bstart,
-                       (const bf16*)q, (const bf16*)Kc, logA, klp);
+                       (const bf16*)q, (const bf16*)Kc, logA, klp, tau_upd, wstart, n_hist, upd_hist);
   else
     hipLaunchKernelGGL(ps_attn_kl_kernel<float>, dim3(Hq, B), dim3(256), 0, st, L, blk, W, K, Hq, Hkv, dh, bstart,
-                       (const float*)q, (const float*)Kc, logA, klp);
+                       (const float*)q, (const float*)Kc, logA, klp, tau_upd, wstart, n_hist, upd_hist);
   return hipGetLastError();
 }
 
 hipError_t launch_ps_select(hipStream_t st, int B, int L, int blk, int W, int K, int Hq, int top,
                             const int32_t* bstart, const int32_t* assign, const double* klp, int32_t* wstart,
-                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n, int32_t* valid) {
+                            double* kl, int32_t* top_out, int32_t* idx, int32_t* n, int32_t* valid, int tau_upd,
+                            const int32_t* n_hist, int32_t* upd_hist) {
   if (W > PS_WMAX || K > 16) return hipErrorInvalidValue;
   hipLaunchKernelGGL(ps_select_kernel, dim3(B), dim3(128), 0, st, L, blk, W, K, Hq, top, bstart, assign, klp, wstart,
-                     kl, top_out, idx, n, valid);
+                     kl, top_out, idx, n, valid, tau_upd, n_hist, upd_hist);
   return hipGetLastError();
 }
 

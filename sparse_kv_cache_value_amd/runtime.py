@@ -114,7 +114,8 @@ class State:
 
 def polestar_params(cfg: Config) -> B.DllmPolestarParams:
     return B.DllmPolestarParams(cfg.n_clusters, cfg.kmeans_iters, cfg.top_clusters, cfg.window_blocks,
-                                1 if cfg.polestar_commit else 0, float(cfg.commit_alpha))
+                                1 if cfg.polestar_commit else 0, float(cfg.commit_alpha), cfg.tau_upd,
+                                cfg.full_period)
 
 
 class PolestarState:
@@ -139,9 +140,10 @@ class PolestarState:
         self.drift_sum = torch.zeros((Bn, cfg.block_len), dtype=torch.float64, device=dev)
         self.drift_cnt = torch.zeros((Bn, cfg.block_len), dtype=torch.int32, device=dev)
         self.drift_valid = torch.zeros(Bn, dtype=torch.int32, device=dev)
+        self.upd_hist = torch.zeros((N, Bn), dtype=torch.int32, device=dev)
         self.c = B.DllmPolestarState(*[t.data_ptr() for t in (
             self.log_attn, self.win_start, self.centroids, self.norms, self.assign, self.codes, self.scales,
-            self.queries, self.kl, self.top, self.drift_sum, self.drift_cnt, self.drift_valid)])
+            self.queries, self.kl, self.top, self.drift_sum, self.drift_cnt, self.drift_valid, self.upd_hist)], 0)
 
 
 def ce_params(cfg: Config) -> B.DllmCEParams:
