@@ -54,7 +54,8 @@ enum {
   DLLM_E_STATE = -3,       /* call order violated (e.g. layer weights missing) */
   DLLM_E_NOMEM = -4,       /* device allocation failed */
   DLLM_E_HIP = -5,         /* a HIP runtime call failed */
-  DLLM_E_UNSUPPORTED = -6  /* feature not built */
+  DLLM_E_UNSUPPORTED = -6, /* feature not built */
+  DLLM_E_NUMERIC = -7      /* a factorisation broke down (dllm_derive_proxy_basis) */
 };
 enum { DLLM_FP32 = 0, DLLM_BF16 = 1 };
 enum { DLLM_MODE_AUTO = 0, DLLM_MODE_FULL = 1, DLLM_MODE_SPARSE = 2 };
@@ -88,7 +89,8 @@ typedef struct {
   const void *w_up;       /* [d_model][d_ffn] */
   const void *w_down;     /* [d_ffn][d_model] */
   /* SPA-Cache step 1: W_r = U_r S_r, the top-r left singular vectors of W_v
-   * scaled by their singular values, [d_model][proxy_rank] fp32. */
+   * scaled by their singular values, [d_model][proxy_rank] fp32.  NULL: the
+   * library derives it from w_v (dllm_derive_proxy_basis, DLLM_PROXY_ITERS). */
   const float *w_proxy;
 } dllm_layer_weights;
 
@@ -221,9 +223,32 @@ dllm_status dllm_create(const dllm_dims *dims, dllm_model **out);
 dllm_status dllm_destroy(dllm_model *m);
 
 /* Copy layer `layer`'s weights into library-owned, repacked buffers (the
- * caller may free its copies once the stream has passed this call). */
+ * caller may free its copies once the stream has passed this call).  With
+ * w->w_proxy == NULL the proxy basis is derived from w->w_v on the device
+ * (waits for the stream). */
 dllm_status dllm_init_layer(dllm_model *m, int32_t layer, const dllm_layer_weights *w,
                             void *stream);
+
+/* Power steps of the in-library proxy basis when dllm_init_layer derives it. */
+#define DLLM_PROXY_ITERS 200
+
+/* SPA-Cache step 1 in the library (init-time): W_r = U_r S_r, the top-r
+ * (r = proxy_rank) left singular vectors of the value projection
+ * w_v [d_model][n_kv_heads*head_dim] (device, storage dtype) times their
+ * singular values, written to w_r_out [d_model][proxy_rank] (device, fp64;
+ * dllm_init_layer stores it in fp32 like a supplied basis).
+ * Randomised subspace iteration in fp64: p = min(r + 8, d_model, n_v, 136)
+ * (rounded down to even) columns started from a fixed pseudo-random matrix,
+ * `iters` steps Q <- orth(W (W^T Q)) with CholeskyQR2, then Rayleigh-Ritz
+ * (Jacobi eigen-decomposition of Z^T Z, Z = W^T Q).  The columns come out in
+ * descending singular value order with an arbitrary sign each, which leaves
+ * every proxy cosine unchanged.  Convergence needs a gap between the r-th and
+ * (p+1)-th singular values: the subspace error shrinks by (s_{p+1}/s_r)^2
+ * per step.  Allocates and frees its fp64 workspace and waits for `stream`.
+ * Errors: DLLM_E_ARG (NULL pointer, iters < 0), DLLM_E_UNSUPPORTED
+ * (proxy_rank > 128 or p < proxy_rank), DLLM_E_NUMERIC (a non-positive
+ * Cholesky pivot: the iterated subspace lost rank). */
+dllm_status dllm_derive_proxy_basis(dllm_model *m, const void *w_v, int32_t iters, double *w_r_out, void *stream);
 
 /* Copy the embedding table [vocab][d_model], the final norm gain [d_model]
  * (fp32) and the LM head [d_model][vocab]. */

@@ -16,7 +16,9 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdllm.so")
 
-DLLM_OK, DLLM_E_ARG, DLLM_E_SHAPE, DLLM_E_STATE, DLLM_E_NOMEM, DLLM_E_HIP, DLLM_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+(DLLM_OK, DLLM_E_ARG, DLLM_E_SHAPE, DLLM_E_STATE, DLLM_E_NOMEM, DLLM_E_HIP, DLLM_E_UNSUPPORTED,
+ DLLM_E_NUMERIC) = 0, -1, -2, -3, -4, -5, -6, -7
+DLLM_PROXY_ITERS = 200
 DLLM_FP32, DLLM_BF16 = 0, 1
 DLLM_MODE_AUTO, DLLM_MODE_FULL, DLLM_MODE_SPARSE = 0, 1, 2
 DLLM_FORCED_NONE, DLLM_FORCED_BLOCK, DLLM_FORCED_BLOCK_RECENT = 0, 1, 2
@@ -109,6 +111,7 @@ SIGNATURES = {
     "dllm_profile": (_i32, [_vp, _i32]),
     "dllm_profile_read": (_i32, [_vp, ctypes.POINTER(DllmKernelStats)]),
     "dllm_stream_probe": (_i32, [_vp, ctypes.c_size_t, _vp, _i32, ctypes.POINTER(_f64), _vp]),
+    "dllm_derive_proxy_basis": (_i32, [_vp, _vp, _i32, _vp, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -262,6 +265,11 @@ def dllm_profile(m: int, enable: bool, classes=None):
         for c in classes:
             mask |= 1 << PROF_NAMES.index(c)
     _check(lib().dllm_profile(m, mask))
+
+
+def dllm_derive_proxy_basis(m: int, w_v, w_r_out, iters: int = DLLM_PROXY_ITERS, stream=None):
+    """W_r [d][r] fp64 into w_r_out from the device value projection w_v."""
+    _check(lib().dllm_derive_proxy_basis(m, _p(w_v), int(iters), _p(w_r_out), _stream(stream)))
 
 
 def dllm_stream_probe(buf, scratch, reps: int = 3, stream=None) -> float:

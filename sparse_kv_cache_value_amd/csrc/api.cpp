@@ -666,12 +666,39 @@ dllm_status dllm_destroy(dllm_model* m) {
   return DLLM_OK;
 }
 
+// W_r [d][r] fp32 from the value projection (device, storage dtype); waits
+// for the stream and frees its workspace.
+dllm_status derive_basis(dllm_model* m, const void* w_v, int iters, double* wr, hipStream_t st) {
+  const dllm_dims& d = m->d;
+  const int D = d.d_model, nv = nv_of(d), r = d.proxy_rank;
+  if (r > 128 || proxy_basis_width(D, nv, r) < r)
+    return fail(DLLM_E_UNSUPPORTED, "proxy basis: need proxy_rank <= 128 and a subspace of at least r columns");
+  double* ws = nullptr;
+  int32_t* status = nullptr;
+  if (hipMalloc((void**)&ws, proxy_basis_workspace_doubles(D, nv, r) * 8) != hipSuccess)
+    return fail(DLLM_E_NOMEM, "proxy basis workspace");
+  if (hipMalloc((void**)&status, 16) != hipSuccess) {
+    (void)hipFree(ws);
+    return fail(DLLM_E_NOMEM, "proxy basis workspace");
+  }
+  int32_t st_h = 0;
+  hipError_t e = hipMemsetAsync(status, 0, 16, st);
+  if (e == hipSuccess) e = launch_proxy_basis(st, m->bf16, D, nv, r, iters, w_v, wr, ws, status);
+  if (e == hipSuccess) e = hipMemcpyAsync(&st_h, status, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  (void)hipFree(ws);
+  (void)hipFree(status);
+  if (e != hipSuccess) return fail(DLLM_E_HIP, "proxy basis: %s", hipGetErrorString(e));
+  if (st_h != 0) return fail(DLLM_E_NUMERIC, "proxy basis: a Cholesky pivot was not positive");
+  return DLLM_OK;
+}
+
 dllm_status dllm_init_layer(dllm_model* m, int32_t layer, const dllm_layer_weights* w, void* stream) {
   CHK(check_model(m));
   if (!w) return fail(DLLM_E_ARG, "weights is NULL");
   if (layer < 0 || layer >= m->d.n_layers) return fail(DLLM_E_ARG, "layer %d outside [0, %d)", layer, m->d.n_layers);
   if (!w->attn_norm || !w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->ffn_norm || !w->w_gate || !w->w_up ||
-      !w->w_down || !w->w_proxy)
+      !w->w_down)
     return fail(DLLM_E_ARG, "layer %d: a weight pointer is NULL", layer);
   const dllm_dims& d = m->d;
   const int D = d.d_model, F = d.d_ffn, nq = nq_of(d), nv = nv_of(d), r = d.proxy_rank;
@@ -698,9 +725,35 @@ dllm_status dllm_init_layer(dllm_model* m, int32_t layer, const dllm_layer_weigh
   CHK(pack(m, st, D, F, w->w_gate, L.w_gu, 2 * F, 0, 64));
   CHK(pack(m, st, D, F, w->w_up, L.w_gu, 2 * F, 32, 64));
   CHK(pack(m, st, F, D, w->w_down, L.w_down, D, 0, 32));
-  HIPCHK(launch_pad_proxy(st, D, r, w->w_proxy, L.w_proxy));
+  if (w->w_proxy) {
+    HIPCHK(launch_pad_proxy(st, D, r, w->w_proxy, L.w_proxy));
+  } else {
+    // derived in fp64, stored in fp32 like a supplied basis
+    double* w64 = nullptr;
+    float* w32 = nullptr;
+    if (hipMalloc((void**)&w64, (size_t)D * r * 8) != hipSuccess) return fail(DLLM_E_NOMEM, "proxy basis buffer");
+    if (hipMalloc((void**)&w32, (size_t)D * r * 4) != hipSuccess) {
+      (void)hipFree(w64);
+      return fail(DLLM_E_NOMEM, "proxy basis buffer");
+    }
+    dllm_status e = derive_basis(m, w->w_v, DLLM_PROXY_ITERS, w64, st);
+    if (e == DLLM_OK && (launch_f64_to_f32(st, (size_t)D * r, w64, w32) != hipSuccess ||
+                         launch_pad_proxy(st, D, r, w32, L.w_proxy) != hipSuccess))
+      e = fail(DLLM_E_HIP, "proxy basis packing failed");
+    if (e == DLLM_OK && hipStreamSynchronize(st) != hipSuccess) e = fail(DLLM_E_HIP, "hipStreamSynchronize failed");
+    (void)hipFree(w64);
+    (void)hipFree(w32);
+    if (e != DLLM_OK) return e;
+  }
   L.ready = true;
   return DLLM_OK;
+}
+
+dllm_status dllm_derive_proxy_basis(dllm_model* m, const void* w_v, int32_t iters, double* w_r_out, void* stream) {
+  CHK(check_model(m));
+  if (!w_v || !w_r_out) return fail(DLLM_E_ARG, "w_v/w_r_out is NULL");
+  if (iters < 0) return fail(DLLM_E_ARG, "iters < 0");
+  return derive_basis(m, w_v, iters, w_r_out, S(stream));
 }
 
 dllm_status dllm_init_head(dllm_model* m, const void* embed, const float* final_norm, const void* lm_head,

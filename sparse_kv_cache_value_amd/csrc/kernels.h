@@ -149,6 +149,18 @@ hipError_t launch_ps_commit(hipStream_t st, int B, int L, int blk, int W, int K,
                             int32_t* tokens, uint8_t* committed, int32_t* history, int32_t* n_history,
                             int32_t* n_new, int32_t* block_start, uint8_t* full_next, double* max_entropy);
 
+// ---- proxy basis derivation (basis.hip) ----
+// Subspace width p (r + oversampling, even, <= 136) and the fp64 workspace
+// launch_proxy_basis needs.
+int proxy_basis_width(int d, int nv, int r);
+size_t proxy_basis_workspace_doubles(int d, int nv, int r);
+// wr [d][r] fp64 = U_r S_r of W [d][nv] (storage dtype) by randomised
+// subspace iteration (iters power steps) and Rayleigh-Ritz; status[0] is set
+// to 1 when a Cholesky pivot was not positive (rank-deficient subspace).
+hipError_t launch_proxy_basis(hipStream_t st, bool bf16, int d, int nv, int r, int iters, const void* W, double* wr,
+                              double* ws, int32_t* status);
+hipError_t launch_f64_to_f32(hipStream_t st, size_t n, const double* src, float* dst);
+
 // ---- diagnostics (probe.hip) ----
 // bytes must be a positive multiple of stream_probe_quantum(grid, depth);
 // depth is 4 or 8 loads of 16 bytes in flight per thread; out holds grid words.

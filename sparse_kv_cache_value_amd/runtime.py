@@ -38,7 +38,7 @@ class Model:
         self.h = B.dllm_create(dims_of(cfg, max_batch))
         for l in range(cfg.n_layers):
             w = layers[l] if layers is not None else inputs.layer_weights(cfg, l, self.device, gain_std)
-            w = {k: v.to(self.device).contiguous() for k, v in w.items()}
+            w = {k: (v.to(self.device).contiguous() if v is not None else None) for k, v in w.items()}
             B.dllm_init_layer(self.h, l, w)
             torch.cuda.current_stream().synchronize()
             del w
