@@ -248,6 +248,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the short per-config runs (C1, C2, C4, C5) reported under other_configs")
+    ap.add_argument("--config", choices=sorted(set(WORKLOADS) - {"C3"}),
+                    help="only the per-config sparse-step figures of this config (--steps timed steps, "
+                         "--warmup untimed), printed as one JSON line; for profiling one config")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 256 MiB device copy before the timed steps (untimed), the reference kernel for "
                          "the HBM byte counters")
@@ -259,6 +262,11 @@ def main():
 
     import torch
     _ensure_built()
+    if args.config:
+        torch.cuda.set_device(0)
+        print(json.dumps({"config": args.config, **bench_config(args.config, args.steps, args.warmup,
+                                                                achievable_read_gbs())}), flush=True)
+        return
     from sparse_kv_cache_value_amd import binding as B
     from sparse_kv_cache_value_amd import configs, runtime
 

@@ -115,9 +115,31 @@ def traffic(fetch_csv: str, write_csv: str, nsteps: int = 3) -> dict:
             "traffic_bytes_per_launch": round(fetch + write), "source_hash": gemm_source_hash()}
 
 
+def sq_table(path: str, top: int = 10) -> str:
+    """Per-kernel ratios from one rocprofv3 --pmc pass of SQ counters:
+    SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES) (share of SIMD cycles the
+    matrix pipe is busy, 4 SIMDs per CU), and SQ_WAIT_ANY, SQ_WAIT_INST_LDS,
+    SQ_ACTIVE_INST_LDS over SQ_WAVE_CYCLES (share of wave cycles waiting on any
+    counter, waiting on LDS, issuing LDS)."""
+    rows = list(csv.DictReader(open(path)))
+    agg, disp = defaultdict(lambda: defaultdict(float)), defaultdict(set)
+    for r in rows:
+        n = _name(r["Kernel_Name"])
+        agg[n][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[n].add(r["Dispatch_Id"])
+    out = [f"{'kernel':48s} {'dispatches':>10s} {'mfma_busy':>9s} {'wait_any':>8s} {'wait_lds':>8s} {'lds_issue':>9s}"]
+    for n, c in sorted(agg.items(), key=lambda x: -x[1].get("SQ_WAVE_CYCLES", 0.0))[:top]:
+        wc = max(c["SQ_WAVE_CYCLES"], 1.0)
+        out.append(f"{n[:48]:48s} {len(disp[n]):10d} {c['SQ_VALU_MFMA_BUSY_CYCLES'] / max(4 * c['SQ_BUSY_CU_CYCLES'], 1):9.3f} "
+                   f"{c['SQ_WAIT_ANY'] / wc:8.3f} {c['SQ_WAIT_INST_LDS'] / wc:8.3f} {c['SQ_ACTIVE_INST_LDS'] / wc:9.3f}")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "kernels":
         print(kernels(sys.argv[2], int(sys.argv[3]) if len(sys.argv) > 3 else 10))
+    elif len(sys.argv) >= 3 and sys.argv[1] == "sq":
+        print(sq_table(sys.argv[2]))
     elif len(sys.argv) >= 4 and sys.argv[1] == "traffic":
         print(json.dumps(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]) if len(sys.argv) > 4 else 3), indent=1))
     else:
