@@ -1,0 +1,123 @@
+"""Full-size headline workload: the LLaDA-8B-shaped model (32 layers,
+d = 4096, 32 x 128 heads, SwiGLU 12288, vocab 126464), batch 1, L = 1024
+(512 prompt + 512 masked), the split-Gaussian rho(l) (k = 45..283 rows per
+layer) with forced = current block + 32 recent.  After a full pass and two
+sparse steps of dllm_step (the launch configuration bench.py times), one more
+sparse step runs through the C-ABI entry points with the oracle in shadow
+mode on layers 0, 15 (k = 283, the widest GEMM tiling) and 31 (k = 45 below
+the 64 forced rows): drift scores, the index set, the refreshed rows of
+H, K and V, then the LM-head statistics and the commit.  A copy of the state
+stepped by dllm_step must equal the entry-point result bit for bit."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import assert_close, assert_same_selection, commit_band, say, unpack_k, unpack_v
+from helpers import np_weights, spec_of
+from sparse_kv_cache_value_amd import binding as B
+from sparse_kv_cache_value_amd import configs, inputs, runtime
+
+pytestmark = pytest.mark.gpu
+
+
+def _slice(st, l):
+    torch.cuda.synchronize()
+    L = st.cfg.seq_len
+    return {
+        "x": st.hidden[l, 0].float().cpu().numpy(),
+        "h": st.hidden[l + 1, 0].float().cpu().numpy(),
+        "K": unpack_k(st.k_cache[l:l + 1, 0:1].float().cpu())[0, 0, :L],
+        "V": unpack_v(st.v_cache[l:l + 1, 0:1].float().cpu())[0, 0, :L],
+        "Pr": st.proxy_ref[l, 0].cpu().numpy(),
+        "Pc": st.proxy_cur[l, 0].cpu().numpy(),
+        "score": st.score[l, 0].cpu().numpy(),
+    }
+
+
+def test_c3_full_size_sampled():
+    cfg = configs.C3
+    spec = spec_of(cfg)
+    N, L = cfg.n_layers, cfg.seq_len
+    check = (0, 15, N - 1)
+    say("== C3: building the 32-layer model on the GPU")
+    model = runtime.Model(cfg, "cuda")
+    W = {l: np_weights(inputs.layer_weights(cfg, l, "cuda")) for l in check}
+    head = np_weights(inputs.head_weights(cfg, "cuda"))
+    torch.cuda.empty_cache()
+    st = runtime.State(cfg)
+    runtime.step(model, st, mode=B.DLLM_MODE_FULL)
+    for _ in range(2):
+        runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False)
+    twin = runtime.State(cfg)
+    for k_, v in st.tensors().items():
+        getattr(twin, k_).copy_(v)
+    runtime.step(model, twin, mode=B.DLLM_MODE_SPARSE, want_result=False)
+    say("C3: full pass + 2 sparse steps done; shadow-checked step through the entry points")
+    dev = "cuda"
+    forced = torch.zeros((1, L), dtype=torch.uint8, device=dev)
+    B.dllm_forced_set(model.h, st, runtime.FORCED_RULE[cfg.forced], cfg.recent_k, forced)
+    fr = forced.cpu().numpy().astype(bool)[0]
+    nh, nn = int(st.n_history[0]), int(st.n_new[0])
+    hist = st.history.cpu().numpy()[0]
+    rows0 = torch.zeros((1, L), dtype=torch.int32)
+    rows0[0, :nn] = torch.from_numpy(hist[nh - nn:nh].copy())
+    pi, pn, pmax = rows0.to(dev), torch.tensor([nn], dtype=torch.int32, device=dev), min(L, cfg.block_len)
+    idx = [torch.zeros((1, L), dtype=torch.int32, device=dev) for _ in range(2)]
+    n = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(2)]
+    committed0 = st.committed.cpu().numpy().astype(bool)[0]
+    bs0 = int(st.block_start[0])
+    fmax = cfg.block_len + cfg.recent_k
+    B.dllm_embed(model.h, st, pi, pn)
+    for l in range(N):
+        pre = _slice(st, l) if l in check else None
+        B.dllm_drift_score(model.h, l, st, pi, pn, pmax)
+        k = oracle.budget_k(cfg.rho[l], L)
+        mid = _slice(st, l) if l in check else None
+        B.dllm_select(model.h, l, st, forced, None, cfg.rho[l], idx[l & 1], n[l & 1])
+        rmax = min(L, max(k, fmax))
+        B.dllm_sparse_layer(model.h, l, st, idx[l & 1], n[l & 1], rmax)
+        if pre is not None:
+            post = _slice(st, l)
+            # drift of the rows whose input changed, against the proxy cached at their last refresh
+            C = oracle.proxy(pre["x"], W[l]["attn_norm"], W[l]["w_proxy"])
+            changed = pi.cpu().numpy()[0][:int(pn.cpu()[0])]
+            sc = mid["score"].copy()
+            sc_or = oracle.drift(C[changed], pre["Pr"][changed])
+            assert np.all(np.abs(sc[changed] - sc_or) <= 1e-10 * np.maximum(sc_or, 1e-300) + 1e-15), f"l={l} drift"
+            I_gpu = idx[l & 1].cpu().numpy()[0][:int(n[l & 1].cpu()[0])]
+            I_or = oracle.select(sc, fr, k)
+            band = assert_same_selection(I_gpu, I_or, sc, fr, k, f"C3 l={l}")
+            Kx, Vx, Hx = pre["K"].copy(), pre["V"].copy(), pre["h"].copy()
+            oracle.sparse_layer(pre["x"], Kx, Vx, Hx, I_gpu, W[l], spec)
+            mask = np.zeros(L, bool)
+            mask[I_gpu] = True
+            e = assert_close(post["h"][mask], Hx[mask], 2e-2, f"C3 l={l} sparse H")
+            assert_close(post["K"][mask], Kx[mask], 2e-2, f"C3 l={l} K rows")
+            assert_close(post["V"][mask], Vx[mask], 2e-2, f"C3 l={l} V rows")
+            assert np.array_equal(post["h"][~mask], pre["h"][~mask]), "rows outside I changed"
+            assert np.array_equal(post["Pr"][mask], post["Pc"][mask])
+            say(f"C3 l={l}: |I|={len(I_gpu)} (k={k}) band={band} H rel err {e:.2e}")
+        pi, pn, pmax = idx[l & 1], n[l & 1], rmax
+    stats = torch.zeros((1, cfg.block_len, 4), dtype=torch.float64, device=dev)
+    B.dllm_lm_head(model.h, st, stats)
+    B.dllm_commit(model.h, st, cfg.conf_threshold, cfg.tau)
+    rows = np.arange(bs0, bs0 + cfg.block_len)
+    so = oracle.lm_stats(st.hidden[N, 0].float().cpu().numpy()[rows], head["final_norm"], head["lm_head"], spec)
+    sg = stats.cpu().numpy()[0]
+    assert np.max(np.abs(sg[:, 0] - so["m"])) <= 1e-5 * np.max(np.abs(so["logits"]))
+    ent = np.log(sg[:, 2]) - sg[:, 3] / sg[:, 2]
+    assert np.max(np.abs(ent - so["entropy"])) <= 1e-5
+    band = commit_band(so, None, cfg.conf_threshold)
+    pos, tok, _ = oracle.commit(rows, so["conf"], so["argmax"], so["entropy"], committed0, cfg.conf_threshold)
+    got = [int(p) for p in st.history.cpu().numpy()[0][nh:int(st.n_history[0])]]
+    if not ({int(rows[j]) for j in band} & set(pos + got)):
+        assert got == pos and [int(st.tokens[0, p]) for p in pos] == tok
+    say(f"C3 commit: {got}")
+    torch.cuda.synchronize()
+    for k_, v in st.tensors().items():
+        assert torch.equal(v, getattr(twin, k_)), f"dllm_step differs from the entry points in {k_}"
+    model.close()
