@@ -92,7 +92,7 @@ hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, in
 // activation of the next GEMM.
 // ---------------------------------------------------------------------------
 template <int MTW, int KS, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const u32x4* __restrict__ Ap, int MTt,
+__global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel(const u32x4* __restrict__ Ap, int MTt,
                                                            const u32x4* __restrict__ Wp, float* __restrict__ out,
                                                            uint16_t* __restrict__ act, int MTt_out,
                                                            const int32_t* __restrict__ n_sel, int B, int K, int N,
@@ -237,12 +237,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const u32x4* __restri
   }
 }
 
+// Row tiles per wave: 384-row blocks (3) unless 256-row blocks (2, two
+// workgroups per CU) leave fewer padded row tiles (measured: a 1024-row full
+// pass -21 %, 2624 rows +8 % with 256-row blocks).
 static int mtw_for_rows(int max_rows) {
   if (max_rows <= 128) return 1;
   if (max_rows <= 256) return 2;
-  return 3;
+  const int t = (max_rows + 31) / 32;
+  const int b3 = (t + 11) / 12, b2 = (t + 7) / 8;
+  return t * 12 * b3 > t * 8 * b2 ? 2 : 3;  // t/(8 b2) > t/(12 b3)
 }
-static int ks_for(int) { return 4; }
+// k16 steps per chunk: 2 for 2 row tiles per wave (fewer registers: two
+// waves per SIMD), else 4.
+static int ks_for(int mtw) { return mtw == 2 ? 2 : 4; }
 
 template <int MTW, int KS, int EPI>
 static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
@@ -276,8 +283,9 @@ int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
   int best_s = 1;
   for (int s = 1; s <= 32; s *= 2) {
     if (K % (s * 32 * ks) != 0) break;  // an even number of chunks per split
-    const int waves = (base * s + n_cu - 1) / n_cu;
-    const double eff = (double)base * s / ((double)waves * n_cu);
+    const int slots = mtw * ks <= 4 ? 2 * n_cu : n_cu;  // workgroups resident at once (two when they fit)
+    const int waves = (base * s + slots - 1) / slots;
+    const double eff = (double)base * s / ((double)waves * slots);
     // weight stream at the achieved occupancy + split partial round trip
     const double cost = wbytes / eff + (s > 1 ? 2.0 * 4.0 * s * (double)max_rows * N : 0.0);
     if (cost < best * 0.999) {
@@ -305,11 +313,11 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
   launch_cfg<MTW, KS, EPI>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows)
   if (act == nullptr) {
     if (mtw == 1) return GL(1, 4, 0);
-    if (mtw == 2) return GL(2, 4, 0);
+    if (mtw == 2) return GL(2, 2, 0);
     return GL(3, 4, 0);
   }
   if (mtw == 1) return GL(1, 4, 1);
-  if (mtw == 2) return GL(2, 4, 1);
+  if (mtw == 2) return GL(2, 2, 1);
   return GL(3, 4, 1);
 #undef GL
 }
