@@ -243,7 +243,7 @@ dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int 
   Prof prof(m, st, cls, (double)K * N * m->esize + (double)max_rows * K * m->esize + (double)max_rows * N * 4.0,
             2.0 * max_rows * (double)K * N);
   if (m->bf16) {
-    // up to 192 rows: the weight-streaming kernel, when the shape suits it
+    // up to 288 rows: the weight-streaming kernel, when the shape suits it
     int ss = gemm_stream_pick_splits(max_rows, K, N, m->n_cu, act != nullptr, MTt);
     if (ss > 0 && !act && (size_t)ss * max_rows * N > out_floats) ss = 0;
     if (ss > 0) {

@@ -323,7 +323,7 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming bf16 GEMM for up to 384 rows (12 row tiles).
+// Weight-streaming bf16 GEMM for up to 288 rows (9 row tiles).
 //
 // Workgroup = 4 waves and a 128-column slab; wave w owns column tile w of the
 // slab and every row tile.  Each wave streams its own weight tile straight
@@ -345,11 +345,11 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
 // they wait at least as long as needed.  EPI as above.
 // ---------------------------------------------------------------------------
 constexpr int GS_KC = 4;  // k16 steps per activation chunk
-constexpr int GS_MAXMT = 12;
+constexpr int GS_MAXMT = 9;
 
 template <int MT>
 struct StreamShape {
-  static constexpr int NS = MT <= 9 ? 4 : 3;  // activation ring slots (chunks)
+  static constexpr int NS = 4;  // activation ring slots (chunks)
   static constexpr int P = NS - 1;             // chunks requested ahead
   static constexpr int NW = 4;  // chunks per weight-ring turn (ring depth GS_KC * NW steps)
   // VMEM operations issued after the request of chunk c+1 (step 0 of chunk
@@ -546,184 +546,6 @@ static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, c
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// The same stream with a 2x2 wave grid: waves 2p and 2p+1 share column tiles
-// 2p and 2p+1 of the slab, and split the row tiles (MTH each).  Each
-// activation fragment read from LDS feeds two MFMAs, halving the LDS read
-// traffic that limits the one-tile-per-wave layout at many row tiles; both
-// waves of a pair load the pair's weight fragments (ordinary loads, so the
-// second one is served by L2).  Gate and up tiles of the fused SwiGLU GEMM
-// sit in the same wave.  Requests, waits and barriers as above, with 2 MTH
-// requests per wave per chunk and 2 weight loads per step.
-// ---------------------------------------------------------------------------
-template <int MTH>
-struct QuadShape {
-  static constexpr int MT = 2 * MTH;
-  static constexpr int NS = MT <= 8 ? 4 : 3;
-  static constexpr int P = NS - 1;
-  static constexpr int REQ = 2 * MTH;  // DMA requests per wave per chunk
-  static constexpr int DMA_AFTER = 2 * GS_KC + (P - 2) * (REQ + 2 * GS_KC) + REQ + 2 * (GS_KC - 1);
-  static constexpr int WAIT = DMA_AFTER - 2;
-  static constexpr size_t LDS = (size_t)NS * GS_KC * MT * 64 * 16;
-  static_assert(WAIT >= 0 && WAIT < 64, "vmcnt field");
-  static_assert(LDS <= 160 * 1024, "LDS");
-};
-#define GS_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
-template <int MTH, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_stream_quad_kernel(const u32x4* __restrict__ Ap, int MTt,
-                                                       const u32x4* __restrict__ Wp, float* __restrict__ out,
-                                                       uint16_t* __restrict__ act, int MTt_out,
-                                                       const int32_t* __restrict__ n_sel, int B, int K, int N,
-                                                       int kps, int n_slabs, int total, int cap) {
-  using S = QuadShape<MTH>;
-  constexpr int MT = S::MT, NS = S::NS, P = S::P;
-  extern __shared__ u32x4 lds[];
-  constexpr int ABUF = GS_KC * MT * 64;
-  const int G = gridDim.x;
-  const int w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  if (w >= total) return;
-  const int slab = w % n_slabs, split = w / n_slabs;
-  const int M = total_rows(n_sel, B, cap);
-  if (M <= 0) return;
-  const int m_tiles = (M + 31) >> 5;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cp = wid >> 1, rh = wid & 1;
-  const int NT = N >> 5, KT = K >> 4;
-  const int nt0 = min(slab * 4 + 2 * cp, NT - 1), nt1 = min(slab * 4 + 2 * cp + 1, NT - 1);
-  const int kt0 = (split * kps) >> 4;
-  constexpr int GS_D = GS_KC * 4;
-  const int nsteps = kps >> 4, nch = nsteps / GS_KC, nsup = nsteps / GS_D;
-  const u32x4* wsrc0 = Wp + ((size_t)nt0 * KT + kt0) * 64 + lane;
-  const u32x4* wsrc1 = Wp + ((size_t)nt1 * KT + kt0) * 64 + lane;
-  const unsigned voff = (unsigned)lane * 16u;
-  auto request_a = [&](int c) {
-    const int cc = min(c, nch - 1);
-    const int slot = c % NS;
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-#pragma unroll
-    for (int i = 0; i < S::REQ; ++i) {
-      const int f = wid * S::REQ + i;  // fragment (step f / MT, row tile f % MT) of the chunk
-      const int stp = f / MT, mt = f % MT;
-      const u32x4* g = Ap + ((size_t)(kt0 + cc * GS_KC + stp) * MTt + min(mt, m_tiles - 1)) * 64;
-      const unsigned l = (unsigned)(uintptr_t)(lds_void_t*)&lds[slot * ABUF + f * 64];
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(l)),
-                   "v"(voff), "s"(uniform_ptr(g))
-                   : "memory", "m0");
-    }
-#pragma clang diagnostic pop
-  };
-  auto read_af = [&](int c, int st, u32x4* dst) {
-    const int slot = c % NS;
-#pragma unroll
-    for (int i = 0; i < MTH; ++i) dst[i] = lds[slot * ABUF + (st * MT + rh * MTH + i) * 64 + lane];
-  };
-  f32x16_t acc[2][MTH];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int i = 0; i < MTH; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[q][i][e] = 0.f;
-#pragma unroll
-  for (int c = 0; c < P; ++c) request_a(c);
-  u32x4 wr0[GS_D], wr1[GS_D];
-#pragma unroll
-  for (int j = 0; j < GS_D; ++j) {
-    wr0[j] = wsrc0[(size_t)min(j, nsteps - 1) * 64];
-    wr1[j] = wsrc1[(size_t)min(j, nsteps - 1) * 64];
-  }
-  GS_WAIT_VM_LGKM0(0);
-  __builtin_amdgcn_s_barrier();
-  u32x4 af[2][MTH];
-  read_af(0, 0, af[0]);
-  for (int sc = 0; sc < nsup; ++sc) {
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int c = sc * 4 + cc;
-#pragma unroll
-      for (int st = 0; st < GS_KC; ++st) {
-        const int j = cc * GS_KC + st;
-        const int s = c * GS_KC + st;
-        if (st + 1 < GS_KC) read_af(c, st + 1, af[(j + 1) & 1]);
-        else read_af(c + 1, 0, af[(j + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, wr0[j]);
-        const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, wr1[j]);
-#pragma unroll
-        for (int i = 0; i < MTH; ++i) {
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, af[j & 1][i]);
-          acc[0][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[0][i], 0, 0, 0);
-          acc[1][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[1][i], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (st == 0) request_a(c + P);
-        __builtin_amdgcn_sched_barrier(0);
-        wr0[j] = wsrc0[(size_t)min(s + GS_D, nsteps - 1) * 64];
-        wr1[j] = wsrc1[(size_t)min(s + GS_D, nsteps - 1) * 64];
-        __builtin_amdgcn_sched_barrier(0);
-        if (st == GS_KC - 2) {
-          // as in gemm_stream_kernel: chunk c+1 landed, chunk c reads done
-          GS_WAIT_VM_LGKM0(S::WAIT);
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-  }
-  GS_WAIT_VM_LGKM0(0);
-  if constexpr (EPI == 0) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (slab * 4 + 2 * cp + q >= NT) continue;
-      const int ncol = (slab * 4 + 2 * cp + q) * 32 + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < MTH; ++i) {
-        const int mrow = (rh * MTH + i) * 32 + (lane >> 5) * 4;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = mrow + (e >> 2) * 8 + (e & 3);
-          if (m < M) out[((size_t)split * M + m) * N + ncol] = acc[q][i][e];
-        }
-      }
-    }
-  } else {
-    if (slab * 4 + 2 * cp + 1 < NT) {
-      const int f = (slab * 2 + cp) * 32 + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < MTH; ++i) {
-        const int mrow = (rh * MTH + i) * 32 + (lane >> 5) * 4;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = mrow + (e >> 2) * 8 + (e & 3);
-          if (m < M) {
-            const float g = acc[0][i][e], u = acc[1][i][e];
-            act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
-          }
-        }
-      }
-    }
-  }
-}
-#undef GS_WAIT_VM_LGKM0
-template <int MTH, int EPI>
-static hipError_t quad_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
-                           uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
-                           int n_slabs, int total, int cap) {
-  static bool attr_set = false;
-  const size_t lds = QuadShape<MTH>::LDS;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_stream_quad_kernel<MTH, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((gemm_stream_quad_kernel<MTH, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
-                     (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, cap);
-  return hipGetLastError();
-}
-
 static int stream_mt(int max_rows) {
   const int t = (max_rows + 31) / 32;
   return t <= GS_MAXMT ? (t < 1 ? 1 : t) : -1;
@@ -731,7 +553,7 @@ static int stream_mt(int max_rows) {
 
 // Split count for the streaming kernel: K must split into multiples of 256;
 // the largest split whose workgroup count still fits the chip in one pass (one
-// per CU).  0 when the shape does not suit the kernel (more than 384 rows, or
+// per CU).  0 when the shape does not suit the kernel (more than 288 rows, or
 // more row tiles than the activation buffer holds).
 int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, int MTt) {
   const int mt = stream_mt(max_rows);
@@ -762,22 +584,13 @@ hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N,
                                     max_rows)                                                                     \
                : stream_cfg<MT_, 0>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, \
                                     max_rows);
-#define GQL(MT_, MTH_)                                                                                            \
-  case MT_:                                                                                                       \
-    return act ? quad_cfg<MTH_, 1>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total,  \
-                                   max_rows)                                                                      \
-               : quad_cfg<MTH_, 0>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total,  \
-                                   max_rows);
-  // one column tile per wave up to 9 row tiles; beyond, the LDS reads of the
-  // activation fragments dominate and the 2x2 grid wins despite its doubled
-  // weight-fragment requests (measured with weights streamed from HBM)
+  // one column tile per wave up to 9 row tiles; more rows go to the
+  // row-blocked kernel (measured faster from 10 row tiles on)
   switch (mt) {
     GSL(1) GSL(2) GSL(3) GSL(4) GSL(5) GSL(6) GSL(7) GSL(8) GSL(9)
-    GQL(10, 5) GQL(11, 6) GQL(12, 6)
     default: return hipErrorInvalidValue;
   }
 #undef GSL
-#undef GQL
 }
 
 // ---------------------------------------------------------------------------

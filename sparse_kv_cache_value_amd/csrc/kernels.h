@@ -72,7 +72,7 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
                             const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
                             int MTt_out);
 int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu);
-// Streaming variant for up to 384 rows (N % 128 == 0, K % 256 == 0); `splits`
+// Streaming variant for up to 288 rows (N % 128 == 0, K % 256 == 0); `splits`
 // from gemm_stream_pick_splits (0 there = use launch_gemm_bf16).
 int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, int MTt);
 hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,

@@ -26,6 +26,7 @@ pytestmark = pytest.mark.gpu
 PC = medium_cfg(name="medium-polestar-commit", score=configs.SCORE_POLESTAR, forced=configs.FORCED_BLOCK,
                 recent_k=0, seed=31, batch=2, seq_len=224, prompt_len=96, top_clusters=8,
                 conf_threshold=0.00125, polestar_commit=True, commit_alpha=1e-5, n_steps=10)
+# (test_polestar_commit_decode replaces conf_threshold by a data-derived one)
 
 
 def _ps_host(pst):
@@ -113,6 +114,18 @@ def test_polestar_commit_decode():
     st = runtime.State(cfg)
     pst = runtime.PolestarState(cfg)
     runtime.step(model, st, mode=B.DLLM_MODE_FULL, polestar_state=pst)
+    # threshold at the 80th percentile of the next block's confidences after
+    # the full pass (random weights keep them near 1/V), so that suffix
+    # commits can happen
+    stats = torch.zeros((cfg.batch * cfg.block_len, 4), dtype=torch.float64, device="cuda")
+    bs = st.block_start.clone()
+    st.block_start.add_(cfg.block_len)
+    B.dllm_lm_head(model.h, st, stats)
+    st.block_start.copy_(bs)
+    thr = float(np.quantile(1.0 / stats[:, 2].cpu().numpy(), 0.8))
+    cfg = cfg.with_(conf_threshold=thr)
+    model.cfg = cfg
+    say(f"commit threshold {thr:.6e}")
     counts = {"drift": 0, "suffix": 0, "threshold": 0, "fallback": 0}
     for t in range(cfg.n_steps):
         before, pb = Snap(st), _ps_host(pst)
