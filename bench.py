@@ -366,7 +366,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemm_stream_kernel, gemm_stream_quad_kernel, gemm_bf16_kernel (layer GEMMs + LM head)",
+            "kernel": "gemm_stream_kernel, gemm_bf16_kernel (layer GEMMs + LM head)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
