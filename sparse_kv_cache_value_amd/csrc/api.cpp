@@ -366,8 +366,15 @@ dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int n
     Prof prof(m, st, DLLM_PROF_LMHEAD,
               (double)d.d_model * d.vocab * 2.0 + (double)B * blk * d.d_model * 2.0 + (double)B * blk * d.vocab * 4.0,
               2.0 * B * blk * (double)d.d_model * d.vocab);
-    HIPCHK(launch_gemm_bf16(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
-                            (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0));
+    // up to two row tiles the weight-streaming kernel reads W_lm faster (one
+    // split: the logits are written once, in the same [M][V] layout)
+    const int ss = B * blk <= 64 ? gemm_stream_pick_splits(B * blk, d.d_model, d.vocab, m->n_cu, false, m->lm_MTt) : 0;
+    if (ss == 1)
+      HIPCHK(launch_gemm_stream(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
+                                (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0));
+    else
+      HIPCHK(launch_gemm_bf16(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
+                              (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0));
     prof.done();
   } else {
     CHK(gemm(m, st, B * blk, 1, d.d_model, d.vocab, m->A_lm, m->lm_head, m->lm_rows, m->logits, cap, &sp,
