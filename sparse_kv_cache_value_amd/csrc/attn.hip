@@ -14,7 +14,8 @@
 // V loads in flight during the current tile's arithmetic), computing
 // S^T = K Q^T (so a query's scores sit in one lane pair and the row max/sum need
 // one cross-lane exchange) and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16.
-// The eight partial results are merged in LDS by a fixed-order tree.  Otherwise a
+// The eight partial results are merged in one LDS round, each wave combining
+// and storing an eighth of the output in a fixed wave order.  Otherwise a
 // reference kernel (one wave per query row and head).
 #include "common.h"
 #include "kernels.h"
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   constexpr int KS = DH / 16;  // k-steps of S^T
   constexpr int DT = DH / 32;  // d-tiles of O^T
   __shared__ float ms[ATT_NW][32], ls[ATT_NW][32];
-  __shared__ float ox[ATT_NW / 2][DT][16][64];  // element i of lane l at [i][l]: no bank conflicts
+  __shared__ float ox[ATT_NW][DT][16][64];  // element i of lane l at [i][l]: no bank conflicts
   // Workgroups are dealt round-robin to the 8 XCDs; remap so that the query
   // tiles of one head run on one XCD and share its K/V through that L2.
   const int G = gridDim.x;  // ntq * Hq rounded up to a multiple of 8
@@ -204,62 +205,51 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
     }
   }
 
-  // merge the waves' partial softmax states: a fixed-order tree in LDS
+  // merge the waves' partial softmax states in one LDS round: every wave
+  // writes (m, l, O), then wave w combines the output groups (dt, q4) it owns
+  // from all eight waves in a fixed order and stores them
+  static_assert((DT * 4) % ATT_NW == 0, "output groups per wave");
+  constexpr int GPW = DT * 4 / ATT_NW;
   if (lane < 32) {
     ms[wv][ln] = m_run;
     ls[wv][ln] = l_run;
   }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ox[wv][dt][i][lane] = o[dt][i];
   __syncthreads();
   float mg = ms[0][ln];
 #pragma unroll
   for (int w2 = 1; w2 < ATT_NW; ++w2) mg = fmaxf(mg, ms[w2][ln]);
-  float lg = 0.f;
+  float fw[ATT_NW], lg = 0.f;
 #pragma unroll
-  for (int w2 = 0; w2 < ATT_NW; ++w2) lg += ls[w2][ln] * exp2f(ms[w2][ln] - mg);
-  const float f = exp2f(m_run - mg);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] *= f;
-#pragma unroll
-  for (int half = ATT_NW / 2; half >= 1; half >>= 1) {
-    if (wv >= half && wv < 2 * half) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ox[wv - half][dt][i][lane] = o[dt][i];
-    }
-    __syncthreads();
-    if (wv < half) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] += ox[wv][dt][i][lane];
-    }
-    __syncthreads();
+  for (int w2 = 0; w2 < ATT_NW; ++w2) {
+    fw[w2] = exp2f(ms[w2][ln] - mg);  // 0 for a wave without keys
+    lg += ls[w2][ln] * fw[w2];
   }
-  if (wv != 0) return;
   const float inv = 1.0f / lg;
   const int m = r0 + ln;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+  for (int gg = 0; gg < GPW; ++gg) {
+    const int g = wv * GPW + gg, dt = g >> 2, q4 = g & 3;
+    float mine[4], part[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float mine[4], part[4];
+    for (int e = 0; e < 4; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < ATT_NW; ++w2) acc += ox[w2][dt][q4 * 4 + e][lane] * fw[w2];
+      mine[e] = acc * inv;
+      part[e] = __shfl_xor(mine[e], 32, 64);
+    }
+    if ((q4 & 1) == hlf && qv) {
+      float v8[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        mine[e] = o[dt][q4 * 4 + e] * inv;
-        part[e] = __shfl_xor(mine[e], 32, 64);
+        v8[e] = hlf ? part[e] : mine[e];
+        v8[4 + e] = hlf ? mine[e] : part[e];
       }
-      if ((q4 & 1) == hlf && qv) {
-        float v8[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v8[e] = hlf ? part[e] : mine[e];
-          v8[4 + e] = hlf ? mine[e] : part[e];
-        }
-        store_a8(out, m, h * DH + dt * 32 + q4 * 8, MTt, Hq * DH, v8);
-      }
+      store_a8(out, m, h * DH + dt * 32 + q4 * 8, MTt, Hq * DH, v8);
     }
   }
 }
