@@ -183,6 +183,28 @@ struct Prof {
   }
 };
 
+// Event pair of one kernel launch of a class, stamped by the launch itself
+// (hipExtLaunchKernel): the kernel's own begin and end, with no marker packets
+// in the stream around it (diagnostics).
+struct ProfLaunch {
+  dllm_model* m;
+  int cls;
+  double bytes, flops;
+  LaunchEvents ev;
+  ProfLaunch(dllm_model* m_, int cls_, double bytes_, double flops_) : m(m_), cls(cls_), bytes(bytes_), flops(flops_) {
+    if (m->prof_on && ((m->prof_mask >> cls) & 1)) {
+      ev.start = Prof::get(m);
+      ev.stop = ev.start ? Prof::get(m) : nullptr;
+      if (!ev.stop) ev.start = nullptr;
+    }
+  }
+  // after a successful launch
+  void done() {
+    if (ev.start) m->prof_pending.push_back({ev.start, ev.stop, cls, bytes, flops});
+    ev = {};
+  }
+};
+
 int nq_of(const dllm_dims& d) { return d.n_q_heads * d.head_dim; }
 int nv_of(const dllm_dims& d) { return d.n_kv_heads * d.head_dim; }
 
@@ -240,15 +262,15 @@ dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int 
                  const int32_t* n_sel, float* out, size_t out_floats, int* splits, int cls = DLLM_PROF_GEMM,
                  int MTt = -1, void* act = nullptr) {
   if (MTt < 0) MTt = m->MTt;
-  Prof prof(m, st, cls, (double)K * N * m->esize + (double)max_rows * K * m->esize + (double)max_rows * N * 4.0,
-            2.0 * max_rows * (double)K * N);
+  ProfLaunch prof(m, cls, (double)K * N * m->esize + (double)max_rows * K * m->esize + (double)max_rows * N * 4.0,
+                  2.0 * max_rows * (double)K * N);
   if (m->bf16) {
     // up to 288 rows: the weight-streaming kernel, when the shape suits it
     int ss = gemm_stream_pick_splits(max_rows, K, N, m->n_cu, act != nullptr, MTt);
     if (ss > 0 && !act && (size_t)ss * max_rows * N > out_floats) ss = 0;
     if (ss > 0) {
       HIPCHK(launch_gemm_stream(st, max_rows, B, K, N, (const uint16_t*)A, MTt, (const uint16_t*)W, n_sel, out, ss,
-                                (uint16_t*)act, m->MTt));
+                                (uint16_t*)act, m->MTt, prof.ev));
       *splits = ss;
       prof.done();
       return DLLM_OK;
@@ -257,11 +279,11 @@ dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int 
     while (sp > 1 && (size_t)sp * max_rows * N > out_floats) sp /= 2;
     if (!act && (size_t)sp * max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
     HIPCHK(launch_gemm_bf16(st, max_rows, B, K, N, (const uint16_t*)A, MTt, (const uint16_t*)W, n_sel, out, sp,
-                            (uint16_t*)act, m->MTt));
+                            (uint16_t*)act, m->MTt, prof.ev));
     *splits = sp;
   } else {
     if ((size_t)max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
-    HIPCHK(launch_gemm_f32(st, max_rows, B, K, N, (const float*)A, (const float*)W, n_sel, out));
+    HIPCHK(launch_gemm_f32(st, max_rows, B, K, N, (const float*)A, (const float*)W, n_sel, out, prof.ev));
     *splits = 1;
   }
   prof.done();
@@ -363,18 +385,19 @@ dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int n
   int sp = 1;
   const size_t cap = (size_t)d.max_batch * 2 * d.block_len * d.vocab;
   if (m->bf16) {
-    Prof prof(m, st, DLLM_PROF_LMHEAD,
-              (double)d.d_model * d.vocab * 2.0 + (double)B * blk * d.d_model * 2.0 + (double)B * blk * d.vocab * 4.0,
-              2.0 * B * blk * (double)d.d_model * d.vocab);
+    ProfLaunch prof(m, DLLM_PROF_LMHEAD,
+                    (double)d.d_model * d.vocab * 2.0 + (double)B * blk * d.d_model * 2.0 +
+                        (double)B * blk * d.vocab * 4.0,
+                    2.0 * B * blk * (double)d.d_model * d.vocab);
     // up to two row tiles the weight-streaming kernel reads W_lm faster (one
     // split: the logits are written once, in the same [M][V] layout)
     const int ss = B * blk <= 64 ? gemm_stream_pick_splits(B * blk, d.d_model, d.vocab, m->n_cu, false, m->lm_MTt) : 0;
     if (ss == 1)
       HIPCHK(launch_gemm_stream(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
-                                (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0));
+                                (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0, prof.ev));
     else
       HIPCHK(launch_gemm_bf16(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
-                              (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0));
+                              (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0, prof.ev));
     prof.done();
   } else {
     CHK(gemm(m, st, B * blk, 1, d.d_model, d.vocab, m->A_lm, m->lm_head, m->lm_rows, m->logits, cap, &sp,

@@ -15,6 +15,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <hip/hip_ext.h>
+
 namespace dllm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -254,7 +256,7 @@ static int ks_for(int mtw) { return mtw == 2 ? 2 : 4; }
 template <int MTW, int KS, int EPI>
 static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
                              uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
-                             int row_blocks, int n_slabs, int total, int cap) {
+                             int row_blocks, int n_slabs, int total, int cap, LaunchEvents ev) {
   static bool attr_set = false;
   const size_t lds = (size_t)2 * KS * 4 * 64 * 16;
   if (!attr_set) {
@@ -263,8 +265,13 @@ static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, c
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
-                     (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, cap);
+  if (ev.start)
+    hipExtLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI>), dim3(grid), dim3(256), lds, st, ev.start, ev.stop, 0,
+                          (const u32x4*)A, MTt, (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks,
+                          n_slabs, total, cap);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
+                       (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, cap);
   return hipGetLastError();
 }
 
@@ -298,7 +305,7 @@ int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
 
 hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                             const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
-                            int MTt_out) {
+                            int MTt_out, LaunchEvents ev) {
   if (max_rows <= 0) return hipSuccess;
   const int mtw = mtw_for_rows(max_rows);
   const int ks = ks_for(mtw);
@@ -310,7 +317,7 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
   const int total = n_slabs * row_blocks * splits;
   const int grid = (total + 7) / 8 * 8;
 #define GL(MTW, KS, EPI) \
-  launch_cfg<MTW, KS, EPI>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows)
+  launch_cfg<MTW, KS, EPI>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows, ev)
   if (act == nullptr) {
     if (mtw == 1) return GL(1, 4, 0);
     if (mtw == 2) return GL(2, 2, 0);
@@ -532,7 +539,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
 template <int MT, int EPI>
 static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
                              uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
-                             int n_slabs, int total, int cap) {
+                             int n_slabs, int total, int cap, LaunchEvents ev) {
   static bool attr_set = false;
   const size_t lds = StreamShape<MT>::LDS;
   if (!attr_set) {
@@ -541,8 +548,13 @@ static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, c
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_stream_kernel<MT, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
-                     (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, cap);
+  if (ev.start)
+    hipExtLaunchKernelGGL((gemm_stream_kernel<MT, EPI>), dim3(grid), dim3(256), lds, st, ev.start, ev.stop, 0,
+                          (const u32x4*)A, MTt, (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs,
+                          total, cap);
+  else
+    hipLaunchKernelGGL((gemm_stream_kernel<MT, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
+                       (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, cap);
   return hipGetLastError();
 }
 
@@ -568,7 +580,7 @@ int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, in
 
 hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                               const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
-                              int MTt_out) {
+                              int MTt_out, LaunchEvents ev) {
   if (max_rows <= 0) return hipSuccess;
   const int mt = stream_mt(max_rows);
   if (mt < 0 || mt > MTt || N % 128 != 0 || splits < 1) return hipErrorInvalidValue;
@@ -581,9 +593,9 @@ hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N,
 #define GSL(MT_)                                                                                                  \
   case MT_:                                                                                                       \
     return act ? stream_cfg<MT_, 1>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, \
-                                    max_rows)                                                                     \
+                                    max_rows, ev)                                                                 \
                : stream_cfg<MT_, 0>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, \
-                                    max_rows);
+                                    max_rows, ev);
   // one column tile per wave up to 9 row tiles; more rows go to the
   // row-blocked kernel (measured faster from 10 row tiles on)
   switch (mt) {
@@ -641,10 +653,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 hipError_t launch_gemm_f32(hipStream_t st, int max_rows, int B, int K, int N, const float* A, const float* W,
-                           const int32_t* n_sel, float* out) {
+                           const int32_t* n_sel, float* out, LaunchEvents ev) {
   if (max_rows <= 0) return hipSuccess;
   dim3 grid((N + 63) / 64, (max_rows + 63) / 64);
-  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, A, W, n_sel, B, K, N, max_rows, out);
+  if (ev.start)
+    hipExtLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, ev.start, ev.stop, 0, A, W, n_sel, B, K, N, max_rows,
+                          out);
+  else
+    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, A, W, n_sel, B, K, N, max_rows, out);
   return hipGetLastError();
 }
 

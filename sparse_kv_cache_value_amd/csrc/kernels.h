@@ -61,23 +61,28 @@ hipError_t launch_select(hipStream_t st, int B, int L, int k, const double* scor
                          const uint8_t* full, int32_t* idx, int32_t* n);
 
 // ---- GEMMs (gemm.hip) ----
+// Optional event pair stamped by the GEMM launch itself (hipExtLaunchKernel:
+// the kernel's own begin and end, no marker packets around it); diagnostics.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
 // out[s][m][n] = sum_{k in split s} A[m][k] W[k][n] for m < sum(n_sel).
 hipError_t launch_gemm_f32(hipStream_t st, int max_rows, int B, int K, int N, const float* A,
-                           const float* W, const int32_t* n_sel, float* out);
+                           const float* W, const int32_t* n_sel, float* out, LaunchEvents ev = {});
 // bf16 weights pre-packed by launch_pack_bf16; `splits` from gemm_bf16_pick_splits.
 // A is packed (apack_off) with MTt row tiles.  act != NULL (one split, N a
 // multiple of 64, gate/up interleaved by 32 columns) writes SwiGLU(gate, up)
 // as a packed bf16 [M][N/2] activation with MTt_out row tiles instead of out.
 hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                             const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
-                            int MTt_out);
+                            int MTt_out, LaunchEvents ev = {});
 int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu);
 // Streaming variant for up to 288 rows (N % 128 == 0, K % 256 == 0); `splits`
 // from gemm_stream_pick_splits (0 there = use launch_gemm_bf16).
 int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, int MTt);
 hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                               const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
-                              int MTt_out);
+                              int MTt_out, LaunchEvents ev = {});
 // Padding (elements) a packed buffer needs past its end: for weights pass 1,
 // for packed activations the buffer's row-tile count.
 size_t gemm_pad_elems(int rows_tiles);
