@@ -382,3 +382,96 @@ def m_refresh_ignores_window(monkeypatch):
 def test_schedule_mutation_is_caught(monkeypatch, mutation):
     mutation(monkeypatch)
     assert _fails(pins.ALL_CHECKS), f"no pin catches {mutation.__name__}"
+
+
+# ---- EntropyCache gate, forced set, cached-proxy refresh (decode loop) ----
+import oracle.decode as od
+
+
+def _commit_variant(monkeypatch, emax_of):
+    """Threshold commit whose reported entropy is ``emax_of(entropy, picks, cand)``."""
+    orig = od.commit
+
+    def bad(rows, conf, argmax, entropy, committed, threshold):
+        pos, tok, _ = orig(rows, conf, argmax, entropy, committed, threshold)
+        picks = [j for j in range(len(rows)) if int(rows[j]) in pos]
+        cand = [j for j in range(len(rows)) if not committed[rows[j]]]
+        return pos, tok, emax_of(entropy, picks, cand)
+    monkeypatch.setattr(od, "commit", bad)
+
+
+def m_gate_zero_entropy(monkeypatch):
+    _commit_variant(monkeypatch, lambda e, p, c: 0.0)
+
+
+def m_gate_first_commit(monkeypatch):
+    _commit_variant(monkeypatch, lambda e, p, c: float(e[p[0]]) if p else 0.0)
+
+
+def m_gate_block_max(monkeypatch):
+    _commit_variant(monkeypatch, lambda e, p, c: max((float(e[j]) for j in c), default=0.0))
+
+
+def m_gate_nonstrict(monkeypatch):
+    orig = od.commit_block
+
+    def bad(st, head, spec, pol):
+        info = orig(st, head, spec, pol)
+        st.full_next = info["emax"] >= pol.tau
+        return info
+    monkeypatch.setattr(od, "commit_block", bad)
+
+
+def _forced_variant(monkeypatch, recent_of, with_block=True):
+    def bad(self, pol):
+        f = np.zeros(self.spec.seq_len, bool)
+        if pol.forced in ("block", "block+recent") and (with_block or pol.forced == "block"):
+            f[self.block_rows()] = True
+        if pol.forced == "block+recent" and pol.recent_k > 0:
+            f[recent_of(list(self.history), pol.recent_k)] = True
+        return f
+    monkeypatch.setattr(od.SeqState, "forced_set", bad)
+
+
+def m_forced_oldest(monkeypatch):
+    _forced_variant(monkeypatch, lambda h, k: h[:k])
+
+
+def m_forced_by_position(monkeypatch):
+    _forced_variant(monkeypatch, lambda h, k: sorted(h)[-k:])
+
+
+def m_forced_drops_block(monkeypatch):
+    _forced_variant(monkeypatch, lambda h, k: h[-k:], with_block=False)
+
+
+def _refresh_variant(monkeypatch, update):
+    def bad(x, K, V, H_out, P, W, spec, k, forced):
+        C = om.proxy(x, W["attn_norm"], W["w_proxy"])
+        s = om.drift(C, P)
+        I = np.arange(spec.seq_len) if k is None else om.select(s, forced, k)
+        om.sparse_layer(x, K, V, H_out, I, W, spec)
+        update(P, C, I)
+        return I, s, C
+    monkeypatch.setattr(od, "layer_refresh", bad)
+
+
+def m_refresh_every_row(monkeypatch):
+    def upd(P, C, I):
+        P[:] = C
+    _refresh_variant(monkeypatch, upd)
+
+
+def m_refresh_nothing(monkeypatch):
+    _refresh_variant(monkeypatch, lambda P, C, I: None)
+
+
+DECODE_MUTATIONS = [m_gate_zero_entropy, m_gate_first_commit, m_gate_block_max, m_gate_nonstrict,
+                    m_forced_oldest, m_forced_by_position, m_forced_drops_block,
+                    m_refresh_every_row, m_refresh_nothing]
+
+
+@pytest.mark.parametrize("mutation", DECODE_MUTATIONS, ids=lambda f: f.__name__)
+def test_decode_mutation_is_caught(monkeypatch, mutation):
+    mutation(monkeypatch)
+    assert _fails(pins.ALL_CHECKS), f"no pin catches {mutation.__name__}"
