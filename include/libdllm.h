@@ -203,6 +203,11 @@ typedef struct {
   const dllm_ce_params *ce;               /* host; non-NULL: commit with Confidence Extrapolation
                                              (dllm_commit_ce); not with Polestar-Commit */
   dllm_ce_state *ce_state;                /* with ce */
+  /* Optional inspection output (both NULL or both set): every layer's index
+   * set of this step, sets_out[l][b][0..n_sets_out[l][b]) ascending
+   * ([N][B][L] and [N][B], device). */
+  int32_t *sets_out;
+  int32_t *n_sets_out;
 } dllm_step_params;
 
 typedef struct {
@@ -375,10 +380,14 @@ dllm_status dllm_forced_set(dllm_model *m, const dllm_state *s, int32_t rule, in
  * (every row in a full pass), then per layer drift score, selection (every
  * row in a full pass) and sparse layer, then commit.  With
  * score = DLLM_SCORE_POLESTAR_KL a sparse step uses dllm_polestar_drift and
- * dllm_polestar_select instead of the value-proxy drift and top-k.  Mode FULL or SPARSE
- * applies to every sequence; AUTO runs a full pass for the sequences whose
- * full_next is set (the caller sets it before the first step, whose caches are
- * empty).  If res_h is non-NULL the call waits for the stream and fills it. */
+ * dllm_polestar_select instead of the value-proxy drift and top-k, and leaves
+ * proxy_ref and score untouched.  Mode FULL or SPARSE applies to every
+ * sequence; AUTO runs a full pass for the sequences whose full_next is set
+ * (the caller sets it before the first step, whose caches are empty).  With
+ * DLLM_SCORE_POLESTAR_KL, AUTO returns DLLM_E_UNSUPPORTED (nothing enqueued
+ * after the read of full_next) when full_next is set for some sequences but
+ * not all, and no periodic full pass is due.  If res_h is non-NULL the call
+ * waits for the stream and fills it. */
 dllm_status dllm_step(dllm_model *m, dllm_state *s, const dllm_step_params *p,
                       dllm_step_result *res_h, void *stream);
 

@@ -68,7 +68,8 @@ class DllmStepParams(ctypes.Structure):
                 ("conf_threshold", _f64), ("rho_h", ctypes.POINTER(_f64)), ("score", _i32),
                 ("polestar", ctypes.POINTER(DllmPolestarParams)),
                 ("polestar_state", ctypes.POINTER(DllmPolestarState)),
-                ("ce", ctypes.POINTER(DllmCEParams)), ("ce_state", ctypes.POINTER(DllmCEState))]
+                ("ce", ctypes.POINTER(DllmCEParams)), ("ce_state", ctypes.POINTER(DllmCEState)),
+                ("sets_out", _vp), ("n_sets_out", _vp)]
 
 
 class DllmStepResult(ctypes.Structure):
@@ -239,14 +240,19 @@ def dllm_polestar_commit(m: int, state, ps, params: DllmPolestarParams, conf_thr
 def dllm_step(m: int, state, mode: int, forced_rule: int, recent_k: int, tau: float, conf_threshold: float,
               rho, want_result: bool = True, stream=None, score: int = DLLM_SCORE_SPA_COS,
               polestar: Optional[DllmPolestarParams] = None, polestar_state=None,
-              ce: Optional[DllmCEParams] = None, ce_state=None) -> Optional[DllmStepResult]:
+              ce: Optional[DllmCEParams] = None, ce_state=None, sets_out=None,
+              n_sets_out=None) -> Optional[DllmStepResult]:
+    """sets_out [N][B][L] / n_sets_out [N][B] (int32 device tensors, both or
+    neither): every layer's index set of the step."""
     rho_arr = (_f64 * len(rho))(*[float(r) for r in rho])
     p = DllmStepParams(mode, forced_rule, recent_k, float(tau), float(conf_threshold),
                        ctypes.cast(rho_arr, ctypes.POINTER(_f64)), score,
                        ctypes.pointer(polestar) if polestar is not None else None,
                        ctypes.pointer(polestar_state.c) if polestar_state is not None else None,
                        ctypes.pointer(ce) if ce is not None else None,
-                       ctypes.pointer(ce_state.c) if ce_state is not None else None)
+                       ctypes.pointer(ce_state.c) if ce_state is not None else None,
+                       _p(sets_out) if sets_out is not None else None,
+                       _p(n_sets_out) if n_sets_out is not None else None)
     res = DllmStepResult() if want_result else None
     _check(lib().dllm_step(m, ctypes.byref(state.c), ctypes.byref(p),
                            ctypes.byref(res) if res is not None else None, _stream(stream)))

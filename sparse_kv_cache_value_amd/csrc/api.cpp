@@ -314,8 +314,10 @@ dllm_status do_drift(dllm_model* m, int layer, dllm_state* s, const int32_t* row
   return DLLM_OK;
 }
 
+// refresh_proxy: P <- C and score <- 0 on I (the value-proxy path; the
+// Polestar drift path keeps no value proxy and leaves both untouched)
 dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* idx, const int32_t* n, int max_rows,
-                      hipStream_t st) {
+                      hipStream_t st, bool refresh_proxy = true) {
   const dllm_dims& d = m->d;
   const int B = s->batch, L = d.seq_len, D = d.d_model, F = d.d_ffn;
   const int nq = nq_of(d), nv = nv_of(d);
@@ -365,7 +367,8 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
     Prof prof(m, st, DLLM_PROF_ROWS,
               sp * Mr * D * 4.0 + Mr * D * (4.0 + es) + Mr * d.proxy_rank * 16.0 + Mr * 8.0, Mr * D * sp);
     HIPCHK(launch_down_epilogue(st, m->bf16, max_rows, B, L, D, d.proxy_rank, sp, idx, n, m->part, m->hprime,
-                                hid(m, s, layer + 1), pcur(m, s, layer), pref(m, s, layer), score(m, s, layer)));
+                                hid(m, s, layer + 1), pcur(m, s, layer), refresh_proxy ? pref(m, s, layer) : nullptr,
+                                score(m, s, layer)));
     prof.done();
   }
   return DLLM_OK;
@@ -451,6 +454,16 @@ dllm_status do_polestar_commit(dllm_model* m, dllm_state* s, dllm_polestar_state
                           ps->drift_sum, ps->drift_cnt, s->tokens, s->committed, s->history, s->n_history, s->n_new,
                           s->block_start, s->full_next, s->max_entropy));
   prof.done();
+  return DLLM_OK;
+}
+
+// copy of layer l's index set into the caller's inspection buffers
+dllm_status save_sets(dllm_model* m, const dllm_state* s, const dllm_step_params* p, int l, const int32_t* idx,
+                      const int32_t* n, hipStream_t st) {
+  if (!p->sets_out) return DLLM_OK;
+  const size_t BL = (size_t)s->batch * m->d.seq_len;
+  HIPCHK(hipMemcpyAsync(p->sets_out + (size_t)l * BL, idx, BL * 4, hipMemcpyDeviceToDevice, st));
+  HIPCHK(hipMemcpyAsync(p->n_sets_out + (size_t)l * s->batch, n, (size_t)s->batch * 4, hipMemcpyDeviceToDevice, st));
   return DLLM_OK;
 }
 
@@ -591,7 +604,10 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
     g_err = keep;
     return st;
   };
-  if (hipGetDevice(&m->device) != hipSuccess) return cleanup(fail(DLLM_E_HIP, "hipGetDevice failed"));
+  {
+    const hipError_t e = hipGetDevice(&m->device);
+    if (e != hipSuccess) return cleanup(fail(DLLM_E_HIP, "hipGetDevice: %s", hipGetErrorString(e)));
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, m->device) == hipSuccess && prop.multiProcessorCount > 0)
     m->n_cu = prop.multiProcessorCount;
@@ -943,6 +959,8 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     return fail(DLLM_E_ARG, "unknown forced rule %d", p->forced_rule);
   if (p->recent_k < 0) return fail(DLLM_E_ARG, "recent_k < 0");
   if (std::isnan(p->tau) || std::isnan(p->conf_threshold)) return fail(DLLM_E_ARG, "threshold is NaN");
+  if ((p->sets_out == nullptr) != (p->n_sets_out == nullptr))
+    return fail(DLLM_E_ARG, "sets_out and n_sets_out must both be set or NULL");
   if (p->score != DLLM_SCORE_SPA_COS && p->score != DLLM_SCORE_POLESTAR_KL)
     return fail(DLLM_E_ARG, "unknown score %d", p->score);
   const bool polestar = p->score == DLLM_SCORE_POLESTAR_KL;
@@ -973,13 +991,26 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
       mode = DLLM_MODE_FULL;
     }
   }
+  if (polestar && any_full && mode != DLLM_MODE_FULL) {
+    // the entropy gate fired for some sequences only: the Polestar drift path
+    // runs for every sequence of a step or for none
+    int nf = 0;
+    for (int b = 0; b < B; ++b) nf += m->full_host[b] != 0;
+    if (nf != B)
+      return fail(DLLM_E_UNSUPPORTED,
+                  "Polestar drift path: the entropy gate fired for %d of %d sequences; a step is full or "
+                  "sparse for every sequence (run the step in FULL or SPARSE mode)", nf, B);
+  }
   if (polestar) {
     // the step is a full pass for every sequence exactly when mode is FULL
     p->polestar_state->steps_since_full = mode == DLLM_MODE_FULL ? 0 : p->polestar_state->steps_since_full + 1;
   }
   const int fmax = p->forced_rule == DLLM_FORCED_NONE ? 0
                    : (p->forced_rule == DLLM_FORCED_BLOCK ? d.block_len : d.block_len + p->recent_k);
-  int prev_max = any_full ? B * L : B * std::min(L, d.block_len);
+  // rows whose token changed: the last commit's, at most one block (two with
+  // Polestar-Commit's suffix-block commit)
+  const int new_max = (polestar && p->polestar->drift_commit) ? 2 * d.block_len : d.block_len;
+  int prev_max = any_full ? B * L : B * std::min(L, new_max);
   {
     Prof prof(m, st, DLLM_PROF_DECIDE, (double)B * L * 6.0 + 2.0 * prev_max * d.d_model * m->esize, 0.0);
     HIPCHK(launch_prep(st, B, L, d.block_len, p->forced_rule, p->recent_k, mode, s->history, s->n_history,
@@ -998,7 +1029,8 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
       int32_t* n = m->nsel[l & 1];
       CHK(do_polestar_drift(m, l, s, p->polestar_state, p->polestar, st));
       CHK(do_polestar_select(m, l, s, p->polestar_state, p->polestar, idx, n, st));
-      CHK(do_sparse(m, l, s, idx, n, B * W, st));
+      CHK(do_sparse(m, l, s, idx, n, B * W, st, false));
+      CHK(save_sets(m, s, p, l, idx, n, st));
     }
     if (p->polestar->drift_commit)
       CHK(do_polestar_commit(m, s, p->polestar_state, p->polestar, p->conf_threshold, p->tau, st));
@@ -1021,6 +1053,7 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     }
     const int rows = any_full ? B * L : B * std::min(L, std::max(k, fmax));
     CHK(do_sparse(m, l, s, idx, n, rows, st));
+    CHK(save_sets(m, s, p, l, idx, n, st));
     prev_idx = idx;
     prev_n = n;
     prev_max = rows;

@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256) void down_epilogue_kernel(int B, int L, int d,
     const float4 h = *reinterpret_cast<const float4*>(hp + c4);
     store4<T>(o + c4, make_float4(h.x + a.x, h.y + a.y, h.z + a.z, h.w + a.w));
   }
-  if (blockIdx.y != 0) return;
+  if (blockIdx.y != 0 || !pref) return;
   for (int j = threadIdx.x; j < r; j += 256) pref[row * r + j] = pcur[row * r + j];
   if (threadIdx.x == 0) score[row] = 0.0;
 }

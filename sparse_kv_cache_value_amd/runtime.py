@@ -162,9 +162,10 @@ class CEState:
 
 def step(model: Model, state: State, mode: int = B.DLLM_MODE_AUTO, want_result: bool = True, stream=None,
          tau: Optional[float] = None, polestar_state: Optional[PolestarState] = None,
-         ce_state: Optional[CEState] = None):
+         ce_state: Optional[CEState] = None, sets_out=None, n_sets_out=None):
     """One dllm_step; a config with ce_horizon > 0 commits with Confidence
-    Extrapolation and needs a CEState."""
+    Extrapolation and needs a CEState.  sets_out/n_sets_out (optional int32
+    device tensors [N][B][L] / [N][B]) receive every layer's index set."""
     cfg = model.cfg
     ce = None
     if cfg.ce_horizon > 0:
@@ -176,7 +177,8 @@ def step(model: Model, state: State, mode: int = B.DLLM_MODE_AUTO, want_result: 
             raise ValueError("the Polestar score needs a PolestarState")
         return B.dllm_step(model.h, state, mode, FORCED_RULE[cfg.forced], cfg.recent_k,
                            cfg.tau if tau is None else tau, cfg.conf_threshold, cfg.rho, want_result, stream,
-                           B.DLLM_SCORE_POLESTAR_KL, polestar_params(cfg), polestar_state, ce, ce_state)
+                           B.DLLM_SCORE_POLESTAR_KL, polestar_params(cfg), polestar_state, ce, ce_state,
+                           sets_out, n_sets_out)
     return B.dllm_step(model.h, state, mode, FORCED_RULE[cfg.forced], cfg.recent_k,
                        cfg.tau if tau is None else tau, cfg.conf_threshold, cfg.rho, want_result, stream,
-                       ce=ce, ce_state=ce_state)
+                       ce=ce, ce_state=ce_state, sets_out=sets_out, n_sets_out=n_sets_out)

@@ -110,19 +110,43 @@ def assert_same_selection(I_gpu, I_ref, s_ref, forced, k, what=""):
     return len(band)
 
 
-def commit_band(stats, committed_rows_mask, thr):
+# LM-head statistics are checked to 1e-5 of max|z| (logits accumulate in fp32
+# on the device, fp64 in the oracle); a commit decision closer than that to
+# flipping is left undecided
+COMMIT_BAND = 1e-5
+
+
+def commit_band(stats, masked, thr, rel=COMMIT_BAND):
     """Rows whose commit decision the float tolerance cannot decide: top-2 logit
-    gap within 1e-6 max|z|, or confidence within 1e-6 of the threshold."""
+    gap within rel*max|z|, confidence within rel of the threshold, or (masked:
+    bool per row, the rows still masked) a most-confident fallback whose
+    runner-up confidence is within rel of it."""
     z = stats["logits"]
+    conf = np.asarray(stats["conf"], np.float64)
     out = set()
     for j in range(z.shape[0]):
         zz = np.sort(z[j])[-2:]
         scale = max(np.max(np.abs(z[j])), 1e-30)
-        if zz[1] - zz[0] <= 1e-6 * scale:
+        if zz[1] - zz[0] <= rel * scale:
             out.add(j)
-        if abs(stats["conf"][j] - thr) <= 1e-6:
+        if abs(conf[j] - thr) <= rel * max(thr, 1e-30):
             out.add(j)
+    if masked is not None:
+        cand = [j for j in range(z.shape[0]) if masked[j]]
+        if cand and not any(conf[j] >= thr for j in cand):
+            best = max(conf[j] for j in cand)
+            close = [j for j in cand if best - conf[j] <= rel * best]
+            if len(close) > 1:
+                out.update(close)
     return out
+
+
+def assert_states_equal(a, b, what="", skip=()):
+    """Two States hold bit-identical buffers (except those named in skip)."""
+    torch.cuda.synchronize()
+    for k, v in a.tensors().items():
+        if k not in skip:
+            assert torch.equal(v, getattr(b, k)), f"{what}: {k} differs"
 
 
 def mode_of(full: bool) -> int:

@@ -91,3 +91,18 @@ def test_product_path_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def test_hip_failure_maps_to_dllm_e_hip():
+    """A HIP runtime failure (here: no device on this host) comes back as
+    DLLM_E_HIP with the runtime's own error text, and no model."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: hipGetDevice succeeds")
+    lib = _lib()
+    h = ctypes.c_void_p()
+    st = lib.dllm_create(ctypes.byref(_dims()), ctypes.byref(h))
+    assert st == B.DLLM_E_HIP
+    assert h.value is None
+    msg = lib.dllm_last_error().decode()
+    assert msg.startswith("hipGetDevice: ") and len(msg) > len("hipGetDevice: "), msg

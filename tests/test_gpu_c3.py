@@ -111,7 +111,7 @@ def test_c3_full_size_sampled():
     assert np.max(np.abs(sg[:, 0] - so["m"])) <= 1e-5 * np.max(np.abs(so["logits"]))
     ent = np.log(sg[:, 2]) - sg[:, 3] / sg[:, 2]
     assert np.max(np.abs(ent - so["entropy"])) <= 1e-5
-    band = commit_band(so, None, cfg.conf_threshold)
+    band = commit_band(so, ~committed0[rows], cfg.conf_threshold)
     pos, tok, _ = oracle.commit(rows, so["conf"], so["argmax"], so["entropy"], committed0, cfg.conf_threshold)
     got = [int(p) for p in st.history.cpu().numpy()[0][nh:int(st.n_history[0])]]
     if not ({int(rows[j]) for j in band} & set(pos + got)):

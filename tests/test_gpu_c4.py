@@ -131,7 +131,7 @@ def test_c4_full_size_sampled():
         assert np.max(np.abs(sg[b, :, 0] - so["m"])) <= 1e-5 * np.max(np.abs(so["logits"]))
         ent = np.log(sg[b, :, 2]) - sg[b, :, 3] / sg[b, :, 2]
         assert np.max(np.abs(ent - so["entropy"])) <= 1e-5
-        band = commit_band(so, None, cfg.conf_threshold)
+        band = commit_band(so, ~committed0[b][rows], cfg.conf_threshold)
         pos, tok, _ = oracle.commit(rows, so["conf"], so["argmax"], so["entropy"], committed0[b],
                                     cfg.conf_threshold)
         got = [int(p) for p in hist1[b][hist_n0[b]:hn1[b]]]

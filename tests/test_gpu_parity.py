@@ -50,7 +50,7 @@ def _check_commit(cfg, spec, head, before, after, what):
             assert after.n_new[b] == 0
             continue
         st = oracle.lm_stats(after.H[cfg.n_layers][b][rows], head["final_norm"], head["lm_head"], spec)
-        band = commit_band(st, None, thr)
+        band = commit_band(st, ~before.committed[b][rows], thr)
         pos, tok, emax = oracle.commit(rows, st["conf"], st["argmax"], st["entropy"], before.committed[b], thr)
         cand_band = {int(rows[j]) for j in band}
         got_pos = [int(p) for p in after.history[b][before.n_history[b]:after.n_history[b]]]
@@ -168,7 +168,7 @@ def test_layerwise_parity(name):
             if rows.size == 0:
                 continue
             so = oracle.lm_stats(Sl.H[N][b][rows], head["final_norm"], head["lm_head"], spec)
-            band = commit_band(so, None, cfg.conf_threshold)
+            band = commit_band(so, ~Sl.committed[b][rows], cfg.conf_threshold)
             nr = rows.size
             assert np.max(np.abs(sg[b, :nr, 0] - so["m"])) <= 1e-5 * np.max(np.abs(so["logits"]))
             assert np.max(np.abs(sg[b, :nr, 2] / so["S"] - 1)) <= 1e-5

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from oracle import polestar as ps
-from gpu_common import assert_close, build, medium_cfg, say, unpack_k, unpack_v
+from gpu_common import assert_close, assert_states_equal, build, medium_cfg, say, unpack_k, unpack_v
 from helpers import np_weights, spec_of
 from sparse_kv_cache_value_amd import binding as B
 from sparse_kv_cache_value_amd import configs, inputs, runtime
@@ -69,9 +69,11 @@ def check_layer(cfg, spec, W, l, b, pre, pre_ps, mid_ps, post_ps, post, I_gpu, w
     if not np.array_equal(a_gpu, a_or):
         bad = np.nonzero(a_gpu != a_or)[0]
         assert np.all(margin[bad] < 1e-9), f"{what}: assignment differs at rows {bad[:8]} (margins {margin[bad][:4]})"
-        say(f"{what}: k-means tie at rows {bad}, skipped")
-        return
-    assert_close(mid_ps["centroids"], C_or, 1e-12, f"{what}: centroids")
+        # a near-tie decided the other way: the centroids differ, but every
+        # later check below runs on the GPU's own assignment and centroids
+        say(f"{what}: k-means tie at rows {bad}, centroid comparison skipped")
+    else:
+        assert_close(mid_ps["centroids"], C_or, 1e-12, f"{what}: centroids")
     # NVFP4 codes from the GPU's norms and centroids: bit-exact
     R = X / mid_ps["norms"][:, None] - mid_ps["centroids"][a_gpu]
     codes, scales = ps.nvfp4_encode(R)
@@ -170,12 +172,15 @@ def test_polestar_step_equals_entry_points():
     b_, pb = runtime.State(cfg), runtime.PolestarState(cfg)
     for k, v in a.tensors().items():
         getattr(b_, k).copy_(v)
+    P0, s0 = a.proxy_ref.clone(), a.score.clone()
     for t in range(3):
         runtime.step(model, a, mode=B.DLLM_MODE_SPARSE, polestar_state=pa)
         _run(cfg, None, model, b_, pb, 1, set(), [], None)
         torch.cuda.synchronize()
-        for k, v in a.tensors().items():
-            assert torch.equal(v, getattr(b_, k)), f"t={t}: {k} differs"
+        assert_states_equal(a, b_, f"t={t}", skip=("proxy_ref", "score"))
+        # the Polestar step keeps no value proxy: P and the drift scores stay
+        # as the full pass left them (dllm_sparse_layer alone refreshes them)
+        assert torch.equal(a.proxy_ref, P0) and torch.equal(a.score, s0)
         for k in ("log_attn", "win_start", "assign", "codes", "scales", "kl", "top"):
             assert torch.equal(getattr(pa, k), getattr(pb, k)), f"t={t}: polestar {k} differs"
     model.close()
