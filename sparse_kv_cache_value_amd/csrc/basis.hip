@@ -271,14 +271,15 @@ static hipError_t run_basis(hipStream_t st, int d, int nv, int r, int iters, con
   double* lam = V + (size_t)p * p;
   double* Bs = lam + p;
   hipError_t e;
-  static bool attr = false;
-  if (!attr) {
+  static std::atomic<unsigned long long> attr{0};
+  e = once_per_device(attr, [] {
     const size_t mx = (size_t)BS_PMAX * BS_PMAX * 8;
-    if ((e = set_lds((const void*)bs_chol_kernel, mx)) != hipSuccess) return e;
-    if ((e = set_lds((const void*)bs_trsm_kernel, mx)) != hipSuccess) return e;
-    if ((e = set_lds((const void*)bs_jacobi_kernel, mx + BS_PMAX * 8 + BS_PMAX * 4)) != hipSuccess) return e;
-    attr = true;
-  }
+    hipError_t r;
+    if ((r = set_lds((const void*)bs_chol_kernel, mx)) != hipSuccess) return r;
+    if ((r = set_lds((const void*)bs_trsm_kernel, mx)) != hipSuccess) return r;
+    return set_lds((const void*)bs_jacobi_kernel, mx + BS_PMAX * 8 + BS_PMAX * 4);
+  });
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bs_init_kernel, dim3((unsigned)(((size_t)d * p + 255) / 256)), dim3(256), 0, st, d, p,
                      (uint64_t)0x5EED5EEDull, Q);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -4,7 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace dllm {
+
+// Kernel attributes (the dynamic LDS limit) are set per device: `done` keeps
+// one bit per device id.  Runs `set` on the current device the first time
+// (again after a failure) and returns its status.
+template <typename F>
+inline hipError_t once_per_device(std::atomic<unsigned long long>& done, F set) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = (dev >= 0 && dev < 64) ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = set();
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 typedef uint16_t bf16;  // raw bfloat16 storage
 

@@ -257,14 +257,13 @@ template <int MTW, int KS, int EPI>
 static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
                              uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
                              int row_blocks, int n_slabs, int total, int cap, LaunchEvents ev) {
-  static bool attr_set = false;
+  static std::atomic<unsigned long long> attr_set{0};
   const size_t lds = (size_t)2 * KS * 4 * 64 * 16;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MTW, KS, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t ea = once_per_device(attr_set, [&] {
+    return hipFuncSetAttribute((const void*)gemm_bf16_kernel<MTW, KS, EPI>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (ea != hipSuccess) return ea;
   if (ev.start)
     hipExtLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI>), dim3(grid), dim3(256), lds, st, ev.start, ev.stop, 0,
                           (const u32x4*)A, MTt, (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks,
@@ -540,14 +539,13 @@ template <int MT, int EPI>
 static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
                              uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
                              int n_slabs, int total, int cap, LaunchEvents ev) {
-  static bool attr_set = false;
+  static std::atomic<unsigned long long> attr_set{0};
   const size_t lds = StreamShape<MT>::LDS;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_stream_kernel<MT, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t ea = once_per_device(attr_set, [&] {
+    return hipFuncSetAttribute((const void*)gemm_stream_kernel<MT, EPI>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (ea != hipSuccess) return ea;
   if (ev.start)
     hipExtLaunchKernelGGL((gemm_stream_kernel<MT, EPI>), dim3(grid), dim3(256), lds, st, ev.start, ev.stop, 0,
                           (const u32x4*)A, MTt, (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs,

@@ -787,14 +787,12 @@ hipError_t launch_ps_kmeans(hipStream_t st, int B, int W, int K, int iters, cons
                             double* norms, double* coef, int32_t* nsel) {
   if (W > PS_WMAX || W > 128 || K > 16 || K < 1 || W < K) return hipErrorInvalidValue;
   const size_t lds = ((size_t)W * W + K * W + W) * sizeof(double) + (size_t)W * sizeof(int);
-  static bool attr = false;
-  if (!attr) {
+  static std::atomic<unsigned long long> attr{0};
+  hipError_t ea = once_per_device(attr, [] {
     const size_t mx = ((size_t)PS_WMAX * PS_WMAX + 16 * PS_WMAX + PS_WMAX) * sizeof(double) + PS_WMAX * sizeof(int);
-    hipError_t e = hipFuncSetAttribute((const void*)ps_kmeans_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)mx);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+    return hipFuncSetAttribute((const void*)ps_kmeans_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mx);
+  });
+  if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL(ps_kmeans_kernel, dim3(B), dim3(PS_KM_THREADS), lds, st, W, K, iters, R, assign, norms, coef,
                      nsel);
   return hipGetLastError();
