@@ -255,6 +255,23 @@ dllm_status dllm_init_layer(dllm_model *m, int32_t layer, const dllm_layer_weigh
  * Cholesky pivot: the iterated subspace lost rank). */
 dllm_status dllm_derive_proxy_basis(dllm_model *m, const void *w_v, int32_t iters, double *w_r_out, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dllm_derive_proxy_basis with its fp64 workspace and status word in a fixed
+ * library-owned device array instead of memory allocated and freed per call;
+ * the same kernels, so the same W_r bit for bit.  The array holds
+ * DLLM_BASIS_NOALLOC_DOUBLES doubles (32 MiB) per device, from the first
+ * dllm_create on that device until the process ends.  The workspace a shape
+ * needs, (2 d_model + n_kv_heads*head_dim) p + 4 p^2 + p + p*proxy_rank + 16
+ * doubles with p as in dllm_derive_proxy_basis, must fit (every shape with
+ * d_model and n_kv_heads*head_dim <= 8192 does); otherwise DLLM_E_SHAPE.
+ * Every call on a device shares that device's array, so calls that overlap
+ * on one device (any stream, any model) race: the caller serialises them.
+ * Waits for `stream`.  Other errors as dllm_derive_proxy_basis. */
+#define DLLM_BASIS_NOALLOC_DOUBLES (4u << 20)
+dllm_status dllm_derive_proxy_basis_noalloc(dllm_model *m, const void *w_v, int32_t iters, double *w_r_out,
+                                            void *stream);
+
 /* Copy the embedding table [vocab][d_model], the final norm gain [d_model]
  * (fp32) and the LM head [d_model][vocab]. */
 dllm_status dllm_init_head(dllm_model *m, const void *embed, const float *final_norm,

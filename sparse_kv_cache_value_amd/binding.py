@@ -113,6 +113,7 @@ SIGNATURES = {
     "dllm_profile_read": (_i32, [_vp, ctypes.POINTER(DllmKernelStats)]),
     "dllm_stream_probe": (_i32, [_vp, ctypes.c_size_t, _vp, _i32, ctypes.POINTER(_f64), _vp]),
     "dllm_derive_proxy_basis": (_i32, [_vp, _vp, _i32, _vp, _vp]),
+    "dllm_derive_proxy_basis_noalloc": (_i32, [_vp, _vp, _i32, _vp, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -276,6 +277,12 @@ def dllm_profile(m: int, enable: bool, classes=None):
 def dllm_derive_proxy_basis(m: int, w_v, w_r_out, iters: int = DLLM_PROXY_ITERS, stream=None):
     """W_r [d][r] fp64 into w_r_out from the device value projection w_v."""
     _check(lib().dllm_derive_proxy_basis(m, _p(w_v), int(iters), _p(w_r_out), _stream(stream)))
+
+
+def dllm_derive_proxy_basis_noalloc(m: int, w_v, w_r_out, iters: int = DLLM_PROXY_ITERS, stream=None):
+    """dllm_derive_proxy_basis with the library's fixed per-device workspace
+    (no device allocation in the call)."""
+    _check(lib().dllm_derive_proxy_basis_noalloc(m, _p(w_v), int(iters), _p(w_r_out), _stream(stream)))
 
 
 def dllm_stream_probe(buf, scratch, reps: int = 3, stream=None) -> float:

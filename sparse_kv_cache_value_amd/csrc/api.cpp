@@ -605,8 +605,12 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
     return st;
   };
   {
-    const hipError_t e = hipGetDevice(&m->device);
+    hipError_t e = hipGetDevice(&m->device);
     if (e != hipSuccess) return cleanup(fail(DLLM_E_HIP, "hipGetDevice: %s", hipGetErrorString(e)));
+    // the device address of the allocation-free basis workspace, once per device
+    e = proxy_basis_static_setup(m->device);
+    if (e != hipSuccess)
+      return cleanup(fail(DLLM_E_HIP, "fixed proxy-basis workspace (hipGetSymbolAddress): %s", hipGetErrorString(e)));
   }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, m->device) == hipSuccess && prop.multiProcessorCount > 0)
@@ -712,31 +716,43 @@ dllm_status dllm_destroy(dllm_model* m) {
   return DLLM_OK;
 }
 
-// W_r [d][r] fp32 from the value projection (device, storage dtype); waits
+dllm_status basis_supported(const dllm_model* m) {
+  const dllm_dims& d = m->d;
+  if (d.proxy_rank > 128 || proxy_basis_width(d.d_model, nv_of(d), d.proxy_rank) < d.proxy_rank)
+    return fail(DLLM_E_UNSUPPORTED, "proxy basis: need proxy_rank <= 128 and a subspace of at least r columns");
+  return DLLM_OK;
+}
+
+// The derivation on a given workspace and status word; waits for the stream.
+dllm_status run_derive(dllm_model* m, const void* w_v, int iters, double* wr, double* ws, int32_t* status,
+                       hipStream_t st) {
+  const dllm_dims& d = m->d;
+  int32_t st_h = 0;
+  hipError_t e = launch_proxy_basis(st, m->bf16, d.d_model, nv_of(d), d.proxy_rank, iters, w_v, wr, ws, status);
+  if (e == hipSuccess) e = hipMemcpyAsync(&st_h, status, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(DLLM_E_HIP, "proxy basis: %s", hipGetErrorString(e));
+  if (st_h != 0) return fail(DLLM_E_NUMERIC, "proxy basis: a Cholesky pivot was not positive");
+  return DLLM_OK;
+}
+
+// W_r [d][r] fp64 from the value projection (device, storage dtype); waits
 // for the stream and frees its workspace.
 dllm_status derive_basis(dllm_model* m, const void* w_v, int iters, double* wr, hipStream_t st) {
   const dllm_dims& d = m->d;
-  const int D = d.d_model, nv = nv_of(d), r = d.proxy_rank;
-  if (r > 128 || proxy_basis_width(D, nv, r) < r)
-    return fail(DLLM_E_UNSUPPORTED, "proxy basis: need proxy_rank <= 128 and a subspace of at least r columns");
+  CHK(basis_supported(m));
   double* ws = nullptr;
   int32_t* status = nullptr;
-  if (hipMalloc((void**)&ws, proxy_basis_workspace_doubles(D, nv, r) * 8) != hipSuccess)
+  if (hipMalloc((void**)&ws, proxy_basis_workspace_doubles(d.d_model, nv_of(d), d.proxy_rank) * 8) != hipSuccess)
     return fail(DLLM_E_NOMEM, "proxy basis workspace");
   if (hipMalloc((void**)&status, 16) != hipSuccess) {
     (void)hipFree(ws);
     return fail(DLLM_E_NOMEM, "proxy basis workspace");
   }
-  int32_t st_h = 0;
-  hipError_t e = hipMemsetAsync(status, 0, 16, st);
-  if (e == hipSuccess) e = launch_proxy_basis(st, m->bf16, D, nv, r, iters, w_v, wr, ws, status);
-  if (e == hipSuccess) e = hipMemcpyAsync(&st_h, status, 4, hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  const dllm_status r = run_derive(m, w_v, iters, wr, ws, status, st);
   (void)hipFree(ws);
   (void)hipFree(status);
-  if (e != hipSuccess) return fail(DLLM_E_HIP, "proxy basis: %s", hipGetErrorString(e));
-  if (st_h != 0) return fail(DLLM_E_NUMERIC, "proxy basis: a Cholesky pivot was not positive");
-  return DLLM_OK;
+  return r;
 }
 
 dllm_status dllm_init_layer(dllm_model* m, int32_t layer, const dllm_layer_weights* w, void* stream) {
@@ -800,6 +816,23 @@ dllm_status dllm_derive_proxy_basis(dllm_model* m, const void* w_v, int32_t iter
   if (!w_v || !w_r_out) return fail(DLLM_E_ARG, "w_v/w_r_out is NULL");
   if (iters < 0) return fail(DLLM_E_ARG, "iters < 0");
   return derive_basis(m, w_v, iters, w_r_out, S(stream));
+}
+
+dllm_status dllm_derive_proxy_basis_noalloc(dllm_model* m, const void* w_v, int32_t iters, double* w_r_out,
+                                            void* stream) {
+  CHK(check_model(m));
+  if (!w_v || !w_r_out) return fail(DLLM_E_ARG, "w_v/w_r_out is NULL");
+  if (iters < 0) return fail(DLLM_E_ARG, "iters < 0");
+  CHK(basis_supported(m));
+  const dllm_dims& d = m->d;
+  const size_t need = proxy_basis_workspace_doubles(d.d_model, nv_of(d), d.proxy_rank);
+  if (need > PROXY_BASIS_STATIC_DOUBLES)
+    return fail(DLLM_E_SHAPE, "proxy basis without allocation: the workspace needs %zu doubles, the fixed array "
+                "holds %zu", need, (size_t)PROXY_BASIS_STATIC_DOUBLES);
+  // set up at dllm_create on the model's device
+  double* ws = proxy_basis_static_ws(m->device);
+  if (!ws) return fail(DLLM_E_STATE, "the fixed workspace of device %d is not set up", m->device);
+  return run_derive(m, w_v, iters, w_r_out, ws, (int32_t*)(ws + PROXY_BASIS_STATIC_DOUBLES), S(stream));
 }
 
 dllm_status dllm_init_head(dllm_model* m, const void* embed, const float* final_norm, const void* lm_head,

@@ -13,6 +13,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace dllm {
 
 typedef double f64x4_b __attribute__((ext_vector_type(4)));
@@ -111,8 +113,9 @@ __global__ __launch_bounds__(256) void bs_trsm_kernel(int rows, int p, const dou
 }
 
 // Random start: uniform values in [-1, 1) from a 64-bit mix of (i, j).
-__global__ void bs_init_kernel(int rows, int p, uint64_t seed, double* __restrict__ Q) {
+__global__ void bs_init_kernel(int rows, int p, uint64_t seed, double* __restrict__ Q, int32_t* __restrict__ status) {
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e == 0) status[0] = 0;  // the factorisations only ever set it
   if (e >= (size_t)rows * p) return;
   uint64_t z = seed + 0x9E3779B97F4A7C15ull * (e + 1);
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -281,7 +284,7 @@ static hipError_t run_basis(hipStream_t st, int d, int nv, int r, int iters, con
   });
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bs_init_kernel, dim3((unsigned)(((size_t)d * p + 255) / 256)), dim3(256), 0, st, d, p,
-                     (uint64_t)0x5EED5EEDull, Q);
+                     (uint64_t)0x5EED5EEDull, Q, status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = cholqr2(st, d, p, Q, G, L, status)) != hipSuccess) return e;
   for (int it = 0; it < iters; ++it) {
@@ -298,6 +301,37 @@ static hipError_t run_basis(hipStream_t st, int d, int nv, int r, int iters, con
   hipLaunchKernelGGL(bs_pick_kernel, dim3(1), dim3(256), 0, st, p, r, V, lam, Bs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return gemm64<double, false>(st, d, r, p, Q, p, Bs, r, wr, r);  // W_r = Q Bsel
+}
+
+// Fixed workspace of the allocation-free derivation: a file-scope device
+// array (one copy per device, held until the process ends) of
+// PROXY_BASIS_STATIC_DOUBLES workspace doubles followed by the status word.
+// Host code never passes the array's name to a kernel: its device address,
+// looked up once per device, is kept in g_static_ws.
+static __device__ __align__(256) double scratch[PROXY_BASIS_STATIC_DOUBLES + 32];
+static std::mutex g_static_mu;
+static double* g_static_ws[64] = {};
+
+hipError_t proxy_basis_static_setup(int dev) {
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (g_static_ws[dev]) return hipSuccess;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != dev) return hipErrorInvalidDevice;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  g_static_ws[dev] = (double*)ptr;
+  return hipSuccess;
+}
+
+double* proxy_basis_static_ws(int dev) {
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  return g_static_ws[dev];
 }
 
 hipError_t launch_f64_to_f32(hipStream_t st, size_t n, const double* src, float* dst) {

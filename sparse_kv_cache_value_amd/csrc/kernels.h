@@ -159,6 +159,15 @@ hipError_t launch_ps_commit(hipStream_t st, int B, int L, int blk, int W, int K,
 // launch_proxy_basis needs.
 int proxy_basis_width(int d, int nv, int r);
 size_t proxy_basis_workspace_doubles(int d, int nv, int r);
+// Allocation-free derivation: a fixed device array per device of this many
+// workspace doubles (32 MiB; every shape with d, nv <= 8192 and r <= 128
+// fits), then 32 more doubles whose first word is the status.
+constexpr size_t PROXY_BASIS_STATIC_DOUBLES = (size_t)4 << 20;
+// Looks the array's device address up on device `dev` (which must be
+// current) once; later calls return at once.
+hipError_t proxy_basis_static_setup(int dev);
+// The address for `dev`, or NULL before its set-up.
+double* proxy_basis_static_ws(int dev);
 // wr [d][r] fp64 = U_r S_r of W [d][nv] (storage dtype) by randomised
 // subspace iteration (iters power steps) and Rayleigh-Ritz; status[0] is set
 // to 1 when a Cholesky pivot was not positive (rank-deficient subspace).
