@@ -64,9 +64,9 @@ enum { DLLM_FORCED_NONE = 0, DLLM_FORCED_BLOCK = 1, DLLM_FORCED_BLOCK_RECENT = 2
 /* Model and sequence dimensions.  Limits checked by dllm_create:
  * head_dim a multiple of 32 and <= 256; d_model <= 8192 and a multiple of 32;
  * d_ffn a multiple of 32; n_q_heads a multiple of n_kv_heads;
- * seq_len <= 8192 and a multiple of 4; block_len <= 64; proxy_rank <= 128; for DLLM_BF16 the
- * widths d_model, d_ffn, n_q_heads*head_dim, n_kv_heads*head_dim and vocab
- * must be multiples of 32 and d_model, d_ffn multiples of 64. */
+ * seq_len <= 8192 and a multiple of 4; block_len <= 64; proxy_rank <= 128 and
+ * <= d_model; for DLLM_BF16 also d_model, d_ffn and n_q_heads*head_dim
+ * multiples of 64, n_kv_heads*head_dim and vocab multiples of 32. */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
   int32_t max_batch, seq_len, block_len, proxy_rank, dtype;

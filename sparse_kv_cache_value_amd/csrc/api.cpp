@@ -262,7 +262,11 @@ dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int 
                  const int32_t* n_sel, float* out, size_t out_floats, int* splits, int cls = DLLM_PROF_GEMM,
                  int MTt = -1, void* act = nullptr) {
   if (MTt < 0) MTt = m->MTt;
-  ProfLaunch prof(m, cls, (double)K * N * m->esize + (double)max_rows * K * m->esize + (double)max_rows * N * 4.0,
+  // algorithmic bytes: the weight, the input rows and the output rows in the
+  // storage type (SwiGLU halves the output width); split-K partials are the
+  // kernel's own traffic, not the method's
+  const double n_out = act ? N / 2.0 : (double)N;
+  ProfLaunch prof(m, cls, (double)K * N * m->esize + (double)max_rows * K * m->esize + (double)max_rows * n_out * m->esize,
                   2.0 * max_rows * (double)K * N);
   if (m->bf16) {
     // up to 288 rows: the weight-streaming kernel, when the shape suits it

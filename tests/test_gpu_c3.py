@@ -1,7 +1,8 @@
 """Full-size headline workload: the LLaDA-8B-shaped model (32 layers,
 d = 4096, 32 x 128 heads, SwiGLU 12288, vocab 126464), batch 1, L = 1024
 (512 prompt + 512 masked), the split-Gaussian rho(l) (k = 45..283 rows per
-layer) with forced = current block + 32 recent.  After a full pass and two
+layer) with forced = current block + 32 recent.  The full pass is checked on
+every row of layer 15 (the row-blocked GEMM at M = 1024).  After it and two
 sparse steps of dllm_step (the launch configuration bench.py times), one more
 sparse step runs through the C-ABI entry points with the oracle in shadow
 mode on layers 0, 15 (k = 283, the widest GEMM tiling) and 31 (k = 45 below
@@ -50,6 +51,14 @@ def test_c3_full_size_sampled():
     torch.cuda.empty_cache()
     st = runtime.State(cfg)
     runtime.step(model, st, mode=B.DLLM_MODE_FULL)
+    # the full pass (M = 1024 rows: the row-blocked GEMM) on a mid-depth layer, every row
+    s = _slice(st, 15)
+    out, Kx, Vx = oracle.layer_dense(s["x"], W[15], spec)
+    e = assert_close(s["h"], out, 2e-2, "C3 full pass l=15 H")
+    assert_close(s["K"], Kx, 2e-2, "C3 full pass l=15 K")
+    assert_close(s["V"], Vx, 2e-2, "C3 full pass l=15 V")
+    assert_close(s["Pr"], oracle.proxy(s["x"], W[15]["attn_norm"], W[15]["w_proxy"]), 1e-12, "C3 full pass l=15 proxy")
+    say(f"C3 full pass l=15: all {L} rows, H rel err {e:.2e}")
     for _ in range(2):
         runtime.step(model, st, mode=B.DLLM_MODE_SPARSE, want_result=False)
     twin = runtime.State(cfg)
