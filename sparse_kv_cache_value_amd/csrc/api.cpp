@@ -94,6 +94,7 @@ struct dllm_model {
   float* logits = nullptr;
   double* lm_part = nullptr;
   double* lm_stats = nullptr;
+  double* lm_wpart = nullptr;  // per-slab statistics of the fused LM head [64][vocab/128][4]
   int32_t* lm_rows = nullptr;
   int lm_slabs = 0;
   // Polestar drift path workspace
@@ -379,8 +380,11 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
 }
 
 // LM-head statistics of the first nblk blocks from each sequence's block
-// start (nblk = 1: the current block; 2: also the next one).
-dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int nblk = 1) {
+// start (nblk = 1: the current block; 2: also the next one).  Up to 64 rows
+// and no logits wanted: the statistics come out of the weight-streaming GEMM
+// per 128-column slab and one merge (no logits buffer); otherwise the logits
+// are materialised (m->logits) and reduced by slab and merge kernels.
+dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int nblk = 1, bool want_logits = false) {
   const dllm_dims& d = m->d;
   const int B = s->batch, blk = d.block_len * nblk;
   {
@@ -388,6 +392,20 @@ dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int n
     HIPCHK(launch_lm_gather(st, m->bf16, B, d.seq_len, blk, d.d_model, d.rms_eps, m->lm_MTt, s->block_start,
                             hid(m, s, d.n_layers), m->final_norm, m->A_lm, m->lm_rows));
     prof.done();
+  }
+  if (m->bf16 && !want_logits && m->lm_wpart && B * blk <= 64 &&
+      gemm_stream_pick_splits(B * blk, d.d_model, d.vocab, m->n_cu, false, m->lm_MTt) > 0) {
+    const int ns = d.vocab / 128;
+    ProfLaunch prof(m, DLLM_PROF_LMHEAD,
+                    (double)d.d_model * d.vocab * 2.0 + (double)B * blk * d.d_model * 2.0 + (double)B * blk * 32.0,
+                    2.0 * B * blk * (double)d.d_model * d.vocab);
+    HIPCHK(launch_gemm_stream_stats(st, B * blk, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
+                                    (const uint16_t*)m->lm_head, m->lm_rows, m->lm_wpart, prof.ev));
+    prof.done();
+    Prof prof2(m, st, DLLM_PROF_DECIDE, (double)B * blk * ns * 32.0, 0.0);
+    HIPCHK(launch_lm_merge_wide(st, B * blk, ns, m->lm_wpart, m->lm_stats));
+    prof2.done();
+    return DLLM_OK;
   }
   int sp = 1;
   const size_t cap = (size_t)d.max_batch * 2 * d.block_len * d.vocab;
@@ -664,6 +682,7 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   m->lm_slabs = lm_stats_slabs(d.vocab);
   ALLOC(m->lm_part, (size_t)lm_rows_cap * m->lm_slabs * 4 * 8);
   ALLOC(m->lm_stats, (size_t)lm_rows_cap * 4 * 8);
+  if (m->bf16 && d.vocab % 128 == 0) ALLOC(m->lm_wpart, (size_t)64 * (d.vocab / 128) * 4 * 8);
   ALLOC(m->lm_rows, 16);
   if (D % 128 == 0) {
     const size_t wmax = 120;
@@ -918,8 +937,8 @@ dllm_status dllm_lm_head(dllm_model* m, const dllm_state* s, double* stats_out, 
   CHK(check_state(m, s, false));
   if (!m->head_ready) return fail(DLLM_E_STATE, "head weights not initialised");
   hipStream_t st = S(stream);
-  CHK(do_lm_head(m, s, st));
   const size_t rows = (size_t)s->batch * m->d.block_len;
+  CHK(do_lm_head(m, s, st, 1, logits_out != nullptr));
   if (stats_out) HIPCHK(hipMemcpyAsync(stats_out, m->lm_stats, rows * 4 * 8, hipMemcpyDeviceToDevice, st));
   if (logits_out)
     HIPCHK(hipMemcpyAsync(logits_out, m->logits, rows * m->d.vocab * 4, hipMemcpyDeviceToDevice, st));

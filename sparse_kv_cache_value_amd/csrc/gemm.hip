@@ -491,7 +491,62 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
   }
   GS_WAIT_VM_LGKM0(0);  // no request may still be writing LDS
 
-  if constexpr (EPI == 0) {
+  if constexpr (EPI == 2) {
+    // LM-head row statistics of this 128-column vocabulary slab (the logits
+    // are never written): per row the max logit, its lowest column, and in
+    // fp64 S = sum e^{z-max}, T = sum e^{z-max} (z-max), into
+    // out (as double) [row][slab][4]
+    __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+    constexpr int ZLD = 129;       // padded row of the slab's logits in LDS
+    float* zs = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int mrow = mt * 32 + (lane >> 5) * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zs[(mrow + (i >> 2) * 8 + (i & 3)) * ZLD + wv * 32 + (lane & 31)] = acc[mt][i];
+    }
+    __syncthreads();
+    // four threads per row, 32 columns each, combined in a fixed order
+    const int r = min(tid >> 2, MT * 32 - 1), q = tid & 3;
+    const float* zr = zs + r * ZLD + q * 32;
+    float best = zr[0];
+    int bidx = 0;
+    for (int c = 1; c < 32; ++c)
+      if (zr[c] > best) {  // increasing column order keeps the lowest index
+        best = zr[c];
+        bidx = c;
+      }
+    bidx += slab * 128 + q * 32;
+#pragma unroll
+    for (int o = 1; o <= 2; o <<= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bidx, o, 64);
+      if (ov > best || (ov == best && oi < bidx)) {
+        best = ov;
+        bidx = oi;
+      }
+    }
+    const double mx = (double)best;
+    double sa = 0.0, ta = 0.0;
+    for (int c = 0; c < 32; ++c) {
+      const double dz = (double)zr[c] - mx;
+      const double e = exp(dz);
+      sa += e;
+      ta += e * dz;
+    }
+#pragma unroll
+    for (int o = 1; o <= 2; o <<= 1) {  // commutative pairs: every lane of the row gets the same sums
+      sa += __shfl_xor(sa, o, 64);
+      ta += __shfl_xor(ta, o, 64);
+    }
+    if (q == 0 && (tid >> 2) < MT * 32 && (tid >> 2) < M) {
+      double* p = reinterpret_cast<double*>(out) + ((size_t)(tid >> 2) * n_slabs + slab) * 4;
+      p[0] = mx;
+      p[1] = (double)bidx;
+      p[2] = sa;
+      p[3] = ta;
+    }
+  } else if constexpr (EPI == 0) {
     const int ncol = nt * 32 + (lane & 31);
     if (slab * 4 + wv < NT) {
 #pragma unroll
@@ -540,7 +595,9 @@ static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, c
                              uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
                              int n_slabs, int total, int cap, LaunchEvents ev) {
   static std::atomic<unsigned long long> attr_set{0};
-  const size_t lds = StreamShape<MT>::LDS;
+  // the statistics epilogue keeps the slab's logits in LDS ([MT*32][129] fp32)
+  constexpr size_t zlds = (size_t)MT * 32 * 129 * 4;
+  const size_t lds = (EPI == 2 && zlds > StreamShape<MT>::LDS) ? zlds : StreamShape<MT>::LDS;
   hipError_t ea = once_per_device(attr_set, [&] {
     return hipFuncSetAttribute((const void*)gemm_stream_kernel<MT, EPI>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -574,6 +631,20 @@ int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, in
   for (int s = 2; s <= 32 && s <= K / 256; ++s)
     if ((K / 256) % s == 0 && n_slabs * s <= n_cu) best = s;
   return best;
+}
+
+hipError_t launch_gemm_stream_stats(hipStream_t st, int max_rows, int K, int N, const uint16_t* A, int MTt,
+                                    const uint16_t* Wp, const int32_t* n_sel, double* part, LaunchEvents ev) {
+  if (max_rows <= 0) return hipSuccess;
+  const int mt = stream_mt(max_rows);
+  if (mt < 1 || mt > 2 || mt > MTt || N % 128 != 0 || K % 256 != 0) return hipErrorInvalidValue;
+  const int n_slabs = N / 128;
+  const int grid = (n_slabs + 7) / 8 * 8;
+  if (mt == 1)
+    return stream_cfg<1, 2>(st, grid, A, MTt, Wp, (float*)part, nullptr, 0, n_sel, 1, K, N, K, n_slabs, n_slabs,
+                            max_rows, ev);
+  return stream_cfg<2, 2>(st, grid, A, MTt, Wp, (float*)part, nullptr, 0, n_sel, 1, K, N, K, n_slabs, n_slabs,
+                          max_rows, ev);
 }
 
 hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,

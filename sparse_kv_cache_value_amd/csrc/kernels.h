@@ -83,6 +83,11 @@ int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, in
 hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                               const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
                               int MTt_out, LaunchEvents ev = {});
+// The LM head on up to 64 rows without logits: per row and 128-column slab
+// (max, lowest argmax, S, T) into part [rows][N/128][4] (fp64); merge with
+// launch_lm_merge_wide.
+hipError_t launch_gemm_stream_stats(hipStream_t st, int max_rows, int K, int N, const uint16_t* A, int MTt,
+                                    const uint16_t* Wp, const int32_t* n_sel, double* part, LaunchEvents ev = {});
 // Padding (elements) a packed buffer needs past its end: for weights pass 1,
 // for packed activations the buffer's row-tile count.
 size_t gemm_pad_elems(int rows_tiles);
@@ -109,6 +114,9 @@ hipError_t launch_lm_gather(hipStream_t st, bool bf16, int B, int L, int blk, in
 hipError_t launch_lm_stats(hipStream_t st, int M, int V, const float* logits, double* part,
                            double* stats, int n_slabs);
 int lm_stats_slabs(int V);
+// Merge of per-slab statistics part [M][n_slabs][4] into stats [M][4] (one
+// wave per row, fixed order).
+hipError_t launch_lm_merge_wide(hipStream_t st, int M, int n_slabs, const double* part, double* stats);
 hipError_t launch_commit(hipStream_t st, int B, int L, int blk, double thr, double tau,
                          const double* stats, int32_t* tokens, uint8_t* committed, int32_t* history,
                          int32_t* n_history, int32_t* n_new, int32_t* block_start, uint8_t* full_next,

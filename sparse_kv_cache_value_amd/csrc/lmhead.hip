@@ -146,6 +146,57 @@ __global__ void lm_merge_kernel(int M, int n_slabs, const double* __restrict__ p
   o[3] = T;
 }
 
+// (max, argmax, S, T) of b merged into a, both relative to their own max;
+// symmetric in a and b (floating-point addition commutes), so both lanes of a
+// butterfly exchange end with the same bits.  A max of -inf marks no data.
+__device__ __forceinline__ void lm_combine(double& mx, double& am, double& S, double& T, double omx, double oam,
+                                           double oS, double oT) {
+  if (omx == -INFINITY) return;
+  if (mx == -INFINITY) {
+    mx = omx;
+    am = oam;
+    S = oS;
+    T = oT;
+    return;
+  }
+  const double m = fmax(mx, omx);
+  const double da = mx - m, db = omx - m;
+  const double fa = exp(da), fb = exp(db);
+  const double Sn = S * fa + oS * fb;
+  const double Tn = (T + da * S) * fa + (oT + db * oS) * fb;
+  if (omx > mx || (omx == mx && oam < am)) am = oam;
+  mx = m;
+  S = Sn;
+  T = Tn;
+}
+
+__global__ __launch_bounds__(64) void lm_merge_wide_kernel(int n_slabs, const double* __restrict__ part,
+                                                           double* __restrict__ stats) {
+  const int m = blockIdx.x, lane = threadIdx.x;
+  const double* p = part + (size_t)m * n_slabs * 4;
+  double mx = -INFINITY, am = 0.0, S = 0.0, T = 0.0;
+  for (int s = lane; s < n_slabs; s += 64) lm_combine(mx, am, S, T, p[s * 4], p[s * 4 + 1], p[s * 4 + 2], p[s * 4 + 3]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double omx = __shfl_xor(mx, o, 64), oam = __shfl_xor(am, o, 64);
+    const double oS = __shfl_xor(S, o, 64), oT = __shfl_xor(T, o, 64);
+    lm_combine(mx, am, S, T, omx, oam, oS, oT);
+  }
+  if (lane == 0) {
+    double* out = stats + (size_t)m * 4;
+    out[0] = mx;
+    out[1] = am;
+    out[2] = S;
+    out[3] = T;
+  }
+}
+
+hipError_t launch_lm_merge_wide(hipStream_t st, int M, int n_slabs, const double* part, double* stats) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lm_merge_wide_kernel, dim3(M), dim3(64), 0, st, n_slabs, part, stats);
+  return hipGetLastError();
+}
+
 hipError_t launch_lm_stats(hipStream_t st, int M, int V, const float* logits, double* part, double* stats,
                            int n_slabs) {
   hipLaunchKernelGGL(lm_slab_kernel, dim3(M, n_slabs), dim3(256), 0, st, V, n_slabs, logits, part);
