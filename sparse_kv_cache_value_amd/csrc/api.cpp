@@ -83,7 +83,6 @@ struct dllm_model {
   size_t part_floats = 0;
   double* ppart = nullptr;
   size_t ppart_doubles = 0;
-  float* attn_part = nullptr;
   int32_t* idx[2] = {nullptr, nullptr};
   int32_t* nsel[2] = {nullptr, nullptr};
   int32_t* idx0 = nullptr;
@@ -347,7 +346,7 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
               2.0 * B * L * nv * m->esize + 2.0 * max_rows * nq * m->esize,
               4.0 * max_rows * (double)L * nq);
     HIPCHK(launch_attention(st, m->bf16, max_rows, B, L, d.n_q_heads, d.n_kv_heads, d.head_dim, idx, n, m->q,
-                            kcache(m, s, layer), vcache(m, s, layer), m->attn_part, m->attn_o, m->MTt));
+                            kcache(m, s, layer), vcache(m, s, layer), m->attn_o, m->MTt));
     prof.done();
   }
   CHK(gemm(m, st, max_rows, B, nq, D, m->attn_o, w.w_o, n, m->part, m->part_floats, &sp));
@@ -663,10 +662,6 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   }
   m->ppart_doubles = proxy_partial_doubles(m->M_cap, D, d.proxy_rank);
   ALLOC(m->ppart, m->ppart_doubles * 8);
-  {
-    const size_t af = attn_partial_floats(m->M_cap, d.n_q_heads, d.head_dim, L);
-    if (af) ALLOC(m->attn_part, af * 4);
-  }
   for (int i = 0; i < 2; ++i) {
     ALLOC(m->idx[i], (size_t)m->M_cap * 4);
     ALLOC(m->nsel[i], (size_t)d.max_batch * 4);

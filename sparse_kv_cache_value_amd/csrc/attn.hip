@@ -27,8 +27,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-size_t attn_partial_floats(int, int, int, int) { return 0; }
-
 template <typename T>
 __global__ __launch_bounds__(64) void attn_ref_kernel(int B, int L, int Hq, int Hkv, int dh, float scale,
                                                       const int32_t* __restrict__ idx, const int32_t* __restrict__ n,
@@ -256,8 +254,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
 
 hipError_t launch_attention(hipStream_t st, bool bf16m, int max_rows, int B, int L, int Hq, int Hkv, int dh,
                             const int32_t* idx, const int32_t* n, const void* q, const void* Kc, const void* Vc,
-                            float* partial, void* out, int MTt) {
-  (void)partial;
+                            void* out, int MTt) {
   if (max_rows <= 0) return hipSuccess;
   const float scale = 1.0f / sqrtf((float)dh);
   if (bf16m && (dh == 128 || dh == 64) && L % 32 == 0) {

@@ -100,12 +100,11 @@ hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, in
                            int col0, int tile_stride);
 
 // ---- attention (attn.hip) ----
-size_t attn_partial_floats(int max_rows, int Hq, int dh, int L);
 // out: the GEMM input of the output projection ([M][Hq*dh], packed for bf16
 // with MTt row tiles).
 hipError_t launch_attention(hipStream_t st, bool bf16, int max_rows, int B, int L, int Hq, int Hkv, int dh,
                             const int32_t* idx, const int32_t* n, const void* q, const void* Kc,
-                            const void* Vc, float* partial, void* out, int MTt);
+                            const void* Vc, void* out, int MTt);
 
 // ---- LM head and commit (lmhead.hip) ----
 hipError_t launch_lm_gather(hipStream_t st, bool bf16, int B, int L, int blk, int d, float eps, int MTt,
