@@ -68,6 +68,19 @@ __device__ __forceinline__ bool row_of(const int32_t* __restrict__ idx, const in
   return false;
 }
 
+// row_of for a kernel that loaded n[0] and sequence 0's entry idx[min(m, L-1)]
+// itself, together with its other row-independent loads (one memory round
+// trip for a one-sequence batch); later sequences take row_of.  i0 is the
+// starting value on every path, so the compiler keeps its load where the
+// caller issued it.
+__device__ __forceinline__ bool row_resolve(const int32_t* __restrict__ idx, const int32_t* __restrict__ n, int B,
+                                            int L, int m, int n0, int i0, int& b, int& i) {
+  b = 0;
+  i = i0;
+  if (m < min(max(n0, 0), L)) return i >= 0 && i < L;
+  return B > 1 && row_of(idx, n, B, L, m, b, i);
+}
+
 // Total listed rows (same clamping), bounded by the caller's `cap` (the grid
 // and the partial buffers are sized for cap rows; rows past it are skipped).
 __device__ __forceinline__ int total_rows(const int32_t* __restrict__ n, int B, int cap) {
@@ -156,6 +169,26 @@ __device__ __forceinline__ void store_a8(float* A, int m, int k8, int /*MTt*/, i
 // One element of a GEMM input (packed for bf16).
 __device__ __forceinline__ void store_a1(bf16* A, int m, int k, int MTt, int, float v) { A[apack_off(m, k, MTt)] = f2bf(v); }
 __device__ __forceinline__ void store_a1(float* A, int m, int k, int, int ld, float v) { A[(size_t)m * ld + k] = v; }
+
+// The S split partials p[s * stride] of four consecutive columns, loaded
+// unconditionally (issued back to back), and their sum in split order.
+template <int S>
+__device__ __forceinline__ void load_splits4(const float* __restrict__ p, size_t stride, float4 (&t)[S]) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) t[s] = *reinterpret_cast<const float4*>(p + (size_t)s * stride);
+}
+template <int S>
+__device__ __forceinline__ float4 add_splits4(const float4 (&t)[S]) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    acc.x += t[s].x;
+    acc.y += t[s].y;
+    acc.z += t[s].z;
+    acc.w += t[s].w;
+  }
+  return acc;
+}
 
 // Sum of S split partials p[s * stride] in split order, loads issued in
 // batches of 8 so they overlap.

@@ -9,8 +9,9 @@
 // next chunk's weight fragments are loaded while the current one is
 // multiplied.  Weights are pre-packed into MFMA B-fragment order so that
 // every lane issues one 16-byte load per fragment and a wave's column tile is
-// one contiguous stream.  Split-K partials [S][M][N] are summed in a fixed
-// order by the epilogue kernels.  Workgroups sharing an A range are placed on
+// one contiguous stream.  Split-K partials [S][cap][N] (cap: the launch's row
+// capacity, so that a row's partial addresses do not depend on the selected
+// row count) are summed in a fixed order by the epilogue kernels.  Workgroups sharing an A range are placed on
 // the same XCD (workgroup i runs on XCD i % 8).
 #include "common.h"
 #include "kernels.h"
@@ -89,7 +90,7 @@ hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, in
 // loaded once per workgroup (wave w loads column tile w) and shared through a
 // double-buffered LDS stage.  Both operands are prefetched two chunks ahead in
 // registers, so the HBM weight stream overlaps the MFMAs of earlier chunks.
-// EPI 0 writes fp32 split-K partials out[split][m][n]; EPI 1 (one split)
+// EPI 0 writes fp32 split-K partials out[split][m][n] ([S][cap][N]); EPI 1 (one split)
 // applies SwiGLU to interleaved gate/up column tiles and writes the packed bf16
 // activation of the next GEMM.
 // ---------------------------------------------------------------------------
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int m = mrow + (i >> 2) * 8 + (i & 3);
-          if (m < M) out[((size_t)split * M + m) * N + ncol] = acc[j][nt][i];
+          if (m < M) out[((size_t)split * cap + m) * N + ncol] = acc[j][nt][i];
         }
       }
     }
@@ -555,7 +556,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int m = mrow + (i >> 2) * 8 + (i & 3);
-          if (m < M) out[((size_t)split * M + m) * N + ncol] = acc[mt][i];
+          if (m < M) out[((size_t)split * cap + m) * N + ncol] = acc[mt][i];
         }
       }
     }

@@ -25,7 +25,7 @@ hipError_t launch_embed(hipStream_t st, bool bf16, int max_rows, int B, int L, i
 hipError_t launch_gather_norm(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, float eps, int MTt,
                               const int32_t* idx, const int32_t* n, const void* H, const float* g,
                               void* A);
-// q/k RoPE + K/V scatter from QKV partials [S][M][nq + 2 nv].
+// q/k RoPE + K/V scatter from QKV partials [S][max_rows][nq + 2 nv].
 hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16, int max_rows, int B, int L, int Hq, int Hkv,
                                int dh, int S, const int32_t* idx, const int32_t* n, const float* part,
                                const float* rope_cos, const float* rope_sin, void* q_out, void* Kc,

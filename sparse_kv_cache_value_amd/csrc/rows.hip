@@ -217,54 +217,107 @@ hipError_t launch_gather_norm(hipStream_t st, bool bf16m, int max_rows, int B, i
 // QKV epilogue: sum split partials, rotate-half RoPE on q and k at the row's
 // position (cos/sin tables [L][dh/2]), write q (compact) and scatter k, v into
 // the cache rows [b][g][i][:].
+//
+// Split partials of every GEMM are laid out [S][cap][N] (cap = the launch's
+// row capacity), so their addresses depend on the compact row m only: a
+// thread issues all its partial loads together with the row-list loads and
+// only then waits, once, for the row's position.  S is a template parameter
+// (1, 2, 4, 8) so the loads are unconditional; other counts take the
+// runtime-S path (S = 0).
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq, int Hkv, int dh, int S, int cap,
+template <typename T, int S>
+__global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq, int Hkv, int dh, int Srt, int cap,
                                                            const int32_t* __restrict__ idx,
                                                            const int32_t* __restrict__ n,
                                                            const float* __restrict__ part,
                                                            const float* __restrict__ rc,
                                                            const float* __restrict__ rs, T* __restrict__ q,
                                                            T* __restrict__ Kc, T* __restrict__ Vc) {
-  int b, i;
   const int m = blockIdx.x;
-  if (!row_of(idx, n, B, L, m, b, i)) return;
-  const int M = total_rows(n, B, cap);
+  const int n0 = n[0];
+  const int i0 = idx[m < L ? m : L - 1];
   const int nq = Hq * dh, nv = Hkv * dh, N = nq + 2 * nv, half = dh / 2;
-  const size_t sstride = (size_t)M * N;
+  const size_t sstride = (size_t)cap * N;
   const float* p0 = part + (size_t)m * N;
-  // rotary pairs, four consecutive j per item
-  const int nquads = (Hq + Hkv) * (half / 4);
+  // item p: rotary quad p (four consecutive pairs (j, j + dh/2) of one q or k
+  // head) and value quad p (four consecutive value columns)
+  const int qph = half / 4, nquads = (Hq + Hkv) * qph, nvq = nv / 4;
+  const int items = nquads > nvq ? nquads : nvq;
   const int t0 = blockIdx.y * 256 + threadIdx.x, tstep = 256 * gridDim.y;
-  for (int p = t0; p < nquads; p += tstep) {
-    const int head = p / (half / 4), j = (p - head * (half / 4)) * 4;
-    const int c0 = head * dh + j, c1 = c0 + half;
-    const float4 a = sum_splits4(p0 + c0, sstride, S), c = sum_splits4(p0 + c1, sstride, S);
-    const float4 cs = *reinterpret_cast<const float4*>(rc + (size_t)i * half + j);
-    const float4 sn = *reinterpret_cast<const float4*>(rs + (size_t)i * half + j);
-    const float4 r0 = make_float4(a.x * cs.x - c.x * sn.x, a.y * cs.y - c.y * sn.y, a.z * cs.z - c.z * sn.z,
-                                  a.w * cs.w - c.w * sn.w);
-    const float4 r1 = make_float4(c.x * cs.x + a.x * sn.x, c.y * cs.y + a.y * sn.y, c.z * cs.z + a.z * sn.z,
-                                  c.w * cs.w + a.w * sn.w);
-    if (head < Hq) {
-      store4<T>(q + (size_t)m * nq + c0, r0);
-      store4<T>(q + (size_t)m * nq + c1, r1);
-    } else {
-      // four consecutive dimensions are adjacent in the fragment layout
-      T* kb = Kc + ((size_t)b * Hkv + (head - Hq)) * (size_t)l32_of(L) * dh;
-      store4<T>(kb + kc_off(i, j, dh), r0);
-      store4<T>(kb + kc_off(i, j + half, dh), r1);
+  constexpr int SA = S ? S : 1;
+  float4 ta[SA], tc[SA], tv[SA];
+  auto issue = [&](int p) {
+    if constexpr (S) {
+      const int pq = p < nquads ? p : 0, pv = p < nvq ? p : 0;
+      const int head = pq / qph, c0 = head * dh + (pq - head * qph) * 4;
+      load_splits4<S>(p0 + c0, sstride, ta);
+      load_splits4<S>(p0 + c0 + half, sstride, tc);
+      load_splits4<S>(p0 + nq + nv + pv * 4, sstride, tv);
+    }
+  };
+  if (t0 < items) issue(t0);
+  int b, i;
+  if (!row_resolve(idx, n, B, L, m, n0, i0, b, i)) return;
+  for (int p = t0; p < items; p += tstep) {
+    if (p != t0) issue(p);
+    if (p < nquads) {
+      const int head = p / qph, j = (p - head * qph) * 4;
+      const int c0 = head * dh + j, c1 = c0 + half;
+      const float4 cs = *reinterpret_cast<const float4*>(rc + (size_t)i * half + j);
+      const float4 sn = *reinterpret_cast<const float4*>(rs + (size_t)i * half + j);
+      float4 a, c;
+      if constexpr (S) {
+        a = add_splits4<S>(ta);
+        c = add_splits4<S>(tc);
+      } else {
+        a = sum_splits4(p0 + c0, sstride, Srt);
+        c = sum_splits4(p0 + c1, sstride, Srt);
+      }
+      const float4 r0 = make_float4(a.x * cs.x - c.x * sn.x, a.y * cs.y - c.y * sn.y, a.z * cs.z - c.z * sn.z,
+                                    a.w * cs.w - c.w * sn.w);
+      const float4 r1 = make_float4(c.x * cs.x + a.x * sn.x, c.y * cs.y + a.y * sn.y, c.z * cs.z + a.z * sn.z,
+                                    c.w * cs.w + a.w * sn.w);
+      if (head < Hq) {
+        store4<T>(q + (size_t)m * nq + c0, r0);
+        store4<T>(q + (size_t)m * nq + c1, r1);
+      } else {
+        // four consecutive dimensions are adjacent in the fragment layout
+        T* kb = Kc + ((size_t)b * Hkv + (head - Hq)) * (size_t)l32_of(L) * dh;
+        store4<T>(kb + kc_off(i, j, dh), r0);
+        store4<T>(kb + kc_off(i, j + half, dh), r1);
+      }
+    }
+    if (p < nvq) {
+      const int c4 = p * 4;
+      float4 v;
+      if constexpr (S) v = add_splits4<S>(tv);
+      else v = sum_splits4(p0 + nq + nv + c4, sstride, Srt);
+      const int g = c4 / dh, t = c4 - g * dh;
+      T* vb = Vc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * dh;
+      io<T>::st(vb + vc_off(i, t, dh), v.x);
+      io<T>::st(vb + vc_off(i, t + 1, dh), v.y);
+      io<T>::st(vb + vc_off(i, t + 2, dh), v.z);
+      io<T>::st(vb + vc_off(i, t + 3, dh), v.w);
     }
   }
-  for (int c4 = t0 * 4; c4 < nv; c4 += tstep * 4) {
-    const float4 v = sum_splits4(p0 + nq + nv + c4, sstride, S);
-    const int g = c4 / dh, t = c4 - g * dh;
-    T* vb = Vc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * dh;
-    io<T>::st(vb + vc_off(i, t, dh), v.x);
-    io<T>::st(vb + vc_off(i, t + 1, dh), v.y);
-    io<T>::st(vb + vc_off(i, t + 2, dh), v.z);
-    io<T>::st(vb + vc_off(i, t + 3, dh), v.w);
+}
+
+template <typename T>
+static hipError_t qkv_epi_cfg(hipStream_t st, int max_rows, int B, int L, int Hq, int Hkv, int dh, int S,
+                              const int32_t* idx, const int32_t* n, const float* part, const float* rc,
+                              const float* rs, T* q, T* Kc, T* Vc) {
+  const dim3 grid(max_rows, 4), blk(256);
+#define QE(SS) hipLaunchKernelGGL((qkv_epilogue_kernel<T, SS>), grid, blk, 0, st, B, L, Hq, Hkv, dh, S, max_rows, idx, \
+                                  n, part, rc, rs, q, Kc, Vc)
+  switch (S) {
+    case 1: QE(1); break;
+    case 2: QE(2); break;
+    case 4: QE(4); break;
+    case 8: QE(8); break;
+    default: QE(0); break;
   }
+#undef QE
+  return hipGetLastError();
 }
 
 hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, int L, int Hq, int Hkv,
@@ -273,34 +326,47 @@ hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, 
                                void* Vc) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(qkv_epilogue_kernel<bf16>, dim3(max_rows, 4), dim3(256), 0, st, B, L, Hq, Hkv, dh, S,
-                       max_rows, idx, n, part, rope_cos, rope_sin, (bf16*)q_out, (bf16*)Kc, (bf16*)Vc);
-  else
-    hipLaunchKernelGGL(qkv_epilogue_kernel<float>, dim3(max_rows, 4), dim3(256), 0, st, B, L, Hq, Hkv, dh, S,
-                       max_rows, idx, n, part, rope_cos, rope_sin, (float*)q_out, (float*)Kc, (float*)Vc);
-  return hipGetLastError();
+    return qkv_epi_cfg<bf16>(st, max_rows, B, L, Hq, Hkv, dh, S, idx, n, part, rope_cos, rope_sin, (bf16*)q_out,
+                             (bf16*)Kc, (bf16*)Vc);
+  return qkv_epi_cfg<float>(st, max_rows, B, L, Hq, Hkv, dh, S, idx, n, part, rope_cos, rope_sin, (float*)q_out,
+                            (float*)Kc, (float*)Vc);
 }
 
 // ---------------------------------------------------------------------------
 // Output projection epilogue: h' = x + o W_o (fp32, split partials summed in
-// order), then the FFN norm into the next GEMM's input.
+// order), then the FFN norm into the next GEMM's input.  The partial loads
+// are issued before the row's position is known (split layout [S][cap][d]).
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(RT) void o_epilogue_kernel(int B, int L, int d, int S, int cap, float eps, int MTt,
+template <typename T, int S>
+__global__ __launch_bounds__(RT) void o_epilogue_kernel(int B, int L, int d, int Srt, int cap, float eps, int MTt,
                                                          const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ n,
                                                          const float* __restrict__ part,
                                                          const T* __restrict__ H, const float* __restrict__ g2,
                                                          float* __restrict__ hprime, T* __restrict__ A2) {
   __shared__ float red[RT / 64];
-  int b, i;
   const int m = blockIdx.x;
-  if (!row_of(idx, n, B, L, m, b, i)) return;
-  const int M = total_rows(n, B, cap);
-  const size_t sstride = (size_t)M * d;
+  const int n0 = n[0];
+  const int i0 = idx[m < L ? m : L - 1];
+  const size_t sstride = (size_t)cap * d;
+  const float* p0 = part + (size_t)m * d;
+  constexpr int SA = S ? S : 1;
+  float4 t[RV][2][SA];
+  if constexpr (S) {
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const int c8 = (threadIdx.x + r * RT) * 8;
+      if (r == 0 || c8 < d) {
+        const int cc = c8 < d ? c8 : 0;
+        load_splits4<S>(p0 + cc, sstride, t[r][0]);
+        load_splits4<S>(p0 + cc + 4, sstride, t[r][1]);
+      }
+    }
+  }
+  int b, i;
+  if (!row_resolve(idx, n, B, L, m, n0, i0, b, i)) return;
   const T* x = H + ((size_t)b * L + i) * d;
   float* hp = hprime + (size_t)m * d;
-  const float* p0 = part + (size_t)m * d;
   float v[RV][8];
   float ss = 0.f;
 #pragma unroll
@@ -308,7 +374,14 @@ __global__ __launch_bounds__(RT) void o_epilogue_kernel(int B, int L, int d, int
     const int c8 = (threadIdx.x + r * RT) * 8;
     if (c8 < d) {
       load8<T>(x + c8, v[r]);
-      const float4 a = sum_splits4(p0 + c8, sstride, S), c = sum_splits4(p0 + c8 + 4, sstride, S);
+      float4 a, c;
+      if constexpr (S) {
+        a = add_splits4<S>(t[r][0]);
+        c = add_splits4<S>(t[r][1]);
+      } else {
+        a = sum_splits4(p0 + c8, sstride, Srt);
+        c = sum_splits4(p0 + c8 + 4, sstride, Srt);
+      }
       v[r][0] += a.x; v[r][1] += a.y; v[r][2] += a.z; v[r][3] += a.w;
       v[r][4] += c.x; v[r][5] += c.y; v[r][6] += c.z; v[r][7] += c.w;
       *reinterpret_cast<float4*>(hp + c8) = make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
@@ -331,17 +404,30 @@ __global__ __launch_bounds__(RT) void o_epilogue_kernel(int B, int L, int d, int
   }
 }
 
+template <typename T>
+static hipError_t o_epi_cfg(hipStream_t st, int max_rows, int B, int L, int d, int S, float eps, int MTt,
+                            const int32_t* idx, const int32_t* n, const float* part, const T* H, const float* g2,
+                            float* hprime, T* A2) {
+#define OE(SS) hipLaunchKernelGGL((o_epilogue_kernel<T, SS>), dim3(max_rows), dim3(RT), 0, st, B, L, d, S, max_rows, \
+                                  eps, MTt, idx, n, part, H, g2, hprime, A2)
+  switch (S) {
+    case 1: OE(1); break;
+    case 2: OE(2); break;
+    case 4: OE(4); break;
+    case 8: OE(8); break;
+    default: OE(0); break;
+  }
+#undef OE
+  return hipGetLastError();
+}
+
 hipError_t launch_o_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, int S,
                              float eps, int MTt, const int32_t* idx, const int32_t* n, const float* part,
                              const void* H, const float* g2, float* hprime, void* A2) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(o_epilogue_kernel<bf16>, dim3(max_rows), dim3(RT), 0, st, B, L, d, S, max_rows, eps, MTt,
-                       idx, n, part, (const bf16*)H, g2, hprime, (bf16*)A2);
-  else
-    hipLaunchKernelGGL(o_epilogue_kernel<float>, dim3(max_rows), dim3(RT), 0, st, B, L, d, S, max_rows, eps, MTt,
-                       idx, n, part, (const float*)H, g2, hprime, (float*)A2);
-  return hipGetLastError();
+    return o_epi_cfg<bf16>(st, max_rows, B, L, d, S, eps, MTt, idx, n, part, (const bf16*)H, g2, hprime, (bf16*)A2);
+  return o_epi_cfg<float>(st, max_rows, B, L, d, S, eps, MTt, idx, n, part, (const float*)H, g2, hprime, (float*)A2);
 }
 
 // ---------------------------------------------------------------------------
@@ -357,7 +443,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(int B, int F, int S, int ca
   const int f = blockIdx.x * 256 + threadIdx.x;
   if (f >= F) return;
   const int N = 2 * F;
-  const size_t sstride = (size_t)M * N;
+  const size_t sstride = (size_t)cap * N;
   const int cg = (f >> 5) * 64 + (f & 31);
   const float gv = sum_splits(part + (size_t)m * N + cg, sstride, S);
   const float uv = sum_splits(part + (size_t)m * N + cg + 32, sstride, S);
@@ -379,32 +465,65 @@ hipError_t launch_swiglu(hipStream_t st, bool bf16m, int max_rows, int B, int F,
 // ---------------------------------------------------------------------------
 // Down-projection epilogue: out = h' + act W_down, written back at the row's
 // slot of the next layer's input; the row's proxy reference is refreshed.
+// The partial and h' loads are issued before the row's position is known.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void down_epilogue_kernel(int B, int L, int d, int r, int S, int cap,
+template <typename T, int S>
+__global__ __launch_bounds__(256) void down_epilogue_kernel(int B, int L, int d, int r, int Srt, int cap,
                                                             const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ n,
                                                             const float* __restrict__ part,
                                                             const float* __restrict__ hprime,
                                                             T* __restrict__ Hout, const double* __restrict__ pcur,
                                                             double* __restrict__ pref, double* __restrict__ score) {
-  int b, i;
   const int m = blockIdx.x;
-  if (!row_of(idx, n, B, L, m, b, i)) return;
-  const int M = total_rows(n, B, cap);
-  const size_t sstride = (size_t)M * d;
-  const size_t row = (size_t)b * L + i;
-  T* o = Hout + row * d;
+  const int n0 = n[0];
+  const int i0 = idx[m < L ? m : L - 1];
+  const size_t sstride = (size_t)cap * d;
   const float* hp = hprime + (size_t)m * d;
   const float* p0 = part + (size_t)m * d;
-  for (int c4 = (blockIdx.y * 256 + threadIdx.x) * 4; c4 < d; c4 += 256 * gridDim.y * 4) {
-    const float4 a = sum_splits4(p0 + c4, sstride, S);
-    const float4 h = *reinterpret_cast<const float4*>(hp + c4);
+  const int t0 = (blockIdx.y * 256 + threadIdx.x) * 4, tstep = 256 * gridDim.y * 4;
+  constexpr int SA = S ? S : 1;
+  float4 t[SA], h;
+  if constexpr (S)
+    if (t0 < d) {
+      h = *reinterpret_cast<const float4*>(hp + t0);
+      load_splits4<S>(p0 + t0, sstride, t);
+    }
+  int b, i;
+  if (!row_resolve(idx, n, B, L, m, n0, i0, b, i)) return;
+  const size_t row = (size_t)b * L + i;
+  T* o = Hout + row * d;
+  for (int c4 = t0; c4 < d; c4 += tstep) {
+    float4 a;
+    if (S && c4 == t0) {
+      if constexpr (S) a = add_splits4<S>(t);
+    } else {
+      a = sum_splits4(p0 + c4, sstride, Srt);
+      h = *reinterpret_cast<const float4*>(hp + c4);
+    }
     store4<T>(o + c4, make_float4(h.x + a.x, h.y + a.y, h.z + a.z, h.w + a.w));
   }
   if (blockIdx.y != 0 || !pref) return;
   for (int j = threadIdx.x; j < r; j += 256) pref[row * r + j] = pcur[row * r + j];
   if (threadIdx.x == 0) score[row] = 0.0;
+}
+
+template <typename T>
+static hipError_t down_epi_cfg(hipStream_t st, int max_rows, int B, int L, int d, int r, int S, const int32_t* idx,
+                               const int32_t* n, const float* part, const float* hprime, T* H_out,
+                               const double* pcur, double* pref, double* score) {
+  const dim3 grid(max_rows, 4), blk(256);
+#define DE(SS) hipLaunchKernelGGL((down_epilogue_kernel<T, SS>), grid, blk, 0, st, B, L, d, r, S, max_rows, idx, n, \
+                                  part, hprime, H_out, pcur, pref, score)
+  switch (S) {
+    case 1: DE(1); break;
+    case 2: DE(2); break;
+    case 4: DE(4); break;
+    case 8: DE(8); break;
+    default: DE(0); break;
+  }
+#undef DE
+  return hipGetLastError();
 }
 
 hipError_t launch_down_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, int r,
@@ -413,12 +532,8 @@ hipError_t launch_down_epilogue(hipStream_t st, bool bf16m, int max_rows, int B,
                                 double* score) {
   if (max_rows <= 0) return hipSuccess;
   if (bf16m)
-    hipLaunchKernelGGL(down_epilogue_kernel<bf16>, dim3(max_rows, 4), dim3(256), 0, st, B, L, d, r, S, max_rows, idx, n,
-                       part, hprime, (bf16*)H_out, pcur, pref, score);
-  else
-    hipLaunchKernelGGL(down_epilogue_kernel<float>, dim3(max_rows, 4), dim3(256), 0, st, B, L, d, r, S, max_rows, idx, n,
-                       part, hprime, (float*)H_out, pcur, pref, score);
-  return hipGetLastError();
+    return down_epi_cfg<bf16>(st, max_rows, B, L, d, r, S, idx, n, part, hprime, (bf16*)H_out, pcur, pref, score);
+  return down_epi_cfg<float>(st, max_rows, B, L, d, r, S, idx, n, part, hprime, (float*)H_out, pcur, pref, score);
 }
 
 }  // namespace dllm
