@@ -126,10 +126,11 @@ __global__ __launch_bounds__(64 * PS_GRAM_WAVES) void ps_gram_kernel(int L, int 
 // member sum; others keep their centroid.  Then a final assignment.  Outputs
 // the assignment, the row norms and each centroid's coefficients over the
 // unit rows.  A cluster's members come from two 64-row ballots and are
-// visited in ascending row order; member sums and the squared norm are added
-// in that order.
+// visited in ascending row order (eight at a time, their rows read together);
+// member sums and the squared norm are added in that order.
 // ---------------------------------------------------------------------------
 constexpr int PS_KM_THREADS = 1024;  // 16 waves: one per cluster (K <= 16)
+constexpr int PS_KM_EPT = 9;         // Gram elements a thread loads at once (one pass for W <= 96)
 
 __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, int iters, const double* __restrict__ R,
                                                                  int32_t* __restrict__ assign,
@@ -139,34 +140,46 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
   double* G = sm;                 // [W][W]  Gram of the unit rows
   double* D = G + W * W;          // [K][W]  centroid . unit row
   double* nrm = D + K * W;        // [W]
-  int* a = reinterpret_cast<int*>(nrm + W);  // [W] (W <= 128)
+  double* dump = nrm + W;         // [1]  target of the stores past the Gram
+  int* a = reinterpret_cast<int*>(dump + 1);  // [W] (W <= 128)
   const int b = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  // Gram = sum of the split partials in split order, then normalised
+  // Gram = sum of the split partials in split order (a thread's loads for up
+  // to PS_KM_EPT elements issued together), then normalised
   const double* Rb = R + (size_t)b * PS_GRAM_SPLITS * W * W;
-  const size_t WW = (size_t)W * W;
-  for (int e0 = tid; e0 < W * W; e0 += 4 * PS_KM_THREADS) {
-    double v[4][PS_GRAM_SPLITS];
+  const int WW = W * W;
+  for (int e0 = tid; e0 < WW; e0 += PS_KM_EPT * PS_KM_THREADS) {
+    double v[PS_KM_EPT][PS_GRAM_SPLITS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < PS_KM_EPT; ++u)
 #pragma unroll
-      for (int q = 0; q < PS_GRAM_SPLITS; ++q) v[u][q] = Rb[q * WW + min(e0 + u * PS_KM_THREADS, W * W - 1)];
+      for (int q = 0; q < PS_GRAM_SPLITS; ++q)
+        v[u][q] = Rb[(size_t)q * WW + min(e0 + u * PS_KM_THREADS, WW - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < PS_KM_EPT; ++u) {
       const int e = e0 + u * PS_KM_THREADS;
       double t = v[u][0];
 #pragma unroll
       for (int q = 1; q < PS_GRAM_SPLITS; ++q) t += v[u][q];
-      if (e < W * W) G[e] = t;
+      // unconditional store (so the loads stay in the batch above)
+      *(e < WW ? G + e : dump) = t;
     }
   }
   __syncthreads();
   for (int i = tid; i < W; i += PS_KM_THREADS) nrm[i] = sqrt(G[(size_t)i * W + i]);
   __syncthreads();
-  for (int e = tid; e < W * W; e += PS_KM_THREADS) {
-    const int i = e / W, j = e - i * W;
-    const double ni = nrm[i], nj = nrm[j];
-    G[e] = (ni > 0.0 && nj > 0.0) ? G[e] / (ni * nj) : 0.0;
+  {
+    // unit-row Gram G[i][j] / (|x_i| |x_j|): thread column j = tid % 128,
+    // rows tid / 128 + 8 t (a wave touches one row, conflict-free)
+    const int j = tid & 127;
+    if (j < W) {
+      const double nj = nrm[j];
+      for (int i = tid >> 7; i < W; i += PS_KM_THREADS / 128) {
+        const double ni = nrm[i];
+        double* g = G + (size_t)i * W + j;
+        *g = (ni > 0.0 && nj > 0.0) ? *g / (ni * nj) : 0.0;
+      }
+    }
   }
   const int stride = W / K;
   double* cf = coef + (size_t)b * K * W;
@@ -182,15 +195,19 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
   auto do_assign = [&]() -> bool {
     int changed = 0;
     for (int i = tid; i < W; i += PS_KM_THREADS) {
+      // all K dot products read first (one LDS latency), then compared in
+      // cluster order
+      double dv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dv[j] = D[(j < K ? j : K - 1) * W + i];
       int best = 0;
-      double bv = D[i];
-      for (int j = 1; j < K; ++j) {
-        const double v = D[j * W + i];
-        if (v > bv) {
-          bv = v;
+      double bv = dv[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j)
+        if (j < K && dv[j] > bv) {
+          bv = dv[j];
           best = j;
         }
-      }
       changed |= a[i] != best;
       a[i] = best;
     }
@@ -205,25 +222,54 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
       // members of cluster j, rows 0..63 and 64..127
       const unsigned long long m0 = __ballot(lane < W && a[lane] == j);
       const unsigned long long m1 = __ballot(lane + 64 < W && a[lane + 64] == j);
-      // member sums of this lane's columns k = lane, lane + 64
+      // member sums of this lane's columns k = lane, lane + 64; members are
+      // taken eight at a time (their rows read together), added in
+      // ascending row order
       double v0 = 0.0, v1 = 0.0;
       for (int h = 0; h < 2; ++h) {
         unsigned long long m = h ? m1 : m0;
         while (m) {
-          const int i = __ffsll((long long)m) - 1 + 64 * h;
-          m &= m - 1;
-          if (lane < W) v0 += G[(size_t)i * W + lane];
-          if (lane + 64 < W) v1 += G[(size_t)i * W + lane + 64];
+          int ii[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            ii[u] = m ? __ffsll((long long)m) - 1 + 64 * h : -1;
+            m &= m - 1;
+          }
+          double g0[8], g1[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (ii[u] >= 0) {
+              g0[u] = lane < W ? G[(size_t)ii[u] * W + lane] : 0.0;
+              g1[u] = lane + 64 < W ? G[(size_t)ii[u] * W + lane + 64] : 0.0;
+            }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (ii[u] >= 0) {
+              if (lane < W) v0 += g0[u];
+              if (lane + 64 < W) v1 += g1[u];
+            }
         }
       }
-      // |member sum|^2 = sum over member columns k (ascending) of v[k]
+      // |member sum|^2 = sum over member columns k (ascending) of v[k], eight
+      // shuffles at a time
       double n2 = 0.0;
       for (int h = 0; h < 2; ++h) {
         unsigned long long m = h ? m1 : m0;
+        const double vh = h ? v1 : v0;
         while (m) {
-          const int k = __ffsll((long long)m) - 1;
-          m &= m - 1;
-          n2 += __shfl(h ? v1 : v0, k, 64);
+          int kk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            kk[u] = m ? __ffsll((long long)m) - 1 : -1;
+            m &= m - 1;
+          }
+          double sv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (kk[u] >= 0) sv[u] = __shfl(vh, kk[u], 64);
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (kk[u] >= 0) n2 += sv[u];
         }
       }
       if ((m0 | m1) != 0ull && n2 > 0.0) {
@@ -252,71 +298,127 @@ __global__ __launch_bounds__(PS_KM_THREADS) void ps_kmeans_kernel(int W, int K, 
 // Explicit centroids c_j = sum_i coef[j][i] * x_i / |x_i| (fp64, ascending i),
 // and the packed query-path input bf16(RMSNorm(c_j) * g1) (fp64 norm, rounded
 // to fp32 then to the storage dtype, as the layer's own input path).  One
-// workgroup per (cluster, sequence); each thread owns 8 consecutive dims and
-// reads the members' rows in batches of 4 so their loads overlap.
+// workgroup per (cluster, sequence); each thread owns 8 consecutive dims (of
+// up to 8192) and reads the members' rows raw, CB at a time, so their loads
+// overlap; the members' weights and norms are staged in LDS.
 // ---------------------------------------------------------------------------
 constexpr int PS_CENT_THREADS = 512;
+
+template <typename T>
+struct RawRow8;  // 8 consecutive stored values of a row, as loaded
+template <>
+struct RawRow8<bf16> {
+  static constexpr int CB = 16;  // member rows in flight per thread
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void widen(double* v) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = (double)__uint_as_float(w[e] << 16);
+      v[2 * e + 1] = (double)__uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct RawRow8<float> {
+  static constexpr int CB = 8;
+  float4 a, c;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    c = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void widen(double* v) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+  }
+};
 
 template <typename T>
 __global__ __launch_bounds__(PS_CENT_THREADS) void ps_centroid_kernel(
     int L, int d, int blk, int W, int K, float eps, int MTt, const int32_t* __restrict__ bstart,
     const T* __restrict__ H, const double* __restrict__ coef, const double* __restrict__ norms,
     const float* __restrict__ g1, double* __restrict__ cent, T* __restrict__ A) {
+  constexpr int CB = RawRow8<T>::CB;
+  constexpr int NIT = 2;  // dims per thread: NIT groups of 8 (d <= 8192)
   __shared__ double red[PS_CENT_THREADS / 64];
   __shared__ int mem[128];
+  __shared__ double wmem[128], nmem[128];
   __shared__ int nm_s;
   const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ws = ps_window_start(bstart[b], L, blk, W);
   const double* cw = coef + ((size_t)b * K + j) * W;
-  if (wv == 0) {  // members in ascending row order (W <= 128)
-    const bool f0 = lane < W && cw[lane] != 0.0;
-    const bool f1 = lane + 64 < W && cw[lane + 64] != 0.0;
+  const double* nb = norms + (size_t)b * W;
+  if (wv == 0) {  // members in ascending row order (W <= 128), with weight and norm
+    const double w0 = lane < W ? cw[lane] : 0.0, w1 = lane + 64 < W ? cw[lane + 64] : 0.0;
+    const double n0 = lane < W ? nb[lane] : 0.0, n1 = lane + 64 < W ? nb[lane + 64] : 0.0;
+    const bool f0 = lane < W && w0 != 0.0;
+    const bool f1 = lane + 64 < W && w1 != 0.0;
     const unsigned long long m0 = __ballot(f0), m1 = __ballot(f1);
     const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
     const int c0 = __popcll(m0);
-    if (f0) mem[__popcll(m0 & below)] = lane;
-    if (f1) mem[c0 + __popcll(m1 & below)] = lane + 64;
+    if (f0) {
+      const int k = __popcll(m0 & below);
+      mem[k] = lane;
+      wmem[k] = w0;
+      nmem[k] = n0;
+    }
+    if (f1) {
+      const int k = c0 + __popcll(m1 & below);
+      mem[k] = lane + 64;
+      wmem[k] = w1;
+      nmem[k] = n1;
+    }
     if (lane == 0) nm_s = c0 + __popcll(m1);
   }
   __syncthreads();
   const int nm = nm_s;
   const T* xw = H + ((size_t)b * L + ws) * d;
-  const double* nb = norms + (size_t)b * W;
   double* cj = cent + ((size_t)b * K + j) * d;
+  double acc[NIT][8];
   double ss = 0.0;
-  for (int t8 = tid * 8; t8 < d; t8 += PS_CENT_THREADS * 8) {
-    double acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    for (int q0 = 0; q0 < nm; q0 += 4) {
-      double x[4][8], wq[4], nq[4];
+  for (int it = 0; it < NIT; ++it) {
+    const int t8 = (tid + it * PS_CENT_THREADS) * 8;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = mem[min(q0 + u, nm - 1)];
-        ld8d(xw + (size_t)i * d + t8, x[u]);
-        wq[u] = cw[i];
-        nq[u] = nb[i];
-      }
+    for (int e = 0; e < 8; ++e) acc[it][e] = 0.0;
+    if (t8 >= d) continue;
+    for (int q0 = 0; q0 < nm; q0 += CB) {
+      // every row address first, then the CB loads back to back
+      const T* src[CB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < CB; ++u) src[u] = xw + (size_t)mem[min(q0 + u, nm - 1)] * d + t8;
+      RawRow8<T> raw[CB];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < CB; ++u) raw[u].load(src[u]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
         if (q0 + u < nm) {
+          double x[8];
+          raw[u].widen(x);
+          const double wq = wmem[q0 + u], nq = nmem[q0 + u];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += wq[u] * (x[u][e] / nq[u]);
+          for (int e = 0; e < 8; ++e) acc[it][e] += wq * (x[e] / nq);
         }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      cj[t8 + e] = acc[e];
-      ss += acc[e] * acc[e];
+      cj[t8 + e] = acc[it][e];
+      ss += acc[it][e] * acc[it][e];
     }
   }
   const double tot = block_sum<PS_CENT_THREADS / 64>(ss, red);
   const double rms = sqrt(tot / (double)d + (double)eps);
   const int m = b * K + j;
-  for (int t8 = tid * 8; t8 < d; t8 += PS_CENT_THREADS * 8) {
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int t8 = (tid + it * PS_CENT_THREADS) * 8;
+    if (t8 >= d) continue;
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)(cj[t8 + e] / rms * (double)g1[t8 + e]);
+    for (int e = 0; e < 8; ++e) v[e] = (float)(acc[it][e] / rms * (double)g1[t8 + e]);
     store_a8(A, m, t8, MTt, d, v);
   }
 }
@@ -786,10 +888,10 @@ hipError_t launch_ps_gram(hipStream_t st, bool bf16m, int B, int L, int d, int b
 hipError_t launch_ps_kmeans(hipStream_t st, int B, int W, int K, int iters, const double* R, int32_t* assign,
                             double* norms, double* coef, int32_t* nsel) {
   if (W > PS_WMAX || W > 128 || K > 16 || K < 1 || W < K) return hipErrorInvalidValue;
-  const size_t lds = ((size_t)W * W + K * W + W) * sizeof(double) + (size_t)W * sizeof(int);
+  const size_t lds = ((size_t)W * W + K * W + W + 1) * sizeof(double) + (size_t)W * sizeof(int);
   static std::atomic<unsigned long long> attr{0};
   hipError_t ea = once_per_device(attr, [] {
-    const size_t mx = ((size_t)PS_WMAX * PS_WMAX + 16 * PS_WMAX + PS_WMAX) * sizeof(double) + PS_WMAX * sizeof(int);
+    const size_t mx = ((size_t)PS_WMAX * PS_WMAX + 16 * PS_WMAX + PS_WMAX + 1) * sizeof(double) + PS_WMAX * sizeof(int);
     return hipFuncSetAttribute((const void*)ps_kmeans_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mx);
   });
   if (ea != hipSuccess) return ea;
@@ -801,6 +903,7 @@ hipError_t launch_ps_kmeans(hipStream_t st, int B, int W, int K, int iters, cons
 hipError_t launch_ps_centroids(hipStream_t st, bool bf16m, int B, int L, int d, int blk, int W, int K, float eps,
                                int MTt, const int32_t* bstart, const void* H, const double* coef,
                                const double* norms, const float* g1, double* cent, void* A) {
+  if (d > 2 * PS_CENT_THREADS * 8 || d % 8) return hipErrorInvalidValue;  // dims per thread: two groups of 8
   if (bf16m)
     hipLaunchKernelGGL(ps_centroid_kernel<bf16>, dim3(K, B), dim3(PS_CENT_THREADS), 0, st, L, d, blk, W, K, eps, MTt, bstart,
                        (const bf16*)H, coef, norms, g1, cent, (bf16*)A);
