@@ -93,7 +93,7 @@ struct dllm_model {
   float* logits = nullptr;
   double* lm_part = nullptr;
   double* lm_stats = nullptr;
-  double* lm_wpart = nullptr;  // per-slab statistics of the fused LM head [64][vocab/128][4]
+  double* lm_wpart = nullptr;  // per-slab statistics of the fused LM head [rows][vocab/128][4]
   int32_t* lm_rows = nullptr;
   int lm_slabs = 0;
   // Polestar drift path workspace
@@ -378,11 +378,16 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
   return DLLM_OK;
 }
 
+// Rows the weight-streaming GEMM takes (9 row tiles): the LM head's fused
+// statistics path and its streaming logits path.
+constexpr int LM_FUSED_ROWS = 288;
+
 // LM-head statistics of the first nblk blocks from each sequence's block
-// start (nblk = 1: the current block; 2: also the next one).  Up to 64 rows
-// and no logits wanted: the statistics come out of the weight-streaming GEMM
-// per 128-column slab and one merge (no logits buffer); otherwise the logits
-// are materialised (m->logits) and reduced by slab and merge kernels.
+// start (nblk = 1: the current block; 2: also the next one).  Up to
+// LM_FUSED_ROWS rows and no logits wanted: the statistics come out of the
+// weight-streaming GEMM per 128-column slab and one merge (no logits buffer);
+// otherwise the logits are materialised (m->logits) and reduced by slab and
+// merge kernels.
 dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int nblk = 1, bool want_logits = false) {
   const dllm_dims& d = m->d;
   const int B = s->batch, blk = d.block_len * nblk;
@@ -392,7 +397,7 @@ dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int n
                             hid(m, s, d.n_layers), m->final_norm, m->A_lm, m->lm_rows));
     prof.done();
   }
-  if (m->bf16 && !want_logits && m->lm_wpart && B * blk <= 64 &&
+  if (m->bf16 && !want_logits && m->lm_wpart && B * blk <= LM_FUSED_ROWS &&
       gemm_stream_pick_splits(B * blk, d.d_model, d.vocab, m->n_cu, false, m->lm_MTt) > 0) {
     const int ns = d.vocab / 128;
     ProfLaunch prof(m, DLLM_PROF_LMHEAD,
@@ -413,9 +418,10 @@ dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int n
                     (double)d.d_model * d.vocab * 2.0 + (double)B * blk * d.d_model * 2.0 +
                         (double)B * blk * d.vocab * 4.0,
                     2.0 * B * blk * (double)d.d_model * d.vocab);
-    // up to two row tiles the weight-streaming kernel reads W_lm faster (one
-    // split: the logits are written once, in the same [M][V] layout)
-    const int ss = B * blk <= 64 ? gemm_stream_pick_splits(B * blk, d.d_model, d.vocab, m->n_cu, false, m->lm_MTt) : 0;
+    // the weight-streaming kernel (one split: the logits are written once, in
+    // the same [M][V] layout), as in the fused path, where the rows fit it
+    const int ss =
+        B * blk <= LM_FUSED_ROWS ? gemm_stream_pick_splits(B * blk, d.d_model, d.vocab, m->n_cu, false, m->lm_MTt) : 0;
     if (ss == 1)
       HIPCHK(launch_gemm_stream(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
                                 (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0, prof.ev));
@@ -677,7 +683,8 @@ dllm_status dllm_create(const dllm_dims* dims, dllm_model** out) {
   m->lm_slabs = lm_stats_slabs(d.vocab);
   ALLOC(m->lm_part, (size_t)lm_rows_cap * m->lm_slabs * 4 * 8);
   ALLOC(m->lm_stats, (size_t)lm_rows_cap * 4 * 8);
-  if (m->bf16 && d.vocab % 128 == 0) ALLOC(m->lm_wpart, (size_t)64 * (d.vocab / 128) * 4 * 8);
+  if (m->bf16 && d.vocab % 128 == 0)
+    ALLOC(m->lm_wpart, (size_t)std::min(lm_rows_cap, LM_FUSED_ROWS) * (d.vocab / 128) * 4 * 8);
   ALLOC(m->lm_rows, 16);
   if (D % 128 == 0) {
     const size_t wmax = 120;

@@ -507,45 +507,49 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
       for (int i = 0; i < 16; ++i) zs[(mrow + (i >> 2) * 8 + (i & 3)) * ZLD + wv * 32 + (lane & 31)] = acc[mt][i];
     }
     __syncthreads();
-    // four threads per row, 32 columns each, combined in a fixed order
-    const int r = min(tid >> 2, MT * 32 - 1), q = tid & 3;
-    const float* zr = zs + r * ZLD + q * 32;
-    float best = zr[0];
-    int bidx = 0;
-    for (int c = 1; c < 32; ++c)
-      if (zr[c] > best) {  // increasing column order keeps the lowest index
-        best = zr[c];
-        bidx = c;
-      }
-    bidx += slab * 128 + q * 32;
+    // four threads per row, 32 columns each, combined in a fixed order; 64
+    // rows per pass
+    const int q = tid & 3;
+    for (int r0 = 0; r0 < MT * 32; r0 += 64) {
+      const int rr = r0 + (tid >> 2);
+      const float* zr = zs + min(rr, MT * 32 - 1) * ZLD + q * 32;
+      float best = zr[0];
+      int bidx = 0;
+      for (int c = 1; c < 32; ++c)
+        if (zr[c] > best) {  // increasing column order keeps the lowest index
+          best = zr[c];
+          bidx = c;
+        }
+      bidx += slab * 128 + q * 32;
 #pragma unroll
-    for (int o = 1; o <= 2; o <<= 1) {
-      const float ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bidx, o, 64);
-      if (ov > best || (ov == best && oi < bidx)) {
-        best = ov;
-        bidx = oi;
+      for (int o = 1; o <= 2; o <<= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bidx, o, 64);
+        if (ov > best || (ov == best && oi < bidx)) {
+          best = ov;
+          bidx = oi;
+        }
       }
-    }
-    const double mx = (double)best;
-    double sa = 0.0, ta = 0.0;
-    for (int c = 0; c < 32; ++c) {
-      const double dz = (double)zr[c] - mx;
-      const double e = exp(dz);
-      sa += e;
-      ta += e * dz;
-    }
+      const double mx = (double)best;
+      double sa = 0.0, ta = 0.0;
+      for (int c = 0; c < 32; ++c) {
+        const double dz = (double)zr[c] - mx;
+        const double e = exp(dz);
+        sa += e;
+        ta += e * dz;
+      }
 #pragma unroll
-    for (int o = 1; o <= 2; o <<= 1) {  // commutative pairs: every lane of the row gets the same sums
-      sa += __shfl_xor(sa, o, 64);
-      ta += __shfl_xor(ta, o, 64);
-    }
-    if (q == 0 && (tid >> 2) < MT * 32 && (tid >> 2) < M) {
-      double* p = reinterpret_cast<double*>(out) + ((size_t)(tid >> 2) * n_slabs + slab) * 4;
-      p[0] = mx;
-      p[1] = (double)bidx;
-      p[2] = sa;
-      p[3] = ta;
+      for (int o = 1; o <= 2; o <<= 1) {  // commutative pairs: every lane of the row gets the same sums
+        sa += __shfl_xor(sa, o, 64);
+        ta += __shfl_xor(ta, o, 64);
+      }
+      if (q == 0 && rr < MT * 32 && rr < M) {
+        double* p = reinterpret_cast<double*>(out) + ((size_t)rr * n_slabs + slab) * 4;
+        p[0] = mx;
+        p[1] = (double)bidx;
+        p[2] = sa;
+        p[3] = ta;
+      }
     }
   } else if constexpr (EPI == 0) {
     const int ncol = nt * 32 + (lane & 31);
@@ -638,14 +642,18 @@ hipError_t launch_gemm_stream_stats(hipStream_t st, int max_rows, int K, int N, 
                                     const uint16_t* Wp, const int32_t* n_sel, double* part, LaunchEvents ev) {
   if (max_rows <= 0) return hipSuccess;
   const int mt = stream_mt(max_rows);
-  if (mt < 1 || mt > 2 || mt > MTt || N % 128 != 0 || K % 256 != 0) return hipErrorInvalidValue;
+  if (mt < 1 || mt > MTt || N % 128 != 0 || K % 256 != 0) return hipErrorInvalidValue;
   const int n_slabs = N / 128;
   const int grid = (n_slabs + 7) / 8 * 8;
-  if (mt == 1)
-    return stream_cfg<1, 2>(st, grid, A, MTt, Wp, (float*)part, nullptr, 0, n_sel, 1, K, N, K, n_slabs, n_slabs,
-                            max_rows, ev);
-  return stream_cfg<2, 2>(st, grid, A, MTt, Wp, (float*)part, nullptr, 0, n_sel, 1, K, N, K, n_slabs, n_slabs,
-                          max_rows, ev);
+#define GSS(MT_)                                                                                                 \
+  case MT_:                                                                                                      \
+    return stream_cfg<MT_, 2>(st, grid, A, MTt, Wp, (float*)part, nullptr, 0, n_sel, 1, K, N, K, n_slabs, n_slabs, \
+                              max_rows, ev);
+  switch (mt) {
+    GSS(1) GSS(2) GSS(3) GSS(4) GSS(5) GSS(6) GSS(7) GSS(8) GSS(9)
+    default: return hipErrorInvalidValue;
+  }
+#undef GSS
 }
 
 hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,

@@ -83,7 +83,7 @@ int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, in
 hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                               const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
                               int MTt_out, LaunchEvents ev = {});
-// The LM head on up to 64 rows without logits: per row and 128-column slab
+// The LM head on up to 288 rows without logits: per row and 128-column slab
 // (max, lowest argmax, S, T) into part [rows][N/128][4] (fp64); merge with
 // launch_lm_merge_wide.
 hipError_t launch_gemm_stream_stats(hipStream_t st, int max_rows, int K, int N, const uint16_t* A, int MTt,

@@ -1,11 +1,12 @@
 """LM-head row statistics (EntropyCache section 2: the O(V) decision) without
-a logits buffer: for up to 64 rows the weight-streaming GEMM reduces each
+a logits buffer: for up to 288 rows the weight-streaming GEMM reduces each
 128-column vocabulary slab to (max, lowest argmax, S, T) in its epilogue and
 one kernel merges the slabs in a fixed order.  Against the logits of the same
 GEMM (dllm_lm_head with logits requested) reduced on the host in fp64: the
 max and argmax equal bit for bit, S and T to 1e-12 relative; and against the
 oracle's statistics of the same hidden rows.  LLaDA-8B vocabulary (126464)
-and a small one."""
+and a small one; 32 to 288 rows (one to nine row tiles, 64 rows per pass of
+the epilogue)."""
 
 from __future__ import annotations
 
@@ -31,7 +32,11 @@ def _host_stats(z):
 
 
 @pytest.mark.parametrize("cfg", [medium_cfg(name="lm-medium", n_layers=1, batch=2),
-                                 configs.C2.with_(n_layers=1)], ids=lambda c: c.name)
+                                 medium_cfg(name="lm-medium-b3", n_layers=1, batch=3),
+                                 medium_cfg(name="lm-medium-b9", n_layers=1, batch=9),
+                                 configs.C2.with_(n_layers=1),
+                                 configs.C2.with_(name="lm-llada8b-b4", n_layers=1, batch=4)],
+                         ids=lambda c: c.name)
 def test_fused_lm_head_statistics(cfg):
     spec = spec_of(cfg)
     model, _, head = build(cfg)
