@@ -47,7 +47,7 @@ struct LayerW {
   float* ffn_norm = nullptr;
   void* w_qkv = nullptr;   // packed [d][nq + 2 nv]
   void* w_o = nullptr;     // packed [nq][d]
-  void* w_gu = nullptr;    // packed [d][2F], gate/up interleaved by 32 columns
+  void* w_gu = nullptr;    // packed [d][2F]: bf16 gate/up 16 + 16 columns per 32-column tile; fp32 by 32 columns
   void* w_down = nullptr;  // packed [F][d]
   float* w_proxy = nullptr;  // W_r, fp32 [d][proxy_rpad(r)] (zero columns past r)
   bool ready = false;
@@ -269,7 +269,17 @@ dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int 
   ProfLaunch prof(m, cls, (double)K * N * m->esize + (double)max_rows * K * m->esize + (double)max_rows * n_out * m->esize,
                   2.0 * max_rows * (double)K * N);
   if (m->bf16) {
-    // up to 288 rows: the weight-streaming kernel, when the shape suits it
+    // up to 288 rows: the weight-streaming kernel, when the shape suits it, on
+    // 96-column slabs where those fill more of the chip
+    int s3 = gemm_stream3_pick_splits(max_rows, K, N, m->n_cu, act != nullptr, MTt);
+    if (s3 > 0 && !act && (size_t)s3 * max_rows * N > out_floats) s3 = 0;
+    if (s3 > 0) {
+      HIPCHK(launch_gemm_stream3(st, max_rows, B, K, N, (const uint16_t*)A, MTt, (const uint16_t*)W, n_sel, out, s3,
+                                 (uint16_t*)act, m->MTt, prof.ev));
+      *splits = s3;
+      prof.done();
+      return DLLM_OK;
+    }
     int ss = gemm_stream_pick_splits(max_rows, K, N, m->n_cu, act != nullptr, MTt);
     if (ss > 0 && !act && (size_t)ss * max_rows * N > out_floats) ss = 0;
     if (ss > 0) {
@@ -295,9 +305,9 @@ dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int 
 }
 
 dllm_status pack(dllm_model* m, hipStream_t st, int K, int Nsrc, const void* src, void* dst, int Ndst, int col0,
-                 int tile_stride) {
+                 int tile_stride, int gw = 32) {
   if (m->bf16)
-    HIPCHK(launch_pack_bf16(st, K, Nsrc, (const uint16_t*)src, Nsrc, (uint16_t*)dst, col0, tile_stride));
+    HIPCHK(launch_pack_bf16(st, K, Nsrc, (const uint16_t*)src, Nsrc, (uint16_t*)dst, col0, tile_stride, gw));
   else
     HIPCHK(launch_pack_f32(st, K, Nsrc, (const float*)src, Nsrc, (float*)dst, Ndst, col0, tile_stride));
   return DLLM_OK;
@@ -809,8 +819,16 @@ dllm_status dllm_init_layer(dllm_model* m, int32_t layer, const dllm_layer_weigh
   CHK(pack(m, st, D, nv, w->w_k, L.w_qkv, nqkv, nq, 32));
   CHK(pack(m, st, D, nv, w->w_v, L.w_qkv, nqkv, nq + nv, 32));
   CHK(pack(m, st, nq, D, w->w_o, L.w_o, D, 0, 32));
-  CHK(pack(m, st, D, F, w->w_gate, L.w_gu, 2 * F, 0, 64));
-  CHK(pack(m, st, D, F, w->w_up, L.w_gu, 2 * F, 32, 64));
+  if (m->bf16) {
+    // gate and up columns 16 at a time inside each 32-column tile (gate in the
+    // tile's first 16 columns, up in its last 16), so that every tile holds
+    // complete SwiGLU pairs
+    CHK(pack(m, st, D, F, w->w_gate, L.w_gu, 2 * F, 0, 32, 16));
+    CHK(pack(m, st, D, F, w->w_up, L.w_gu, 2 * F, 16, 32, 16));
+  } else {
+    CHK(pack(m, st, D, F, w->w_gate, L.w_gu, 2 * F, 0, 64));
+    CHK(pack(m, st, D, F, w->w_up, L.w_gu, 2 * F, 32, 64));
+  }
   CHK(pack(m, st, F, D, w->w_down, L.w_down, D, 0, 32));
   if (w->w_proxy) {
     HIPCHK(launch_pad_proxy(st, D, r, w->w_proxy, L.w_proxy));

@@ -18,6 +18,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 namespace dllm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -27,21 +29,23 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // Packing.  Fragment (nt, kt) of W [K][N] holds, for lane l and j < 8,
 // W[kt*16 + 8*(l/32) + j][nt*32 + l%32]; fragments are stored nt-major.
-// Source column tile t (32 columns) of a Nsrc-wide source goes to packed
-// column col0 + t*tile_stride.
+// Source column group t (gw = 32 or 16 columns) of a Nsrc-wide source goes to
+// packed columns col0 + t*tile_stride .. + gw - 1 (inside one 32-column tile).
 // ---------------------------------------------------------------------------
 __global__ void pack_bf16_kernel(int K, int Nsrc, const uint16_t* __restrict__ src, int ld_src,
-                                 uint16_t* __restrict__ dst, int col0, int tile_stride) {
+                                 uint16_t* __restrict__ dst, int col0, int tile_stride, int gw) {
   const int KT = K >> 4;
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // (t, kt, lane)
-  const size_t total = (size_t)(Nsrc >> 5) * KT * 64;
+  const size_t total = (size_t)(Nsrc / gw) * KT * 64;
   if (gid >= total) return;
   const int lane = (int)(gid & 63);
+  const int c = lane & 31;
+  if (c >= gw) return;
   const size_t f = gid >> 6;
   const int kt = (int)(f % KT);
   const int t = (int)(f / KT);
-  const int scol = t * 32 + (lane & 31);
-  const int dcol = col0 + t * tile_stride + (lane & 31);
+  const int scol = t * gw + c;
+  const int dcol = col0 + t * tile_stride + c;
   const int nt = dcol >> 5;
   uint16_t v[8];
 #pragma unroll
@@ -51,14 +55,15 @@ __global__ void pack_bf16_kernel(int K, int Nsrc, const uint16_t* __restrict__ s
   w.y = v[2] | ((uint32_t)v[3] << 16);
   w.z = v[4] | ((uint32_t)v[5] << 16);
   w.w = v[6] | ((uint32_t)v[7] << 16);
-  reinterpret_cast<uint4*>(dst)[((size_t)nt * KT + kt) * 64 + lane] = w;
+  reinterpret_cast<uint4*>(dst)[((size_t)nt * KT + kt) * 64 + (dcol & 31) + 32 * (lane >> 5)] = w;
 }
 
 hipError_t launch_pack_bf16(hipStream_t st, int K, int Nsrc, const uint16_t* src, int ld_src, uint16_t* dst,
-                            int col0, int tile_stride) {
-  const size_t total = (size_t)(Nsrc >> 5) * (K >> 4) * 64;
+                            int col0, int tile_stride, int gw) {
+  if ((gw != 32 && gw != 16) || Nsrc % gw != 0 || (col0 & 31) + gw > 32) return hipErrorInvalidValue;
+  const size_t total = (size_t)(Nsrc / gw) * (K >> 4) * 64;
   hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, K, Nsrc, src,
-                     ld_src, dst, col0, tile_stride);
+                     ld_src, dst, col0, tile_stride, gw);
   return hipGetLastError();
 }
 
@@ -91,8 +96,8 @@ hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, in
 // double-buffered LDS stage.  Both operands are prefetched two chunks ahead in
 // registers, so the HBM weight stream overlaps the MFMAs of earlier chunks.
 // EPI 0 writes fp32 split-K partials out[split][m][n] ([S][cap][N]); EPI 1 (one split)
-// applies SwiGLU to interleaved gate/up column tiles and writes the packed bf16
-// activation of the next GEMM.
+// applies SwiGLU to the gate/up pairs inside each 32-column tile (16 gate then
+// 16 up columns) and writes the packed bf16 activation of the next GEMM.
 // ---------------------------------------------------------------------------
 template <int MTW, int KS, int EPI>
 __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel(const u32x4* __restrict__ Ap, int MTt,
@@ -219,21 +224,21 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
       }
     }
   } else {
+    // each 32-column tile holds 16 gate columns (lanes l % 32 < 16) and the
+    // matching 16 up columns (lane l + 16): intermediate column 16 T + l % 16
 #pragma unroll
     for (int j = 0; j < MTW; ++j) {
       if (!tv[j]) continue;
       const int mrow = (mt_base + wv + 4 * j) * 32 + (lane >> 5) * 4;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        if (nt0 + 2 * p + 1 >= NT) continue;
-        const int f = (slab * 2 + p) * 32 + (lane & 31);
+      for (int nt = 0; nt < 4; ++nt) {
+        if (nt0 + nt >= NT) continue;
+        const int f = (nt0 + nt) * 16 + (lane & 15);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int m = mrow + (i >> 2) * 8 + (i & 3);
-          if (m < M) {
-            const float g = acc[j][2 * p][i], u = acc[j][2 * p + 1][i];
-            act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
-          }
+          const float g = acc[j][nt][i], u = __shfl_xor(acc[j][nt][i], 16, 64);
+          if (!(lane & 16) && m < M) act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
         }
       }
     }
@@ -332,8 +337,13 @@ hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, c
 // ---------------------------------------------------------------------------
 // Weight-streaming bf16 GEMM for up to 288 rows (9 row tiles).
 //
-// Workgroup = 4 waves and a 128-column slab; wave w owns column tile w of the
-// slab and every row tile.  Each wave streams its own weight tile straight
+// Workgroup = 4 waves and a 128-column slab (COLS = 4); wave w owns column
+// tile w of the slab and every row tile.  COLS = 3 (96-column slabs, for up to
+// three row tiles where N/128 slabs times the K splits leave CUs idle, e.g. a
+// 12288-column QKV at two splits or a 24576-column fused gate|up: 192
+// workgroups, against 256 with 96-column slabs): waves 0..2 own the three
+// column tiles and wave 3 only shares the activation DMA, its waits and the
+// barriers.  Each wave streams its own weight tile straight
 // from HBM into a register ring of 16 k16 steps (no LDS on the weight path).
 // The activation chunk (64 k, all row tiles) goes from global memory straight
 // into LDS by DMA (global_load_lds_dwordx4: no registers, no ds_write), into a
@@ -385,12 +395,13 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt untouched)
 #define GS_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
 
-template <int MT, int EPI>
+template <int MT, int EPI, int COLS>
 __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __restrict__ Ap, int MTt,
                                                        const u32x4* __restrict__ Wp, float* __restrict__ out,
                                                        uint16_t* __restrict__ act, int MTt_out,
                                                        const int32_t* __restrict__ n_sel, int B, int K, int N,
                                                        int kps, int n_slabs, int total, int cap) {
+  static_assert(COLS == 4 || (COLS == 3 && EPI != 2), "96-column slabs: partials or SwiGLU");
   using S = StreamShape<MT>;
   constexpr int NS = S::NS, P = S::P;
   extern __shared__ u32x4 lds[];  // activation ring: [NS][GS_KC][MT][64]
@@ -405,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NT = N >> 5, KT = K >> 4;
-  const int nt = min(slab * 4 + wv, NT - 1);
+  const int nt = min(slab * COLS + wv, NT - 1);
   const int kt0 = (split * kps) >> 4;
   constexpr int GS_NW = S::NW;
   constexpr int GS_D = GS_KC * GS_NW;  // weight ring depth (k16 steps)
@@ -439,163 +450,171 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
     for (int mt = 0; mt < MT; ++mt) dst[mt] = lds[slot * ABUF + (st * MT + mt) * 64 + lane];
   };
 
-  f32x16_t acc[MT];
+  // IDLE: wave 3 of a 96-column slab, which owns no column tile and only
+  // shares the activation DMA, its waits and the barriers
+  auto run = [&](auto idle_c) {
+    constexpr bool IDLE = decltype(idle_c)::value;
+    // VMEM operations after the request of chunk c+1 until the wait: on an
+    // idle wave only the requests of chunks c+2 .. c+P-1 ((P - 1) MT), less
+    // the same margin of two
+    constexpr int WAIT = IDLE ? (S::P - 1) * MT - 2 : S::WAIT;
+    static_assert(WAIT >= 0 && WAIT < 64, "vmcnt field");
+    f32x16_t acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
 
 #pragma unroll
-  for (int c = 0; c < P; ++c) request_a(c);
-  u32x4 wr[GS_D];  // slot j holds step s with s % GS_D == j
+    for (int c = 0; c < P; ++c) request_a(c);
+    u32x4 wr[GS_D];  // slot j holds step s with s % GS_D == j
+    if constexpr (!IDLE) {
 #pragma unroll
-  for (int j = 0; j < GS_D; ++j) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(j, nsteps - 1) * 64);
-  GS_WAIT_VM_LGKM0(0);
-  __builtin_amdgcn_s_barrier();
-  u32x4 af[2][MT];
-  read_af(0, 0, af[0]);
-  for (int sc = 0; sc < nsup; ++sc) {
-#pragma unroll
-    for (int cc = 0; cc < GS_NW; ++cc) {
-      const int c = sc * GS_NW + cc;
-#pragma unroll
-      for (int st = 0; st < GS_KC; ++st) {
-        const int j = cc * GS_KC + st;
-        const int s = c * GS_KC + st;
-        // the next step's activation fragments are read while this step multiplies
-        if (st + 1 < GS_KC) read_af(c, st + 1, af[(j + 1) & 1]);
-        else read_af(c + 1, 0, af[(j + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, wr[j]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[j & 1][mt]), b, acc[mt],
-                                                            0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        // slot (c+P) % NS held chunk c-1, which every wave finished reading
-        // before the barrier of chunk c-1
-        if (st == 0) request_a(c + P);
-        __builtin_amdgcn_sched_barrier(0);
-        // refill the slot only after its last use, so the new load can take
-        // the same registers (no copy of an in-flight load at the back edge)
-        wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(s + GS_D, nsteps - 1) * 64);
-        __builtin_amdgcn_sched_barrier(0);
-        if (st == GS_KC - 2) {
-          // this wave's requests for chunk c+1 have landed and its reads of
-          // chunk c are complete; after the barrier, for every wave
-          GS_WAIT_VM_LGKM0(S::WAIT);
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      for (int j = 0; j < GS_D; ++j) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(j, nsteps - 1) * 64);
     }
-  }
-  GS_WAIT_VM_LGKM0(0);  // no request may still be writing LDS
-
-  if constexpr (EPI == 2) {
-    // LM-head row statistics of this 128-column vocabulary slab (the logits
-    // are never written): per row the max logit, its lowest column, and in
-    // fp64 S = sum e^{z-max}, T = sum e^{z-max} (z-max), into
-    // out (as double) [row][slab][4]
-    __builtin_amdgcn_s_barrier();  // every wave is done with the ring
-    constexpr int ZLD = 129;       // padded row of the slab's logits in LDS
-    float* zs = reinterpret_cast<float*>(lds);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int mrow = mt * 32 + (lane >> 5) * 4;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) zs[(mrow + (i >> 2) * 8 + (i & 3)) * ZLD + wv * 32 + (lane & 31)] = acc[mt][i];
-    }
-    __syncthreads();
-    // four threads per row, 32 columns each, combined in a fixed order; 64
-    // rows per pass
-    const int q = tid & 3;
-    for (int r0 = 0; r0 < MT * 32; r0 += 64) {
-      const int rr = r0 + (tid >> 2);
-      const float* zr = zs + min(rr, MT * 32 - 1) * ZLD + q * 32;
-      float best = zr[0];
-      int bidx = 0;
-      for (int c = 1; c < 32; ++c)
-        if (zr[c] > best) {  // increasing column order keeps the lowest index
-          best = zr[c];
-          bidx = c;
-        }
-      bidx += slab * 128 + q * 32;
-#pragma unroll
-      for (int o = 1; o <= 2; o <<= 1) {
-        const float ov = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bidx, o, 64);
-        if (ov > best || (ov == best && oi < bidx)) {
-          best = ov;
-          bidx = oi;
-        }
-      }
-      const double mx = (double)best;
-      double sa = 0.0, ta = 0.0;
-      for (int c = 0; c < 32; ++c) {
-        const double dz = (double)zr[c] - mx;
-        const double e = exp(dz);
-        sa += e;
-        ta += e * dz;
-      }
-#pragma unroll
-      for (int o = 1; o <= 2; o <<= 1) {  // commutative pairs: every lane of the row gets the same sums
-        sa += __shfl_xor(sa, o, 64);
-        ta += __shfl_xor(ta, o, 64);
-      }
-      if (q == 0 && rr < MT * 32 && rr < M) {
-        double* p = reinterpret_cast<double*>(out) + ((size_t)rr * n_slabs + slab) * 4;
-        p[0] = mx;
-        p[1] = (double)bidx;
-        p[2] = sa;
-        p[3] = ta;
-      }
-    }
-  } else if constexpr (EPI == 0) {
-    const int ncol = nt * 32 + (lane & 31);
-    if (slab * 4 + wv < NT) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int mrow = mt * 32 + (lane >> 5) * 4;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = mrow + (i >> 2) * 8 + (i & 3);
-          if (m < M) out[((size_t)split * cap + m) * N + ncol] = acc[mt][i];
-        }
-      }
-    }
-  } else {
-    // gate tile 2p (wave 2p), up tile 2p+1 (wave 2p+1): exchange through LDS
+    GS_WAIT_VM_LGKM0(0);
     __builtin_amdgcn_s_barrier();
-    float* ex = reinterpret_cast<float*>(lds);  // [2][MT][16][64]
-    const int p = wv >> 1;
-    if (wv & 1) {
+    u32x4 af[2][MT];
+    if constexpr (!IDLE) read_af(0, 0, af[0]);
+    for (int sc = 0; sc < nsup; ++sc) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int cc = 0; cc < GS_NW; ++cc) {
+        const int c = sc * GS_NW + cc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ex[((p * MT + mt) * 16 + i) * 64 + lane] = acc[mt][i];
-    }
-    __syncthreads();
-    if (!(wv & 1) && slab * 4 + wv + 1 < NT) {
-      const int f = (slab * 2 + p) * 32 + (lane & 31);
+        for (int st = 0; st < GS_KC; ++st) {
+          const int j = cc * GS_KC + st;
+          const int s = c * GS_KC + st;
+          if constexpr (!IDLE) {
+            // the next step's activation fragments are read while this step multiplies
+            if (st + 1 < GS_KC) read_af(c, st + 1, af[(j + 1) & 1]);
+            else read_af(c + 1, 0, af[(j + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, wr[j]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int mrow = mt * 32 + (lane >> 5) * 4;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = mrow + (i >> 2) * 8 + (i & 3);
-          if (m < M) {
-            const float g = acc[mt][i], u = ex[((p * MT + mt) * 16 + i) * 64 + lane];
-            act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
+            for (int mt = 0; mt < MT; ++mt)
+              acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[j & 1][mt]), b,
+                                                                acc[mt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // slot (c+P) % NS held chunk c-1, which every wave finished reading
+          // before the barrier of chunk c-1
+          if (st == 0) request_a(c + P);
+          __builtin_amdgcn_sched_barrier(0);
+          // refill the slot only after its last use, so the new load can take
+          // the same registers (no copy of an in-flight load at the back edge)
+          if constexpr (!IDLE) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(s + GS_D, nsteps - 1) * 64);
+          __builtin_amdgcn_sched_barrier(0);
+          if (st == GS_KC - 2) {
+            // this wave's requests for chunk c+1 have landed and its reads of
+            // chunk c are complete; after the barrier, for every wave
+            GS_WAIT_VM_LGKM0(WAIT);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
     }
-  }
+    GS_WAIT_VM_LGKM0(0);  // no request may still be writing LDS
+
+    if constexpr (!IDLE) {
+      if constexpr (EPI == 2) {
+        // LM-head row statistics of this 128-column vocabulary slab (the logits
+        // are never written): per row the max logit, its lowest column, and in
+        // fp64 S = sum e^{z-max}, T = sum e^{z-max} (z-max), into
+        // out (as double) [row][slab][4]
+        __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+        constexpr int ZLD = 129;       // padded row of the slab's logits in LDS
+        float* zs = reinterpret_cast<float*>(lds);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int mrow = mt * 32 + (lane >> 5) * 4;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) zs[(mrow + (i >> 2) * 8 + (i & 3)) * ZLD + wv * 32 + (lane & 31)] = acc[mt][i];
+        }
+        __syncthreads();
+        // four threads per row, 32 columns each, combined in a fixed order; 64
+        // rows per pass
+        const int q = tid & 3;
+        for (int r0 = 0; r0 < MT * 32; r0 += 64) {
+          const int rr = r0 + (tid >> 2);
+          const float* zr = zs + min(rr, MT * 32 - 1) * ZLD + q * 32;
+          float best = zr[0];
+          int bidx = 0;
+          for (int c = 1; c < 32; ++c)
+            if (zr[c] > best) {  // increasing column order keeps the lowest index
+              best = zr[c];
+              bidx = c;
+            }
+          bidx += slab * 128 + q * 32;
+#pragma unroll
+          for (int o = 1; o <= 2; o <<= 1) {
+            const float ov = __shfl_xor(best, o, 64);
+            const int oi = __shfl_xor(bidx, o, 64);
+            if (ov > best || (ov == best && oi < bidx)) {
+              best = ov;
+              bidx = oi;
+            }
+          }
+          const double mx = (double)best;
+          double sa = 0.0, ta = 0.0;
+          for (int c = 0; c < 32; ++c) {
+            const double dz = (double)zr[c] - mx;
+            const double e = exp(dz);
+            sa += e;
+            ta += e * dz;
+          }
+#pragma unroll
+          for (int o = 1; o <= 2; o <<= 1) {  // commutative pairs: every lane of the row gets the same sums
+            sa += __shfl_xor(sa, o, 64);
+            ta += __shfl_xor(ta, o, 64);
+          }
+          if (q == 0 && rr < MT * 32 && rr < M) {
+            double* p = reinterpret_cast<double*>(out) + ((size_t)rr * n_slabs + slab) * 4;
+            p[0] = mx;
+            p[1] = (double)bidx;
+            p[2] = sa;
+            p[3] = ta;
+          }
+        }
+      } else if constexpr (EPI == 0) {
+        const int ncol = nt * 32 + (lane & 31);
+        if (slab * COLS + wv < NT) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int mrow = mt * 32 + (lane >> 5) * 4;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int m = mrow + (i >> 2) * 8 + (i & 3);
+              if (m < M) out[((size_t)split * cap + m) * N + ncol] = acc[mt][i];
+            }
+          }
+        }
+      } else {
+        // gate columns in lanes l % 32 < 16 of the tile, the matching up columns
+        // in lane l + 16: intermediate column 16 nt + l % 16
+        if (slab * COLS + wv < NT) {
+          const int f = nt * 16 + (lane & 15);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int mrow = mt * 32 + (lane >> 5) * 4;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int m = mrow + (i >> 2) * 8 + (i & 3);
+              const float g = acc[mt][i], u = __shfl_xor(acc[mt][i], 16, 64);
+              if (!(lane & 16) && m < M) act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
+            }
+          }
+        }
+      }
+    }
+  };
+  if (COLS == 3 && wv == 3) run(std::true_type{});
+  else run(std::false_type{});
 }
+
 #undef GS_WAIT_VM_LGKM0
 
-template <int MT, int EPI>
+template <int MT, int EPI, int COLS = 4>
 static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
                              uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
                              int n_slabs, int total, int cap, LaunchEvents ev) {
@@ -604,16 +623,16 @@ static hipError_t stream_cfg(hipStream_t st, int grid, const void* A, int MTt, c
   constexpr size_t zlds = (size_t)MT * 32 * 129 * 4;
   const size_t lds = (EPI == 2 && zlds > StreamShape<MT>::LDS) ? zlds : StreamShape<MT>::LDS;
   hipError_t ea = once_per_device(attr_set, [&] {
-    return hipFuncSetAttribute((const void*)gemm_stream_kernel<MT, EPI>,
+    return hipFuncSetAttribute((const void*)gemm_stream_kernel<MT, EPI, COLS>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   });
   if (ea != hipSuccess) return ea;
   if (ev.start)
-    hipExtLaunchKernelGGL((gemm_stream_kernel<MT, EPI>), dim3(grid), dim3(256), lds, st, ev.start, ev.stop, 0,
+    hipExtLaunchKernelGGL((gemm_stream_kernel<MT, EPI, COLS>), dim3(grid), dim3(256), lds, st, ev.start, ev.stop, 0,
                           (const u32x4*)A, MTt, (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs,
                           total, cap);
   else
-    hipLaunchKernelGGL((gemm_stream_kernel<MT, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
+    hipLaunchKernelGGL((gemm_stream_kernel<MT, EPI, COLS>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
                        (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, cap);
   return hipGetLastError();
 }
@@ -636,6 +655,56 @@ int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, in
   for (int s = 2; s <= 32 && s <= K / 256; ++s)
     if ((K / 256) % s == 0 && n_slabs * s <= n_cu) best = s;
   return best;
+}
+
+// Fraction of the CUs a launch of `wgs` one-per-CU workgroups keeps busy,
+// over its rounds.
+static double cu_fill(int wgs, int n_cu) {
+  const int rounds = (wgs + n_cu - 1) / n_cu;
+  return rounds > 0 ? (double)wgs / ((double)rounds * n_cu) : 0.0;
+}
+
+int gemm_stream3_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, int MTt) {
+  const int mt = stream_mt(max_rows);
+  // up to three row tiles (wave 3 then only shares the activation DMA, and
+  // every weight fragment is loaded once): measured faster where the weight
+  // stream bounds the GEMM; with rows of its own wave 3 re-reads the three
+  // weight tiles and the layout loses from four row tiles on
+  if (mt < 0 || mt > 3 || mt > MTt || N % 96 != 0 || K % 256 != 0) return 0;
+  const int n3 = N / 96;
+  int s3 = 1;
+  if (!fused)
+    for (int s = 2; s <= 32 && s <= K / 256; ++s)
+      if ((K / 256) % s == 0 && n3 * s <= n_cu) s3 = s;
+  // only where the 96-column slabs fill more of the chip than the 128-column ones
+  const int s4 = gemm_stream_pick_splits(max_rows, K, N, n_cu, fused, MTt);
+  const double f4 = s4 > 0 ? cu_fill((N / 128) * s4, n_cu) : 0.0;
+  return cu_fill(n3 * s3, n_cu) > f4 + 1e-9 ? s3 : 0;
+}
+
+hipError_t launch_gemm_stream3(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
+                               const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
+                               int MTt_out, LaunchEvents ev) {
+  if (max_rows <= 0) return hipSuccess;
+  const int mt = stream_mt(max_rows);
+  if (mt < 0 || mt > MTt || N % 96 != 0 || splits < 1) return hipErrorInvalidValue;
+  const int n_slabs = N / 96;
+  const int kps = K / splits;
+  if (kps * splits != K || kps % (16 * GS_KC * 4) != 0) return hipErrorInvalidValue;
+  if (act != nullptr && splits != 1) return hipErrorInvalidValue;
+  const int total = n_slabs * splits;
+  const int grid = (total + 7) / 8 * 8;
+#define GS3(MT_)                                                                                                  \
+  case MT_:                                                                                                       \
+    return act ? stream_cfg<MT_, 1, 3>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, \
+                                     max_rows, ev)                                                                \
+               : stream_cfg<MT_, 0, 3>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, \
+                                     max_rows, ev);
+  switch (mt) {
+    GS3(1) GS3(2) GS3(3)
+    default: return hipErrorInvalidValue;
+  }
+#undef GS3
 }
 
 hipError_t launch_gemm_stream_stats(hipStream_t st, int max_rows, int K, int N, const uint16_t* A, int MTt,

@@ -34,7 +34,7 @@ hipError_t launch_qkv_epilogue(hipStream_t st, bool bf16, int max_rows, int B, i
 hipError_t launch_o_epilogue(hipStream_t st, bool bf16, int max_rows, int B, int L, int d, int S,
                              float eps, int MTt, const int32_t* idx, const int32_t* n, const float* part,
                              const void* H, const float* g2, float* hprime, void* A2);
-// act = SiLU(gate) * up from gate|up partials interleaved by 32 columns.
+// act = SiLU(gate) * up from fp32 gate|up partials interleaved by 32 columns.
 hipError_t launch_swiglu(hipStream_t st, bool bf16, int max_rows, int B, int F, int S, const int32_t* n,
                          const float* part, void* act);
 // H_out[row] = h' + sum_s part; proxy_ref[row] = proxy_cur[row]; score[row] = 0.
@@ -71,8 +71,9 @@ hipError_t launch_gemm_f32(hipStream_t st, int max_rows, int B, int K, int N, co
                            const float* W, const int32_t* n_sel, float* out, LaunchEvents ev = {});
 // bf16 weights pre-packed by launch_pack_bf16; `splits` from gemm_bf16_pick_splits.
 // A is packed (apack_off) with MTt row tiles.  act != NULL (one split, N a
-// multiple of 64, gate/up interleaved by 32 columns) writes SwiGLU(gate, up)
-// as a packed bf16 [M][N/2] activation with MTt_out row tiles instead of out.
+// multiple of 64, each 32-column tile holding 16 gate then the matching 16 up
+// columns) writes SwiGLU(gate, up) as a packed bf16 [M][N/2] activation with
+// MTt_out row tiles instead of out.
 hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                             const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
                             int MTt_out, LaunchEvents ev = {});
@@ -83,6 +84,14 @@ int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, in
 hipError_t launch_gemm_stream(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                               const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
                               int MTt_out, LaunchEvents ev = {});
+// The same on 96-column slabs (three column tiles per workgroup, the fourth
+// wave sharing only the activation DMA), for up to three row tiles and where
+// they fill more of the chip (N a multiple of 96): the split count, or 0 to
+// use launch_gemm_stream.
+int gemm_stream3_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, int MTt);
+hipError_t launch_gemm_stream3(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
+                               const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
+                               int MTt_out, LaunchEvents ev = {});
 // The LM head on up to 288 rows without logits: per row and 128-column slab
 // (max, lowest argmax, S, T) into part [rows][N/128][4] (fp64); merge with
 // launch_lm_merge_wide.
@@ -92,10 +101,10 @@ hipError_t launch_gemm_stream_stats(hipStream_t st, int max_rows, int K, int N, 
 // for packed activations the buffer's row-tile count.
 size_t gemm_pad_elems(int rows_tiles);
 // Pack source columns [0, Nsrc) of a row-major [K][ld_src] weight: source
-// column tile t (32 columns) lands at packed column col0 + t*tile_stride.
-// bf16: MFMA B-fragment tiles; fp32: row-major [K][Ndst].
+// column group t (gw columns: 32, or 16 for bf16) lands at packed column
+// col0 + t*tile_stride.  bf16: MFMA B-fragment tiles; fp32: row-major [K][Ndst].
 hipError_t launch_pack_bf16(hipStream_t st, int K, int Nsrc, const uint16_t* src, int ld_src, uint16_t* dst,
-                            int col0, int tile_stride);
+                            int col0, int tile_stride, int gw = 32);
 hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, int ld_src, float* dst, int Ndst,
                            int col0, int tile_stride);
 

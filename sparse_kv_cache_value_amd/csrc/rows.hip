@@ -431,8 +431,9 @@ hipError_t launch_o_epilogue(hipStream_t st, bool bf16m, int max_rows, int B, in
 }
 
 // ---------------------------------------------------------------------------
-// SwiGLU: act = SiLU(gate) * up.  The fused gate|up weight interleaves the
-// two by 32-column tiles: packed tile 2t is gate tile t, tile 2t+1 is up tile t.
+// SwiGLU (fp32 models): act = SiLU(gate) * up.  The fused fp32 gate|up weight
+// interleaves the two by 32-column tiles: packed tile 2t is gate tile t, tile
+// 2t+1 is up tile t.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu_kernel(int B, int F, int S, int cap, const int32_t* __restrict__ n,
