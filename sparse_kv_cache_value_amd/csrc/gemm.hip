@@ -18,8 +18,6 @@
 
 #include <hip/hip_ext.h>
 
-#include <type_traits>
-
 namespace dllm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -395,12 +393,13 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt untouched)
 #define GS_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
 
-template <int MT, int EPI, int COLS>
-__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __restrict__ Ap, int MTt,
-                                                       const u32x4* __restrict__ Wp, float* __restrict__ out,
-                                                       uint16_t* __restrict__ act, int MTt_out,
-                                                       const int32_t* __restrict__ n_sel, int B, int K, int N,
-                                                       int kps, int n_slabs, int total, int cap) {
+// IDLE: wave 3 of a 96-column slab, which owns no column tile and only shares
+// the activation DMA, its waits and the barriers
+template <int MT, int EPI, int COLS, bool IDLE>
+__device__ __forceinline__ void gemm_stream_body(const u32x4* __restrict__ Ap, int MTt, const u32x4* __restrict__ Wp,
+                                                 float* __restrict__ out, uint16_t* __restrict__ act, int MTt_out,
+                                                 const int32_t* __restrict__ n_sel, int B, int K, int N, int kps,
+                                                 int n_slabs, int total, int cap) {
   static_assert(COLS == 4 || (COLS == 3 && EPI != 2), "96-column slabs: partials or SwiGLU");
   using S = StreamShape<MT>;
   constexpr int NS = S::NS, P = S::P;
@@ -450,166 +449,174 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __rest
     for (int mt = 0; mt < MT; ++mt) dst[mt] = lds[slot * ABUF + (st * MT + mt) * 64 + lane];
   };
 
-  // IDLE: wave 3 of a 96-column slab, which owns no column tile and only
-  // shares the activation DMA, its waits and the barriers
-  auto run = [&](auto idle_c) {
-    constexpr bool IDLE = decltype(idle_c)::value;
-    // VMEM operations after the request of chunk c+1 until the wait: on an
-    // idle wave only the requests of chunks c+2 .. c+P-1 ((P - 1) MT), less
-    // the same margin of two
-    constexpr int WAIT = IDLE ? (S::P - 1) * MT - 2 : S::WAIT;
-    static_assert(WAIT >= 0 && WAIT < 64, "vmcnt field");
-    f32x16_t acc[MT];
+  // VMEM operations after the request of chunk c+1 until the wait: on an
+  // idle wave only the requests of chunks c+2 .. c+P-1 ((P - 1) MT), less
+  // the same margin of two
+  constexpr int WAIT = IDLE ? (S::P - 1) * MT - 2 : S::WAIT;
+  static_assert(WAIT >= 0 && WAIT < 64, "vmcnt field");
+  f32x16_t acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
 
 #pragma unroll
-    for (int c = 0; c < P; ++c) request_a(c);
-    u32x4 wr[GS_D];  // slot j holds step s with s % GS_D == j
-    if constexpr (!IDLE) {
+  for (int c = 0; c < P; ++c) request_a(c);
+  u32x4 wr[GS_D];  // slot j holds step s with s % GS_D == j
+  if constexpr (!IDLE) {
 #pragma unroll
-      for (int j = 0; j < GS_D; ++j) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(j, nsteps - 1) * 64);
-    }
-    GS_WAIT_VM_LGKM0(0);
-    __builtin_amdgcn_s_barrier();
-    u32x4 af[2][MT];
-    if constexpr (!IDLE) read_af(0, 0, af[0]);
-    for (int sc = 0; sc < nsup; ++sc) {
+    for (int j = 0; j < GS_D; ++j) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(j, nsteps - 1) * 64);
+  }
+  GS_WAIT_VM_LGKM0(0);
+  __builtin_amdgcn_s_barrier();
+  u32x4 af[2][MT];
+  if constexpr (!IDLE) read_af(0, 0, af[0]);
+  for (int sc = 0; sc < nsup; ++sc) {
 #pragma unroll
-      for (int cc = 0; cc < GS_NW; ++cc) {
-        const int c = sc * GS_NW + cc;
+    for (int cc = 0; cc < GS_NW; ++cc) {
+      const int c = sc * GS_NW + cc;
 #pragma unroll
-        for (int st = 0; st < GS_KC; ++st) {
-          const int j = cc * GS_KC + st;
-          const int s = c * GS_KC + st;
-          if constexpr (!IDLE) {
-            // the next step's activation fragments are read while this step multiplies
-            if (st + 1 < GS_KC) read_af(c, st + 1, af[(j + 1) & 1]);
-            else read_af(c + 1, 0, af[(j + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, wr[j]);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[j & 1][mt]), b,
-                                                                acc[mt], 0, 0, 0);
-          }
+      for (int st = 0; st < GS_KC; ++st) {
+        const int j = cc * GS_KC + st;
+        const int s = c * GS_KC + st;
+        if constexpr (!IDLE) {
+          // the next step's activation fragments are read while this step multiplies
+          if (st + 1 < GS_KC) read_af(c, st + 1, af[(j + 1) & 1]);
+          else read_af(c + 1, 0, af[(j + 1) & 1]);
           __builtin_amdgcn_sched_barrier(0);
-          // slot (c+P) % NS held chunk c-1, which every wave finished reading
-          // before the barrier of chunk c-1
-          if (st == 0) request_a(c + P);
+          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, wr[j]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[j & 1][mt]), b,
+                                                              acc[mt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // slot (c+P) % NS held chunk c-1, which every wave finished reading
+        // before the barrier of chunk c-1
+        if (st == 0) request_a(c + P);
+        __builtin_amdgcn_sched_barrier(0);
+        // refill the slot only after its last use, so the new load can take
+        // the same registers (no copy of an in-flight load at the back edge)
+        if constexpr (!IDLE) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(s + GS_D, nsteps - 1) * 64);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st == GS_KC - 2) {
+          // this wave's requests for chunk c+1 have landed and its reads of
+          // chunk c are complete; after the barrier, for every wave
+          GS_WAIT_VM_LGKM0(WAIT);
+          __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
-          // refill the slot only after its last use, so the new load can take
-          // the same registers (no copy of an in-flight load at the back edge)
-          if constexpr (!IDLE) wr[j] = __builtin_nontemporal_load(wsrc + (size_t)min(s + GS_D, nsteps - 1) * 64);
-          __builtin_amdgcn_sched_barrier(0);
-          if (st == GS_KC - 2) {
-            // this wave's requests for chunk c+1 have landed and its reads of
-            // chunk c are complete; after the barrier, for every wave
-            GS_WAIT_VM_LGKM0(WAIT);
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-          }
         }
       }
     }
-    GS_WAIT_VM_LGKM0(0);  // no request may still be writing LDS
+  }
+  GS_WAIT_VM_LGKM0(0);  // no request may still be writing LDS
 
-    if constexpr (!IDLE) {
-      if constexpr (EPI == 2) {
-        // LM-head row statistics of this 128-column vocabulary slab (the logits
-        // are never written): per row the max logit, its lowest column, and in
-        // fp64 S = sum e^{z-max}, T = sum e^{z-max} (z-max), into
-        // out (as double) [row][slab][4]
-        __builtin_amdgcn_s_barrier();  // every wave is done with the ring
-        constexpr int ZLD = 129;       // padded row of the slab's logits in LDS
-        float* zs = reinterpret_cast<float*>(lds);
+  if constexpr (!IDLE) {
+    if constexpr (EPI == 2) {
+      // LM-head row statistics of this 128-column vocabulary slab (the logits
+      // are never written): per row the max logit, its lowest column, and in
+      // fp64 S = sum e^{z-max}, T = sum e^{z-max} (z-max), into
+      // out (as double) [row][slab][4]
+      __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+      constexpr int ZLD = 129;       // padded row of the slab's logits in LDS
+      float* zs = reinterpret_cast<float*>(lds);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int mrow = mt * 32 + (lane >> 5) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zs[(mrow + (i >> 2) * 8 + (i & 3)) * ZLD + wv * 32 + (lane & 31)] = acc[mt][i];
+      }
+      __syncthreads();
+      // four threads per row, 32 columns each, combined in a fixed order; 64
+      // rows per pass
+      const int q = tid & 3;
+      for (int r0 = 0; r0 < MT * 32; r0 += 64) {
+        const int rr = r0 + (tid >> 2);
+        const float* zr = zs + min(rr, MT * 32 - 1) * ZLD + q * 32;
+        float best = zr[0];
+        int bidx = 0;
+        for (int c = 1; c < 32; ++c)
+          if (zr[c] > best) {  // increasing column order keeps the lowest index
+            best = zr[c];
+            bidx = c;
+          }
+        bidx += slab * 128 + q * 32;
+#pragma unroll
+        for (int o = 1; o <= 2; o <<= 1) {
+          const float ov = __shfl_xor(best, o, 64);
+          const int oi = __shfl_xor(bidx, o, 64);
+          if (ov > best || (ov == best && oi < bidx)) {
+            best = ov;
+            bidx = oi;
+          }
+        }
+        const double mx = (double)best;
+        double sa = 0.0, ta = 0.0;
+        for (int c = 0; c < 32; ++c) {
+          const double dz = (double)zr[c] - mx;
+          const double e = exp(dz);
+          sa += e;
+          ta += e * dz;
+        }
+#pragma unroll
+        for (int o = 1; o <= 2; o <<= 1) {  // commutative pairs: every lane of the row gets the same sums
+          sa += __shfl_xor(sa, o, 64);
+          ta += __shfl_xor(ta, o, 64);
+        }
+        if (q == 0 && rr < MT * 32 && rr < M) {
+          double* p = reinterpret_cast<double*>(out) + ((size_t)rr * n_slabs + slab) * 4;
+          p[0] = mx;
+          p[1] = (double)bidx;
+          p[2] = sa;
+          p[3] = ta;
+        }
+      }
+    } else if constexpr (EPI == 0) {
+      const int ncol = nt * 32 + (lane & 31);
+      if (slab * COLS + wv < NT) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int mrow = mt * 32 + (lane >> 5) * 4;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) zs[(mrow + (i >> 2) * 8 + (i & 3)) * ZLD + wv * 32 + (lane & 31)] = acc[mt][i];
-        }
-        __syncthreads();
-        // four threads per row, 32 columns each, combined in a fixed order; 64
-        // rows per pass
-        const int q = tid & 3;
-        for (int r0 = 0; r0 < MT * 32; r0 += 64) {
-          const int rr = r0 + (tid >> 2);
-          const float* zr = zs + min(rr, MT * 32 - 1) * ZLD + q * 32;
-          float best = zr[0];
-          int bidx = 0;
-          for (int c = 1; c < 32; ++c)
-            if (zr[c] > best) {  // increasing column order keeps the lowest index
-              best = zr[c];
-              bidx = c;
-            }
-          bidx += slab * 128 + q * 32;
-#pragma unroll
-          for (int o = 1; o <= 2; o <<= 1) {
-            const float ov = __shfl_xor(best, o, 64);
-            const int oi = __shfl_xor(bidx, o, 64);
-            if (ov > best || (ov == best && oi < bidx)) {
-              best = ov;
-              bidx = oi;
-            }
-          }
-          const double mx = (double)best;
-          double sa = 0.0, ta = 0.0;
-          for (int c = 0; c < 32; ++c) {
-            const double dz = (double)zr[c] - mx;
-            const double e = exp(dz);
-            sa += e;
-            ta += e * dz;
-          }
-#pragma unroll
-          for (int o = 1; o <= 2; o <<= 1) {  // commutative pairs: every lane of the row gets the same sums
-            sa += __shfl_xor(sa, o, 64);
-            ta += __shfl_xor(ta, o, 64);
-          }
-          if (q == 0 && rr < MT * 32 && rr < M) {
-            double* p = reinterpret_cast<double*>(out) + ((size_t)rr * n_slabs + slab) * 4;
-            p[0] = mx;
-            p[1] = (double)bidx;
-            p[2] = sa;
-            p[3] = ta;
+          for (int i = 0; i < 16; ++i) {
+            const int m = mrow + (i >> 2) * 8 + (i & 3);
+            if (m < M) out[((size_t)split * cap + m) * N + ncol] = acc[mt][i];
           }
         }
-      } else if constexpr (EPI == 0) {
-        const int ncol = nt * 32 + (lane & 31);
-        if (slab * COLS + wv < NT) {
+      }
+    } else {
+      // gate columns in lanes l % 32 < 16 of the tile, the matching up columns
+      // in lane l + 16: intermediate column 16 nt + l % 16
+      if (slab * COLS + wv < NT) {
+        const int f = nt * 16 + (lane & 15);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int mrow = mt * 32 + (lane >> 5) * 4;
+        for (int mt = 0; mt < MT; ++mt) {
+          const int mrow = mt * 32 + (lane >> 5) * 4;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int m = mrow + (i >> 2) * 8 + (i & 3);
-              if (m < M) out[((size_t)split * cap + m) * N + ncol] = acc[mt][i];
-            }
-          }
-        }
-      } else {
-        // gate columns in lanes l % 32 < 16 of the tile, the matching up columns
-        // in lane l + 16: intermediate column 16 nt + l % 16
-        if (slab * COLS + wv < NT) {
-          const int f = nt * 16 + (lane & 15);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int mrow = mt * 32 + (lane >> 5) * 4;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int m = mrow + (i >> 2) * 8 + (i & 3);
-              const float g = acc[mt][i], u = __shfl_xor(acc[mt][i], 16, 64);
-              if (!(lane & 16) && m < M) act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
-            }
+          for (int i = 0; i < 16; ++i) {
+            const int m = mrow + (i >> 2) * 8 + (i & 3);
+            const float g = acc[mt][i], u = __shfl_xor(acc[mt][i], 16, 64);
+            if (!(lane & 16) && m < M) act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
           }
         }
       }
     }
-  };
-  if (COLS == 3 && wv == 3) run(std::true_type{});
-  else run(std::false_type{});
+  }
+}
+
+template <int MT, int EPI, int COLS>
+__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const u32x4* __restrict__ Ap, int MTt,
+                                                       const u32x4* __restrict__ Wp, float* __restrict__ out,
+                                                       uint16_t* __restrict__ act, int MTt_out,
+                                                       const int32_t* __restrict__ n_sel, int B, int K, int N,
+                                                       int kps, int n_slabs, int total, int cap) {
+  if constexpr (COLS == 3) {
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 3) {
+      gemm_stream_body<MT, EPI, COLS, true>(Ap, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, cap);
+      return;
+    }
+  }
+  gemm_stream_body<MT, EPI, COLS, false>(Ap, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, n_slabs, total, cap);
 }
 
 #undef GS_WAIT_VM_LGKM0
