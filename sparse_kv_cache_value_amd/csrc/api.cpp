@@ -331,7 +331,7 @@ dllm_status do_drift(dllm_model* m, int layer, dllm_state* s, const int32_t* row
 // refresh_proxy: P <- C and score <- 0 on I (the value-proxy path; the
 // Polestar drift path keeps no value proxy and leaves both untouched)
 dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* idx, const int32_t* n, int max_rows,
-                      hipStream_t st, bool refresh_proxy = true) {
+                      hipStream_t st, bool refresh_proxy = true, bool gathered = false) {
   const dllm_dims& d = m->d;
   const int B = s->batch, L = d.seq_len, D = d.d_model, F = d.d_ffn;
   const int nq = nq_of(d), nv = nv_of(d);
@@ -339,7 +339,7 @@ dllm_status do_sparse(dllm_model* m, int layer, dllm_state* s, const int32_t* id
   const void* Hin = hid(m, s, layer);
   int sp = 1;
   const double Mr = max_rows, es = m->esize, nqkv = nq + 2 * nv;
-  {
+  if (!gathered) {
     Prof prof(m, st, DLLM_PROF_ROWS, 2.0 * Mr * D * es + D * 4.0, 4.0 * Mr * D);
     HIPCHK(launch_gather_norm(st, m->bf16, max_rows, B, L, D, d.rms_eps, m->MTt, idx, n, Hin, w.attn_norm, m->A1));
     prof.done();
@@ -1122,13 +1122,22 @@ dllm_status dllm_step(dllm_model* m, dllm_state* s, const dllm_step_params* p, d
     const int k = kf > (double)L ? L : (int)kf;
     int32_t* idx = m->idx[l & 1];
     int32_t* n = m->nsel[l & 1];
-    {
+    const int rows = any_full ? B * L : B * std::min(L, std::max(k, fmax));
+    // one sequence and a small row bound: every gather workgroup selects for
+    // itself (no selection launch); otherwise the selection, then the gather
+    const bool fused = B == 1 && rows <= SG_MAX_ROWS;
+    if (fused) {
+      Prof prof(m, st, DLLM_PROF_SELECT, (double)L * 13.0 + 2.0 * rows * d.d_model * m->esize + d.d_model * 4.0,
+                4.0 * rows * (double)d.d_model);
+      HIPCHK(launch_select_gather(st, m->bf16, rows, L, d.d_model, d.rms_eps, m->MTt, k, score(m, s, l), m->forced,
+                                  m->step_full, hid(m, s, l), m->layers[l].attn_norm, idx, n, m->A1));
+      prof.done();
+    } else {
       Prof prof(m, st, DLLM_PROF_SELECT, (double)B * L * 13.0, 0.0);
       HIPCHK(launch_select(st, B, L, k, score(m, s, l), m->forced, m->step_full, idx, n));
       prof.done();
     }
-    const int rows = any_full ? B * L : B * std::min(L, std::max(k, fmax));
-    CHK(do_sparse(m, l, s, idx, n, rows, st));
+    CHK(do_sparse(m, l, s, idx, n, rows, st, true, fused));
     CHK(save_sets(m, s, p, l, idx, n, st));
     prev_idx = idx;
     prev_n = n;

@@ -170,6 +170,61 @@ __device__ __forceinline__ void store_a8(float* A, int m, int k8, int /*MTt*/, i
 __device__ __forceinline__ void store_a1(bf16* A, int m, int k, int MTt, int, float v) { A[apack_off(m, k, MTt)] = f2bf(v); }
 __device__ __forceinline__ void store_a1(float* A, int m, int k, int, int ld, float v) { A[(size_t)m * ld + k] = v; }
 
+// Row-wide (normalising) kernels: one workgroup of RT threads per row, each
+// thread holding up to RV groups of 8 consecutive values in registers.
+constexpr int RT = 512;  // threads of the row-wide (normalising) kernels
+constexpr int RV = 2;    // groups of 8 per thread: d <= RT * 8 * RV
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// RMSNorm (fp32 statistics) of the d values at x times the gain g, stored as
+// row m of a GEMM input (packed for bf16).  One workgroup of RT threads; red
+// holds RT / 64 floats of LDS.
+template <typename T>
+__device__ __forceinline__ void norm_row_store(const T* __restrict__ x, int d, float eps,
+                                               const float* __restrict__ g, T* __restrict__ A, int m, int MTt,
+                                               float* red) {
+  float v[RV][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < RV; ++r) {
+    const int c8 = (threadIdx.x + r * RT) * 8;
+    if (c8 < d) {
+      load8<T>(x + c8, v[r]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[r][e] * v[r][e];
+    }
+  }
+  ss = block_sum<RT / 64>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int r = 0; r < RV; ++r) {
+    const int c8 = (threadIdx.x + r * RT) * 8;
+    if (c8 < d) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = v[r][e] * inv * g[c8 + e];
+      store_a8(A, m, c8, MTt, d, o);
+    }
+  }
+}
+
 // The S split partials p[s * stride] of four consecutive columns, loaded
 // unconditionally (issued back to back), and their sum in split order.
 template <int S>

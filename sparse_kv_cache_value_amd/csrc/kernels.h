@@ -59,6 +59,13 @@ hipError_t launch_pad_proxy(hipStream_t st, int d, int r, const float* wr, float
 // ---- selection (select.hip) ----
 hipError_t launch_select(hipStream_t st, int B, int L, int k, const double* score, const uint8_t* forced,
                          const uint8_t* full, int32_t* idx, int32_t* n);
+// One sequence: the selection fused with the gather + RMSNorm of the selected
+// rows into compact A (as launch_gather_norm with B = 1); grid max_rows
+// workgroups, each running the selection itself, so max_rows is kept small.
+constexpr int SG_MAX_ROWS = 512;
+hipError_t launch_select_gather(hipStream_t st, bool bf16, int max_rows, int L, int d, float eps, int MTt, int k,
+                                const double* score, const uint8_t* forced, const uint8_t* full, const void* H,
+                                const float* g, int32_t* idx, int32_t* n, void* A);
 
 // ---- GEMMs (gemm.hip) ----
 // Optional event pair stamped by the GEMM launch itself (hipExtLaunchKernel:

@@ -110,32 +110,6 @@ hipError_t launch_embed(hipStream_t st, bool bf16m, int max_rows, int B, int L, 
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Gather + RMSNorm (fp32 statistics) of the selected rows into compact A.
-// One workgroup per row; each thread holds up to RV groups of 8 consecutive
-// values in registers between the statistics and the normalised store.
-// ---------------------------------------------------------------------------
-constexpr int RT = 512;  // threads of the row-wide (normalising) kernels
-constexpr int RV = 2;    // groups of 8 per thread: d <= RT * 8 * RV
-
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float* v);
-template <>
-__device__ __forceinline__ void load8<bf16>(const bf16* p, float* v) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[2 * e] = __uint_as_float(w[e] << 16);
-    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* v) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float4 v);
 template <>
@@ -164,6 +138,11 @@ __device__ __forceinline__ float4 sum_splits4(const float* __restrict__ p, size_
   return acc;
 }
 
+// ---------------------------------------------------------------------------
+// Gather + RMSNorm (fp32 statistics) of the selected rows into compact A.
+// One workgroup per row; each thread holds up to RV groups of 8 consecutive
+// values in registers between the statistics and the normalised store.
+// ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(RT) void gather_norm_kernel(int B, int L, int d, float eps, int MTt,
                                                           const int32_t* __restrict__ idx,
@@ -174,30 +153,7 @@ __global__ __launch_bounds__(RT) void gather_norm_kernel(int B, int L, int d, fl
   int b, i;
   const int m = blockIdx.x;
   if (!row_of(idx, n, B, L, m, b, i)) return;
-  const T* x = H + ((size_t)b * L + i) * d;
-  float v[RV][8];
-  float ss = 0.f;
-#pragma unroll
-  for (int r = 0; r < RV; ++r) {
-    const int c8 = (threadIdx.x + r * RT) * 8;
-    if (c8 < d) {
-      load8<T>(x + c8, v[r]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[r][e] * v[r][e];
-    }
-  }
-  ss = block_sum<RT / 64>(ss, red);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-#pragma unroll
-  for (int r = 0; r < RV; ++r) {
-    const int c8 = (threadIdx.x + r * RT) * 8;
-    if (c8 < d) {
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = v[r][e] * inv * g[c8 + e];
-      store_a8(A, m, c8, MTt, d, o);
-    }
-  }
+  norm_row_store<T>(H + ((size_t)b * L + i) * d, d, eps, g, A, m, MTt, red);
 }
 
 hipError_t launch_gather_norm(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, float eps, int MTt,

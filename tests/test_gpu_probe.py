@@ -41,7 +41,9 @@ def test_profile_classes_of_a_sparse_step():
     assert prof["select"]["launches"] == n
     assert prof["proxy"]["launches"] == n
     assert prof["attention"]["launches"] == n
-    # gather, QKV / O / down epilogues (+ SwiGLU on the fp32 path)
-    assert prof["rows"]["launches"] == (5 if cfg.dtype == configs.FP32 else 4) * n
+    # one sequence: the selection and the gather are one launch (select
+    # class); then the QKV / O / down epilogues (+ SwiGLU on the fp32 path)
+    assert cfg.batch == 1
+    assert prof["rows"]["launches"] == (4 if cfg.dtype == configs.FP32 else 3) * n
     assert prof["decide"]["launches"] >= 4
     assert all(v["ms"] >= 0.0 for v in prof.values())
