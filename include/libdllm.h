@@ -102,9 +102,8 @@ typedef struct {
   void *k_cache;        /* [N][B][n_kv_heads][L32/32][head_dim/16][64][8] post-RoPE keys in
                          * matrix-core fragment order, L32 = L rounded up to 32: key j,
                          * dimension t at [j/32][t/16][j%32 + 32*((t/8)%2)][t%8] */
-  void *v_cache;        /* [N][B][n_kv_heads][L32/16][head_dim/32][64][8] values in fragment
-                         * order: key j (o = j%16), dimension t at
-                         * [j/16][t/32][t%32 + 32*((o/4)%2)][o%4 + 4*(o/8)] */
+  void *v_cache;        /* [N][B][n_kv_heads][L32][head_dim] values, row-major: key j,
+                         * dimension t at [j][t] */
   double *proxy_cur;    /* [N][B][L][r]  current proxy C of each row's layer input */
   double *proxy_ref;    /* [N][B][L][r]  proxy P at the row's last refresh */
   double *score;        /* [N][B][L]     drift of C against P (0 for refreshed rows) */

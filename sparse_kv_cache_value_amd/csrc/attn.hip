@@ -3,20 +3,24 @@
 // updated KV cache; dLLM attention is non-causal, so there is no mask).
 // Query head h reads KV head floor(h * Hkv / Hq).
 //
-// Cache layouts: K and V are stored in matrix-core fragment order (see
-// kc_off/vc_off), so every fragment a wave needs is one contiguous 1 KB load
-// (16 bytes per lane), and the value fragment's key order matches the rows of
-// the score accumulator.
+// Cache layouts: K is stored in matrix-core fragment order (kc_off), so every
+// key fragment a wave needs is one contiguous 1 KB load (16 bytes per lane)
+// straight into registers.  V is stored row-major ([key][dh] per sequence and
+// KV head), so the QKV epilogue writes a refreshed key's values as whole
+// contiguous pieces; the attention moves each 32-key value tile into LDS by
+// DMA (1 KB per request, contiguous in memory) and builds the value operand
+// with transposed LDS reads (ds_read_b64_tr_b16).
 //
 // bf16, dh in {64, 128}, L % 32 == 0: MFMA flash attention.  A workgroup owns
 // 32 query rows of one sequence and one head; its 8 waves split the keys and
-// each keeps an online softmax (fp32) over 32-key tiles (the next tile's K and
-// V loads in flight during the current tile's arithmetic), computing
-// S^T = K Q^T (so a query's scores sit in one lane pair and the row max/sum need
-// one cross-lane exchange) and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16.
-// The eight partial results are merged in one LDS round, each wave combining
-// and storing an eighth of the output in a fixed wave order.  Otherwise a
-// reference kernel (one wave per query row and head).
+// each keeps an online softmax (fp32) over 32-key tiles, computing S^T = K Q^T
+// (so a query's scores sit in one lane pair and the row max/sum need one
+// cross-lane exchange) and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16.  The
+// next tile's key fragments are in flight during the current tile; its value
+// tile is requested as soon as the current one has been read.  The eight
+// partial results are merged in one LDS round (over the value buffers), each
+// wave combining and storing an eighth of the output in a fixed wave order.
+// Otherwise a reference kernel (one wave per query row and head).
 #include "common.h"
 #include "kernels.h"
 
@@ -26,6 +30,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __global__ __launch_bounds__(64) void attn_ref_kernel(int B, int L, int Hq, int Hkv, int dh, float scale,
@@ -65,12 +70,14 @@ __global__ __launch_bounds__(64) void attn_ref_kernel(int B, int L, int Hq, int 
   const float inv = 1.0f / sum;
   for (int t = lane; t < dh; t += 64) {
     float acc = 0.f;
-    for (int j = 0; j < L; ++j) acc = fmaf(ps[j], io<T>::ld(V + vc_off(j, t, dh)), acc);
+    for (int j = 0; j < L; ++j) acc = fmaf(ps[j], io<T>::ld(V + (size_t)j * dh + t), acc);
     store_a1(out, m, h * dh + t, MTt, Hq * dh, acc * inv);
   }
 }
 
 constexpr int ATT_NW = 8;
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 template <int DH>
 __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, int Hq, int Hkv, int ntq, float sl2e, int cap,
@@ -79,10 +86,18 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
                                                                 const bf16* __restrict__ Kc,
                                                                 const bf16* __restrict__ Vc,
                                                                 bf16* __restrict__ out, int MTt) {
-  constexpr int KS = DH / 16;  // k-steps of S^T
-  constexpr int DT = DH / 32;  // d-tiles of O^T
+  constexpr int KS = DH / 16;   // k-steps of S^T
+  constexpr int DT = DH / 32;   // d-tiles of O^T
+  constexpr int RB = DH * 2;    // bytes of one key's values
+  constexpr int VT = 32 * RB;   // bytes of a 32-key value tile
+  constexpr int NV = VT / 1024; // 1 KB DMA requests per value tile
+  constexpr int RPI = 1024 / RB;  // key rows per request
+  constexpr int CPR = DH / 8;     // 16-byte chunks per key row
+  constexpr int VBUF = 2 * ATT_NW * VT;              // two value tiles per wave
+  constexpr int OXB = ATT_NW * DT * 16 * 64 * 4;     // the merge's partial outputs
+  // the value tiles during the key loop, the merge's partial outputs after it
+  __shared__ __attribute__((aligned(16))) unsigned char smem[VBUF > OXB ? VBUF : OXB];
   __shared__ float ms[ATT_NW][32], ls[ATT_NW][32];
-  __shared__ float ox[ATT_NW][DT][16][64];  // element i of lane l at [i][l]: no bank conflicts
   // Workgroups are dealt round-robin to the 8 XCDs; remap so that the query
   // tiles of one head run on one XCD and share its K/V through that L2.
   const int G = gridDim.x;  // ntq * Hq rounded up to a multiple of 8
@@ -107,7 +122,8 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   if (r0 >= cap) return;
   const int nqv = min(min(32, nb - 32 * T), cap - r0);
   const int g = (h * Hkv) / Hq;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, hlf = lane >> 5, ln = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, hlf = lane >> 5,
+            ln = lane & 31;
 
   // Q^T fragments (B operand): lane holds q[r0 + ln][h*DH + ks*16 + 8*hlf + 0..7]
   u32x4 qf[KS];
@@ -130,29 +146,78 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   float m_run = -INFINITY, l_run = 0.f;
 
   // K fragment (A operand of S^T) of key tile kt and dims ks*16 ..: 1 KB at
-  // ((kt*KS + ks)*64 + lane)*8; V fragment (A operand of O^T) of 16-key block
-  // kb and dims dt*32 ..: 1 KB at ((kb*DT + dt)*64 + lane)*8.
-  struct KV {
-    u32x4 k[KS];
-    u32x4 v[2][DT];
-  };
-  auto load_kv = [&](int kt, KV& t) {
+  // ((kt*KS + ks)*64 + lane)*8, straight into registers.
+  auto load_k = [&](int kt, u32x4 (&k)[KS]) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(Kb) + (size_t)kt * KS * 64 + lane;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) t.k[ks] = kp[ks * 64];
-    const u32x4* vp = reinterpret_cast<const u32x4*>(Vb) + (size_t)kt * 2 * DT * 64 + lane;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) t.v[kk][dt] = vp[(kk * DT + dt) * 64];
+    for (int ks = 0; ks < KS; ++ks) k[ks] = kp[ks * 64];
   };
-  auto tile = [&](const KV& t, bool rescale) {
+  // Value tile kt (32 key rows of DH values, row-major in the cache) into
+  // this wave's LDS buffer by DMA (1 KB, RPI rows, per request).  Chunk c of
+  // key row r is stored in slot c ^ vswz(r), so that the transposed reads
+  // below touch every bank once per half-wave.  The requests are issued from
+  // inline asm (the compiler would otherwise make every LDS read wait for
+  // them); each tile starts with a wait for every load in flight, which were
+  // all issued one tile earlier, so the value tile read in a tile has landed.
+  auto vswz = [](int r) { return DH == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  lds_u8* vbuf = (lds_u8*)smem + wv * 2 * VT;
+  // lane byte offset inside a request; vswz(r) depends on r % 4 only, and
+  // every request starts at a multiple of 4 rows
+  const unsigned voff = (unsigned)((lane / CPR) * RB + 16 * ((lane % CPR) ^ vswz(lane / CPR)));
+  auto load_v = [&](int kt, int buf) {
+    const void* src = uniform_ptr(Vb + (size_t)kt * 32 * DH);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is only ever set here
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const unsigned l = (unsigned)(uintptr_t)(vbuf + buf * VT + i * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(l)),
+                   "v"(voff + i * 1024u), "s"(src)
+                   : "memory", "m0");
+    }
+#pragma clang diagnostic pop
+  };
+  // V^T fragment (A operand of O^T) of 16-key half kk and dims dt*32 ..:
+  // lane l needs value [key 16 kk + 4 (l/32) + e%4 + 8 (e/4)][dim dt*32 + l%32]
+  // for e = 0..7 (the key order of the score accumulator's rows).  Two
+  // transposed 64-bit LDS reads give e = 0..3 and e = 4..7: in each group of
+  // 16 lanes, lane j reads the 4 dims 4 (j%4) .. of key j/4, and lane i of
+  // the group receives dim i of those 4 keys.
+  const int jq = lane & 15, Gq = lane >> 4;
+  const int mf = DH == 128 ? (jq >> 2) : (jq >> 3);  // vswz of the lane's key, over 4
+  int vrd[DT];  // byte offset in a value tile for kk = 0 and keys +0..3
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    vrd[dt] = (4 * (Gq >> 1) + (jq >> 2)) * RB + (4 * (dt ^ mf) + 2 * (Gq & 1) + ((jq & 3) >> 1)) * 16 + 8 * (jq & 1);
+  auto read_v = [&](int buf, int kk, u32x4 (&vf)[DT]) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+      const lds_u8* a = vbuf + buf * VT + kk * 16 * RB + vrd[dt];
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a);
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 8 * RB));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      vf[dt] = u32x4{l2.x, l2.y, h2.x, h2.y};
+    }
+  };
+  // one key tile: S^T, online softmax, then the value tile's reads, the next
+  // value tile's request (into the other buffer, read two tiles ago), O^T
+  // kf holds this tile's key fragments; the next tile's (index kn) go into
+  // kn_f, its value tile (index vnext, none if negative) into the other buffer
+  auto tile = [&](const u32x4 (&kf)[KS], u32x4 (&kn_f)[KS], int kn, int buf, bool rescale, int vnext) {
+    // this tile's key fragments and value tile (both requested one tile ago)
+    // have landed; the other value buffer was read by the previous tile
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+    __builtin_amdgcn_sched_barrier(0);
+    if (vnext >= 0) load_v(vnext, buf ^ 1);
+    load_k(kn, kn_f);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16_t s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, t.k[ks]),
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
                                                   __builtin_bit_cast(bf16x8_t, qf[ks]), s, 0, 0, 0);
     float mt = s[0];
 #pragma unroll
@@ -160,12 +225,20 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2e;
     const float m_new = fmaxf(m_run, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[16], rs = 0.f;
+    // probabilities packed to bf16 as they are made (P^T operands of the two
+    // 16-key halves); the row sum in element order
+    u32x4 pf[2];
+    float rs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2e, -m_new));
-      rs += p[i];
-    }
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + 2 * e], sl2e, -m_new));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + 2 * e + 1], sl2e, -m_new));
+        rs += p0;
+        rs += p1;
+        pf[kk][e] = pack2bf(p0, p1);
+      }
     rs += __shfl_xor(rs, 32, 64);
     l_run = l_run * alpha + rs;
     m_run = m_new;
@@ -175,39 +248,46 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
+    // the value reads stay after the softmax: the wait for this tile's value
+    // request comes as late as possible
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      u32x4 pf;
-      pf.x = pack2bf(p[8 * kk + 0], p[8 * kk + 1]);
-      pf.y = pack2bf(p[8 * kk + 2], p[8 * kk + 3]);
-      pf.z = pack2bf(p[8 * kk + 4], p[8 * kk + 5]);
-      pf.w = pack2bf(p[8 * kk + 6], p[8 * kk + 7]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf);
+      u32x4 vf[DT];
+      read_v(buf, kk, vf);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf[kk]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, t.v[kk][dt]), pb, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[dt]), pb, o[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // one half's value fragments live at a time
     }
   };
 
-  // the next tile's loads are in flight while the current one is multiplied
-  // (the prefetch index is clamped, so every load is unconditional and in range)
+  // the next key tile's fragments and value tile are in flight during the
+  // current tile
   if (t_beg < t_end) {
-    KV ta, tb;
-    load_kv(t_beg, ta);
+    u32x4 ka[KS], kb[KS];
+    load_k(t_beg, ka);
+    load_v(t_beg, 0);
+    // (the key prefetch index is clamped, so every load is unconditional and
+    // in range; the value request is skipped past the last tile)
     for (int kt = t_beg; kt < t_end; kt += 2) {
-      load_kv(min(kt + 1, t_end - 1), tb);
-      tile(ta, kt != t_beg);
+      tile(ka, kb, min(kt + 1, t_end - 1), 0, kt != t_beg, kt + 1 < t_end ? kt + 1 : -1);
       if (kt + 1 >= t_end) break;
-      load_kv(min(kt + 2, t_end - 1), ta);
-      tile(tb, true);
+      tile(kb, ka, min(kt + 2, t_end - 1), 1, true, kt + 2 < t_end ? kt + 2 : -1);
     }
   }
 
   // merge the waves' partial softmax states in one LDS round: every wave
   // writes (m, l, O), then wave w combines the output groups (dt, q4) it owns
-  // from all eight waves in a fixed order and stores them
+  // from all eight waves in a fixed order and stores them.  The partial
+  // outputs reuse the value buffers: every wave's reads (and requests) are
+  // done first.
   static_assert((DT * 4) % ATT_NW == 0, "output groups per wave");
   constexpr int GPW = DT * 4 / ATT_NW;
+  float (*ox)[DT][16][64] = reinterpret_cast<float (*)[DT][16][64]>(smem);  // element i of lane l at [i][l]
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no request still writing LDS
+  __syncthreads();
   if (lane < 32) {
     ms[wv][ln] = m_run;
     ls[wv][ln] = l_run;
@@ -230,7 +310,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   const int m = r0 + ln;
 #pragma unroll
   for (int gg = 0; gg < GPW; ++gg) {
-    const int g = wv * GPW + gg, dt = g >> 2, q4 = g & 3;
+    const int gr = wv * GPW + gg, dt = gr >> 2, q4 = gr & 3;
     float mine[4], part[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

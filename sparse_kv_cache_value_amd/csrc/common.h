@@ -110,6 +110,15 @@ __device__ __forceinline__ double wave_max(double v) {
   return v;
 }
 
+// A wave-uniform pointer, made visibly uniform so that it can live in scalar
+// registers (LDS DMA requests take their base address from an SGPR pair).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Sum over a block of NW waves (fixed order, deterministic).  `red` holds NW
 // entries of LDS.  Every thread gets the total.
 template <int NW, typename F>
@@ -136,17 +145,12 @@ __device__ __forceinline__ size_t apack_off(int m, int k, int MTt) {
   return (((size_t)kt * MTt + mt) * 64 + lane) * 8 + (k & 7);
 }
 
-// Key/value cache offsets inside one (sequence, kv head) block of L32 * dh
-// elements (L32 = L rounded up to 32), in matrix-core fragment order: a wave
-// reads the fragment of 32 keys x 16 dims (K) or 16 keys x 32 dims (V) as one
-// contiguous 1 KB.  The key order inside a V fragment matches the row order of
-// the score tile's accumulator, so probabilities feed the next MFMA in place.
+// Key cache offset inside one (sequence, kv head) block of L32 * dh elements
+// (L32 = L rounded up to 32), in matrix-core fragment order: a wave reads the
+// fragment of 32 keys x 16 dims as one contiguous 1 KB.  The value cache is
+// row-major in the same block ([L32][dh]): element (j, t) at j * dh + t.
 __device__ __forceinline__ size_t kc_off(int j, int t, int dh) {
   return (((size_t)(j >> 5) * (dh >> 4) + (t >> 4)) * 64 + (j & 31) + 32 * ((t >> 3) & 1)) * 8 + (t & 7);
-}
-__device__ __forceinline__ size_t vc_off(int j, int t, int dh) {
-  const int o = j & 15;
-  return (((size_t)(j >> 4) * (dh >> 5) + (t >> 5)) * 64 + (t & 31) + 32 * ((o >> 2) & 1)) * 8 + (o & 3) + 4 * (o >> 3);
 }
 __device__ __forceinline__ int l32_of(int L) { return (L + 31) & ~31; }
 

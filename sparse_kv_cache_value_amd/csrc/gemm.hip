@@ -381,15 +381,6 @@ struct StreamShape {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// A wave-uniform pointer, made visibly uniform so that it can live in scalar
-// registers (the DMA below takes its base address from an SGPR pair).
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
 // s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt untouched)
 #define GS_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
 

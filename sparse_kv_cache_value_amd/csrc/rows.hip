@@ -249,11 +249,9 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(int B, int L, int Hq,
       if constexpr (S) v = add_splits4<S>(tv);
       else v = sum_splits4(p0 + nq + nv + c4, sstride, Srt);
       const int g = c4 / dh, t = c4 - g * dh;
+      // values are row-major: the quad is one contiguous piece of the key's row
       T* vb = Vc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * dh;
-      io<T>::st(vb + vc_off(i, t, dh), v.x);
-      io<T>::st(vb + vc_off(i, t + 1, dh), v.y);
-      io<T>::st(vb + vc_off(i, t + 2, dh), v.z);
-      io<T>::st(vb + vc_off(i, t + 3, dh), v.w);
+      store4<T>(vb + (size_t)i * dh + t, v);
     }
   }
 }

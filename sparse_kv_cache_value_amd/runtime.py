@@ -82,11 +82,11 @@ class State:
         N, L, d, r = cfg.n_layers, cfg.seq_len, cfg.d_model, cfg.proxy_rank
         dt = inputs.storage_dtype(cfg)
         self.hidden = torch.zeros((N + 1, Bn, L, d), dtype=dt, device=dev)
-        # keys and values in matrix-core fragment order (include/libdllm.h)
+        # keys in matrix-core fragment order, values row-major (include/libdllm.h)
         L32 = (L + 31) // 32 * 32
         dh = cfg.head_dim
         self.k_cache = torch.zeros((N, Bn, cfg.n_kv_heads, L32 // 32, dh // 16, 64, 8), dtype=dt, device=dev)
-        self.v_cache = torch.zeros((N, Bn, cfg.n_kv_heads, L32 // 16, dh // 32, 64, 8), dtype=dt, device=dev)
+        self.v_cache = torch.zeros((N, Bn, cfg.n_kv_heads, L32, dh), dtype=dt, device=dev)
         self.proxy_cur = torch.zeros((N, Bn, L, r), dtype=torch.float64, device=dev)
         self.proxy_ref = torch.zeros_like(self.proxy_cur)
         self.score = torch.zeros((N, Bn, L), dtype=torch.float64, device=dev)

@@ -40,12 +40,8 @@ def unpack_k(k):
 
 
 def unpack_v(v):
-    """[N][B][G][L32/16][dh/32][64][8] fragment order -> [N, B, L32, G, dh]."""
-    N_, B_, G_, KB, DT, _, _ = v.shape
-    v = v.reshape(N_, B_, G_, KB, DT, 2, 32, 2, 4)          # lane = dim%32 + 32*h, slot = jj + 4*jh
-    # key within the 16-block = 8*jh + 4*h + jj
-    v = v.permute(0, 1, 3, 7, 5, 8, 2, 4, 6)               # N B KB jh h jj G DT dl
-    return v.reshape(N_, B_, KB * 16, G_, DT * 32).numpy()
+    """[N][B][G][L32][dh] row-major values -> [N, B, L32, G, dh]."""
+    return v.permute(0, 1, 3, 2, 4).numpy()
 
 
 class Snap:
