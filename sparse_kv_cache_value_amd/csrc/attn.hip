@@ -332,6 +332,229 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-query attention (4 <= Hq/Hkv <= 8, bf16, dh in {64, 128}): a
+// workgroup owns 32 query rows of one sequence and every query head of one KV
+// head.  Wave w < Hq/Hkv owns query head g*(Hq/Hkv) + w over all the keys, so
+// the waves' results need no merge.  Each 32-key tile of keys (fragment order)
+// and values (row-major, chunks XOR-swizzled as above) is moved into LDS once
+// per workgroup by DMA, 1 KB requests spread over the 8 waves, in a ring of
+// GQ_NB slots, and read by all the group's waves: the L2 reads of a KV head's
+// cache shrink by the group size against one workgroup per query head.  Every
+// GQ_TPB tiles: a wait for this wave's requests of those tiles, a workgroup
+// barrier (every wave's requests visible, every wave done with the slots about
+// to be refilled), the requests of the tiles GQ_NB - GQ_TPB ahead; then each
+// tile's arithmetic as in attn_mfma_kernel.
+// ---------------------------------------------------------------------------
+constexpr int GQ_TPB = 1;           // key tiles per barrier (2 measured no faster)
+constexpr int GQ_NB = 4 * GQ_TPB;  // ring slots (key tiles)
+
+template <int DH>
+__global__ __launch_bounds__(ATT_NW * 64) void attn_gqa_kernel(int B, int L, int Hq, int Hkv, int ntq, float sl2e, int cap,
+                                                               const int32_t* __restrict__ n,
+                                                               const bf16* __restrict__ q,
+                                                               const bf16* __restrict__ Kc,
+                                                               const bf16* __restrict__ Vc,
+                                                               bf16* __restrict__ out, int MTt) {
+  constexpr int KS = DH / 16;     // k-steps of S^T (1 KB key fragments per tile)
+  constexpr int DT = DH / 32;     // d-tiles of O^T
+  constexpr int RB = DH * 2;      // bytes of one key's values
+  constexpr int KTB = 32 * RB;    // bytes of a key tile
+  constexpr int SLOT = 2 * KTB;   // key tile, then value tile
+  constexpr int NREQ = SLOT / 1024;
+  static_assert(NREQ % ATT_NW == 0, "requests per wave");
+  constexpr int RPW = NREQ / ATT_NW;  // 1 KB requests per wave per tile
+  constexpr int RPI = 1024 / RB;      // value rows per request
+  constexpr int CPR = DH / 8;         // 16-byte chunks per value row
+  constexpr int P = GQ_NB - GQ_TPB;   // tiles requested ahead
+  __shared__ __attribute__((aligned(16))) unsigned char smem[GQ_NB * SLOT];
+  const int G = gridDim.x;  // ntq * Hkv rounded up to a multiple of 8
+  // a KV head's query tiles side by side on one XCD (its K/V shared in L2)
+  const int wl = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int grp = wl / ntq;
+  if (grp >= Hkv) return;
+  // query tile -> (sequence, first compact row)
+  int T = wl - grp * ntq, b = -1, off = 0, nb = 0;
+  for (int bb = 0; bb < B; ++bb) {
+    const int c = min(max(n[bb], 0), L);
+    const int nt = (c + 31) >> 5;
+    if (T < nt) {
+      b = bb;
+      nb = c;
+      break;
+    }
+    T -= nt;
+    off += c;
+  }
+  if (b < 0) return;
+  const int r0 = off + 32 * T;
+  if (r0 >= cap) return;
+  const int nqv = min(min(32, nb - 32 * T), cap - r0);
+  const int GQ = Hq / Hkv;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, hlf = lane >> 5,
+            ln = lane & 31;
+  const bool comp = wv < GQ;  // waves past the group only move tiles
+  const int h = grp * GQ + (comp ? wv : 0);
+
+  // Q^T fragments (B operand): lane holds q[r0 + ln][h*DH + ks*16 + 8*hlf + 0..7]
+  u32x4 qf[KS];
+  const bool qv = ln < nqv;
+  const bf16* qrow = q + (size_t)(r0 + ln) * Hq * DH + (size_t)h * DH + 8 * hlf;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = (qv && comp) ? *reinterpret_cast<const u32x4*>(qrow + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const bf16* Kb = Kc + ((size_t)b * Hkv + grp) * (size_t)l32_of(L) * DH;
+  const bf16* Vb = Vc + ((size_t)b * Hkv + grp) * (size_t)l32_of(L) * DH;
+  const int ntiles = L >> 5;
+
+  // this wave's RPW requests of tile kt into ring slot `slot`: request r < KS
+  // copies key fragment r (1 KB, lane l at 16 l); the others copy value rows,
+  // chunk c of row r into slot c ^ vswz(r)
+  auto vswz = [](int r) { return DH == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  const unsigned voff = (unsigned)((lane / CPR) * RB + 16 * ((lane % CPR) ^ vswz(lane / CPR)));
+  auto request = [&](int kt, int slot) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is only ever set here
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = wv * RPW + j;  // wave-uniform
+      const unsigned l = (unsigned)(uintptr_t)((lds_u8*)smem + slot * SLOT + r * 1024);
+      const void* src;
+      unsigned vo;
+      if (r < KS) {
+        src = uniform_ptr(Kb + ((size_t)kt * KS + r) * 512);
+        vo = (unsigned)lane * 16u;
+      } else {
+        src = uniform_ptr(Vb + (size_t)kt * 32 * DH + (size_t)(r - KS) * 512);
+        vo = voff;
+      }
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(l)),
+                   "v"(vo), "s"(src)
+                   : "memory", "m0");
+    }
+#pragma clang diagnostic pop
+  };
+  // transposed value reads (see attn_mfma_kernel): lane byte offsets in a
+  // value tile for kk = 0 and keys +0..3
+  const int jq = lane & 15, Gq = lane >> 4;
+  const int mf = DH == 128 ? (jq >> 2) : (jq >> 3);
+  int vrd[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    vrd[dt] = (4 * (Gq >> 1) + (jq >> 2)) * RB + (4 * (dt ^ mf) + 2 * (Gq & 1) + ((jq & 3) >> 1)) * 16 + 8 * (jq & 1);
+
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // the query fragments have landed before any request goes out, so the only
+  // memory operations in flight in the key loop are this wave's requests
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+#pragma unroll
+  for (int t = 0; t < P; ++t) request(min(t, ntiles - 1), t);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    if (kt % GQ_TPB == 0) {
+      // this wave's requests of tiles kt .. kt + GQ_TPB - 1 have landed
+      // (those of the P - GQ_TPB newer tiles may not have); after the barrier
+      // every wave's have, and every wave is done with the GQ_TPB previous
+      // tiles, whose slots the next requests refill (past the last tile the
+      // requests repeat it, into slots nobody reads again)
+      constexpr int WAITN = (P - GQ_TPB) * RPW;
+      __builtin_amdgcn_s_waitcnt((WAITN & 15) | ((WAITN >> 4) << 14) | (7 << 4) | (15 << 8));
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < GQ_TPB; ++t) request(min(kt + P + t, ntiles - 1), (kt + P + t) % GQ_NB);
+    }
+    if (!comp) continue;
+    const lds_u8* sb = (lds_u8*)smem + (kt % GQ_NB) * SLOT;
+    u32x4 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(sb + ks * 1024 + lane * 16);
+    f32x16_t s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
+                                                  __builtin_bit_cast(bf16x8_t, qf[ks]), s, 0, 0, 0);
+    float mt = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2e;
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    u32x4 pf[2];
+    float rs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + 2 * e], sl2e, -m_new));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + 2 * e + 1], sl2e, -m_new));
+        rs += p0;
+        rs += p1;
+        pf[kk][e] = pack2bf(p0, p1);
+      }
+    rs += __shfl_xor(rs, 32, 64);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    if (kt > 0) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 vf[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+        const lds_u8* a = sb + KTB + kk * 16 * RB + vrd[dt];
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 8 * RB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        vf[dt] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf[kk]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[dt]), pb, o[dt], 0, 0, 0);
+    }
+  }
+  // no request may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+  if (!comp) return;
+  // O / l, this wave's head only: lanes pair up (shuffle across the halves)
+  // into 8 consecutive dimensions, as in attn_mfma_kernel's merge
+  const float inv = 1.0f / l_run;
+  const int m = r0 + ln;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float mine[4], part[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mine[e] = o[dt][q4 * 4 + e] * inv;
+        part[e] = __shfl_xor(mine[e], 32, 64);
+      }
+      if ((q4 & 1) == hlf && qv) {
+        float v8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v8[e] = hlf ? part[e] : mine[e];
+          v8[4 + e] = hlf ? mine[e] : part[e];
+        }
+        store_a8(out, m, h * DH + dt * 32 + q4 * 8, MTt, Hq * DH, v8);
+      }
+    }
+}
+
 hipError_t launch_attention(hipStream_t st, bool bf16m, int max_rows, int B, int L, int Hq, int Hkv, int dh,
                             const int32_t* idx, const int32_t* n, const void* q, const void* Kc, const void* Vc,
                             void* out, int MTt) {
@@ -340,6 +563,17 @@ hipError_t launch_attention(hipStream_t st, bool bf16m, int max_rows, int B, int
   if (bf16m && (dh == 128 || dh == 64) && L % 32 == 0) {
     const float sl2e = scale * 1.4426950408889634f;
     const int ntq = (max_rows + 31) / 32 + B;  // query tiles per head, an upper bound
+    if (Hq % Hkv == 0 && Hq / Hkv >= 4 && Hq / Hkv <= ATT_NW) {
+      // grouped-query heads: one workgroup per (query tile, KV head)
+      const int grid = (ntq * Hkv + 7) / 8 * 8;
+      if (dh == 128)
+        hipLaunchKernelGGL(attn_gqa_kernel<128>, dim3(grid), dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, ntq, sl2e,
+                           max_rows, n, (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt);
+      else
+        hipLaunchKernelGGL(attn_gqa_kernel<64>, dim3(grid), dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, ntq, sl2e,
+                           max_rows, n, (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt);
+      return hipGetLastError();
+    }
     const int grid = (ntq * Hq + 7) / 8 * 8;
     if (dh == 128)
       hipLaunchKernelGGL(attn_mfma_kernel<128>, dim3(grid), dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, ntq, sl2e,
