@@ -37,6 +37,13 @@ __device__ __forceinline__ uint32_t pack2bf(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
 }
 
+// SiLU for the bf16 paths: x / (1 + e^-x) from the hardware base-2
+// exponential and reciprocal (a few fp32 ulps, far inside the bf16 rounding
+// the result then takes).
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
 // float -> bfloat16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ bf16 f2bf(float f) { return (bf16)(pack2bf(f, 0.0f) & 0xffffu); }
 

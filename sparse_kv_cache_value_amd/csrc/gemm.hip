@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
   const int M = total_rows(n_sel, B, cap);
   const int mt_base = rb * 4 * MTW;
   if (mt_base * 32 >= M) return;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int NT = N >> 5;
   const int nt0 = slab * 4;
   const int KT = K >> 4;
@@ -174,6 +174,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < MTW; ++j) {
+        if (!tv[j]) continue;  // a row tile past the rows (wave-uniform): no MFMAs
         const bf16x8_t aa = __builtin_bit_cast(bf16x8_t, a[j][ks]);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
         for (int i = 0; i < 16; ++i) {
           const int m = mrow + (i >> 2) * 8 + (i & 3);
           const float g = acc[j][nt][i], u = __shfl_xor(acc[j][nt][i], 16, 64);
-          if (!(lane & 16) && m < M) act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
+          if (!(lane & 16) && m < M) act[apack_off(m, f, MTt_out)] = f2bf(silu_fast(g) * u);
         }
       }
     }
@@ -587,7 +588,7 @@ __device__ __forceinline__ void gemm_stream_body(const u32x4* __restrict__ Ap, i
           for (int i = 0; i < 16; ++i) {
             const int m = mrow + (i >> 2) * 8 + (i & 3);
             const float g = acc[mt][i], u = __shfl_xor(acc[mt][i], 16, 64);
-            if (!(lane & 16) && m < M) act[apack_off(m, f, MTt_out)] = f2bf(g / (1.0f + expf(-g)) * u);
+            if (!(lane & 16) && m < M) act[apack_off(m, f, MTt_out)] = f2bf(silu_fast(g) * u);
           }
         }
       }
