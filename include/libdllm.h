@@ -351,9 +351,7 @@ dllm_status dllm_commit_ce(dllm_model *m, dllm_state *s, const dllm_ce_params *c
  * saturating); centroid queries bf16(RMSNorm(c) * attn_norm) W_q with RoPE at
  * the seed row's position; per query head the fp64 log-softmax over the window
  * keys of k_cache[layer] (scale 1/sqrt(head_dim)), and the per-head KL against
- * log_attn, which it then replaces.  The codes are computed on a library-owned
- * second stream that forks from and joins `stream` within the call, so every
- * output is ordered on `stream` as usual. */
+ * log_attn, which it then replaces.  Everything runs on `stream`. */
 dllm_status dllm_polestar_drift(dllm_model *m, int32_t layer, const dllm_state *s, dllm_polestar_state *ps,
                                 const dllm_polestar_params *p, void *stream);
 
