@@ -164,9 +164,10 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) wl[buf * WBUF + (ks * 4 + wv) * 64 + lane] = src[ks];
   };
-  // all_valid (std::true_type when the wave's last row tile holds rows, hence
-  // every one does): no per-tile test in the loop
-  auto compute = [&](int buf, u32x4 (*a)[KS], auto all_valid) {
+  // nv: std::integral_constant<int, v> = the wave's first v row tiles hold
+  // rows and the rest none (no per-tile test in the loop), or -1: test each
+  // tile
+  auto compute = [&](int buf, u32x4 (*a)[KS], auto nv) {
     // all B fragments of the chunk first, so one LDS latency covers them all
     u32x4 b[KS][4];
 #pragma unroll
@@ -178,8 +179,10 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < MTW; ++j) {
-        if constexpr (!decltype(all_valid)::value) {
+        if constexpr (decltype(nv)::value < 0) {
           if (!tv[j]) continue;  // a row tile past the rows (wave-uniform): no MFMAs
+        } else if (j >= decltype(nv)::value) {
+          continue;
         }
         const bf16x8_t aa = __builtin_bit_cast(bf16x8_t, a[j][ks]);
 #pragma unroll
@@ -197,28 +200,39 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
   load_a(1, aB);
   load_w(2, wA);
   __syncthreads();
-  auto main_loop = [&](auto all_valid) {
+  auto main_loop = [&](auto nv) {
     for (int c = 0; c < nchunks; c += 2) {
       // A(c) in aA, W(c) in LDS 0, W(c+1) in wB, W(c+2) in wA
-      compute(0, aA, all_valid);
+      compute(0, aA, nv);
       store_w(wB, 1);
       load_a(c + 2, aA);
       load_w(c + 3, wB);
       __syncthreads();
       // A(c+1) in aB, W(c+1) in LDS 1, W(c+2) in wA
-      compute(1, aB, all_valid);
+      compute(1, aB, nv);
       store_w(wA, 0);
       load_a(c + 3, aB);
       load_w(c + 4, wA);
       __syncthreads();
     }
   };
-  // (384-row blocks only: at 256-row blocks the duplicated loop measured
-  // slower, 23.1 -> 23.6 ms per full-pass step, against 6 % faster GEMMs at 384)
-  if (MTW == 3 && tv[MTW - 1])
-    main_loop(std::true_type{});
-  else
-    main_loop(std::false_type{});
+  // 384-row blocks: one loop per count of row tiles that hold rows (the
+  // tiles are in row order, so they are the first ones).  256-row blocks keep
+  // one loop that tests each tile (a second copy measured slower there, 23.1
+  // -> 23.6 ms per full-pass step, against 6 % faster GEMMs at 384).
+  if constexpr (MTW == 3) {
+    const int nvalid = (int)tv[0] + (int)tv[1] + (int)tv[2];
+    if (nvalid == 3)
+      main_loop(std::integral_constant<int, 3>{});
+    else if (nvalid == 2)
+      main_loop(std::integral_constant<int, 2>{});
+    else if (nvalid == 1)
+      main_loop(std::integral_constant<int, 1>{});
+    else
+      main_loop(std::integral_constant<int, 0>{});
+  } else {
+    main_loop(std::integral_constant<int, -1>{});
+  }
 
   if constexpr (EPI == 0) {
 #pragma unroll
