@@ -76,11 +76,13 @@ __global__ __launch_bounds__(64) void attn_ref_kernel(int B, int L, int Hq, int 
 }
 
 constexpr int ATT_NW = 8;
+constexpr int ATT_ONE_ROUND = 256;  // (query tile, head) workgroups of 8 waves that fit one round (one per CU)
+constexpr int ATT_HALF_MAX_KEYS = 1024;  // longest cache the 4-wave variant takes
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-template <int DH>
-__global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, int Hq, int Hkv, int ntq, float sl2e, int cap,
+template <int DH, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_mfma_kernel(int B, int L, int Hq, int Hkv, int ntq, float sl2e, int cap,
                                                                 const int32_t* __restrict__ n,
                                                                 const bf16* __restrict__ q,
                                                                 const bf16* __restrict__ Kc,
@@ -93,11 +95,11 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   constexpr int NV = VT / 1024; // 1 KB DMA requests per value tile
   constexpr int RPI = 1024 / RB;  // key rows per request
   constexpr int CPR = DH / 8;     // 16-byte chunks per key row
-  constexpr int VBUF = 2 * ATT_NW * VT;              // two value tiles per wave
-  constexpr int OXB = ATT_NW * DT * 16 * 64 * 4;     // the merge's partial outputs
+  constexpr int VBUF = 2 * NW * VT;              // two value tiles per wave
+  constexpr int OXB = NW * DT * 16 * 64 * 4;     // the merge's partial outputs
   // the value tiles during the key loop, the merge's partial outputs after it
   __shared__ __attribute__((aligned(16))) unsigned char smem[VBUF > OXB ? VBUF : OXB];
-  __shared__ float ms[ATT_NW][32], ls[ATT_NW][32];
+  __shared__ float ms[NW][32], ls[NW][32];
   // Workgroups are dealt round-robin to the 8 XCDs; remap so that the query
   // tiles of one head run on one XCD and share its K/V through that L2.
   const int G = gridDim.x;  // ntq * Hq rounded up to a multiple of 8
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   const bf16* Kb = Kc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * DH;
   const bf16* Vb = Vc + ((size_t)b * Hkv + g) * (size_t)l32_of(L) * DH;
   const int ntiles = L >> 5;
-  const int t_beg = (wv * ntiles) / ATT_NW, t_end = ((wv + 1) * ntiles) / ATT_NW;
+  const int t_beg = (wv * ntiles) / NW, t_end = ((wv + 1) * ntiles) / NW;
 
   f32x16_t o[DT];
 #pragma unroll
@@ -280,11 +282,11 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
 
   // merge the waves' partial softmax states in one LDS round: every wave
   // writes (m, l, O), then wave w combines the output groups (dt, q4) it owns
-  // from all eight waves in a fixed order and stores them.  The partial
+  // from all NW waves in a fixed order and stores them.  The partial
   // outputs reuse the value buffers: every wave's reads (and requests) are
   // done first.
-  static_assert((DT * 4) % ATT_NW == 0, "output groups per wave");
-  constexpr int GPW = DT * 4 / ATT_NW;
+  static_assert((DT * 4) % NW == 0, "output groups per wave");
+  constexpr int GPW = DT * 4 / NW;
   float (*ox)[DT][16][64] = reinterpret_cast<float (*)[DT][16][64]>(smem);  // element i of lane l at [i][l]
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no request still writing LDS
   __syncthreads();
@@ -299,10 +301,10 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
   __syncthreads();
   float mg = ms[0][ln];
 #pragma unroll
-  for (int w2 = 1; w2 < ATT_NW; ++w2) mg = fmaxf(mg, ms[w2][ln]);
-  float fw[ATT_NW], lg = 0.f;
+  for (int w2 = 1; w2 < NW; ++w2) mg = fmaxf(mg, ms[w2][ln]);
+  float fw[NW], lg = 0.f;
 #pragma unroll
-  for (int w2 = 0; w2 < ATT_NW; ++w2) {
+  for (int w2 = 0; w2 < NW; ++w2) {
     fw[w2] = exp2f(ms[w2][ln] - mg);  // 0 for a wave without keys
     lg += ls[w2][ln] * fw[w2];
   }
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_mfma_kernel(int B, int L, in
     for (int e = 0; e < 4; ++e) {
       float acc = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < ATT_NW; ++w2) acc += ox[w2][dt][q4 * 4 + e][lane] * fw[w2];
+      for (int w2 = 0; w2 < NW; ++w2) acc += ox[w2][dt][q4 * 4 + e][lane] * fw[w2];
       mine[e] = acc * inv;
       part[e] = __shfl_xor(mine[e], 32, 64);
     }
@@ -575,12 +577,22 @@ hipError_t launch_attention(hipStream_t st, bool bf16m, int max_rows, int B, int
       return hipGetLastError();
     }
     const int grid = (ntq * Hq + 7) / 8 * 8;
-    if (dh == 128)
-      hipLaunchKernelGGL(attn_mfma_kernel<128>, dim3(grid), dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, ntq, sl2e,
-                         max_rows, n, (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt);
-    else
-      hipLaunchKernelGGL(attn_mfma_kernel<64>, dim3(grid), dim3(ATT_NW * 64), 0, st, B, L, Hq, Hkv, ntq, sl2e,
-                         max_rows, n, (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt);
+    // more (query tile, head) pairs than CUs and at most 1024 keys: 4 waves
+    // per workgroup (64 KB of LDS, two workgroups per CU, each wave twice the
+    // keys) instead of a second round of 8-wave ones.  Measured: C3's largest
+    // layers (L = 1024, 288 pairs) 0.529 -> 0.506 ms of attention per step;
+    // at L = 4096 (384 pairs) the doubled key chain per wave costs more than
+    // the second round (1.93 -> 2.69 ms), so longer caches keep 8 waves.
+    const bool half = ntq * Hq > ATT_ONE_ROUND && L <= ATT_HALF_MAX_KEYS;
+#define AM(D, W)                                                                                              \
+  hipLaunchKernelGGL((attn_mfma_kernel<D, W>), dim3(grid), dim3(W * 64), 0, st, B, L, Hq, Hkv, ntq, sl2e, max_rows, \
+                     n, (const bf16*)q, (const bf16*)Kc, (const bf16*)Vc, (bf16*)out, MTt)
+    if (dh == 128) {
+      if (half) AM(128, 4); else AM(128, 8);
+    } else {
+      if (half) AM(64, 4); else AM(64, 8);
+    }
+#undef AM
     return hipGetLastError();
   }
   const size_t lds = (size_t)(dh + L) * sizeof(float);
