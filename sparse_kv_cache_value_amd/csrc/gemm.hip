@@ -503,12 +503,17 @@ __device__ __forceinline__ void gemm_stream_body(const u32x4* __restrict__ Ap, i
           // the next step's activation fragments are read while this step multiplies
           if (st + 1 < GS_KC) read_af(c, st + 1, af[(j + 1) & 1]);
           else read_af(c + 1, 0, af[(j + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
           const bf16x8_t b = __builtin_bit_cast(bf16x8_t, wr[j]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[j & 1][mt]), b,
                                                               acc[mt], 0, 0, 0);
+          // one fragment read for the next step between consecutive MFMAs
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         // slot (c+P) % NS held chunk c-1, which every wave finished reading
