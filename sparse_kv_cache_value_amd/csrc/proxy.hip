@@ -93,13 +93,13 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(int B, int L, int d,
   const int tid = threadIdx.x, lane = tid & 63, i = lane & 15, q = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = rt * 16 + i;
-  long long off = -1;
-  {
-    int b, li;
-    if (m < M && row_of(idx, n, B, L, m, b, li)) off = (long long)((size_t)b * L + li) * d;
-  }
-  const bool valid = off >= 0;
-  const T* xrow = H + (valid ? off : 0) + 8 * q;  // rows past M read row 0 and are zeroed
+  // the row's sequence-0 list entry, loaded before anything else (see
+  // row_resolve); the row itself is resolved after the first chunk's gain
+  // and basis loads are issued
+  const int n0 = n[0];
+  const int i0 = idx[m < L ? m : L - 1];
+  bool valid = false;
+  const T* xrow = H + 8 * q;  // rows past M read row 0 and are zeroed
   // this wave's chunks of the workgroup's K range
   const int nch = kps / PX_KC;
   const int c_beg = blockIdx.y * nch + (wv * nch) / 4;
@@ -114,10 +114,13 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(int B, int L, int d,
     float4 g[2];
     float4 w[PX_NCT][2];
   };
-  auto fetch = [&](int kc, Raw& r) {
+  auto fetch_x = [&](int kc, Raw& r) {
     const int k0 = kc * PX_KC;
 #pragma unroll
     for (int h = 0; h < 8 / XV; ++h) r.x[h] = *reinterpret_cast<const typename XVec<T>::V*>(xrow + k0 + h * XV);
+  };
+  auto fetch_gw = [&](int kc, Raw& r) {
+    const int k0 = kc * PX_KC;
     r.g[0] = *reinterpret_cast<const float4*>(g1 + k0 + 8 * q);
     r.g[1] = *reinterpret_cast<const float4*>(g1 + k0 + 8 * q + 4);
 #pragma unroll
@@ -142,9 +145,21 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(int B, int L, int d,
       for (int t = 0; t < 8; ++t) acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[t], w[t], acc[c], 0, 0, 0);
     }
   };
+  auto fetch = [&](int kc, Raw& r) {
+    fetch_x(kc, r);
+    fetch_gw(kc, r);
+  };
+  Raw ra, rb;
+  if (c_beg < c_end) fetch_gw(c_beg, ra);
+  {
+    int b, li;
+    if (m < M && row_resolve(idx, n, B, L, m, n0, i0, b, li)) {
+      valid = true;
+      xrow = H + ((size_t)b * L + li) * d + 8 * q;
+    }
+  }
   if (c_beg < c_end) {
-    Raw ra, rb;
-    fetch(c_beg, ra);
+    fetch_x(c_beg, ra);
     for (int c = c_beg; c < c_end; c += 2) {
       fetch(min(c + 1, c_end - 1), rb);
       mma(ra);
@@ -188,19 +203,26 @@ __global__ __launch_bounds__(256) void proxy_finish_kernel(int B, int L, int r, 
   constexpr int PER = PX_SMAX / SG > 0 ? PX_SMAX / SG : 1;
   __shared__ double gs[SG][RPAD];
   __shared__ double red[2][4];
-  int b, i;
   const int m = blockIdx.x;
-  if (!row_of(idx, n, B, L, m, b, i)) return;
   const int M = total_rows(n, B, cap);
+  if (m >= M) return;
+  // the split partials (addressed by the compact row m alone) and the row's
+  // sequence-0 list entry are loaded before the row is resolved
+  const int n0 = n[0];
+  const int i0 = idx[m < L ? m : L - 1];
   const int tid = threadIdx.x, j = tid % RPAD, sg = tid / RPAD;
-  const size_t row = (size_t)b * L + i;
   const int per = (S + SG - 1) / SG, s0 = sg * per;
+  // unconditional loads (the split index clamped), so they are issued
+  // together; the sum below takes only the group's own splits
   double t[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    const int s = s0 + q;
-    t[q] = (q < per && s < S) ? partial[((size_t)s * M + m) * RPAD + j] : 0.0;
+    const int s = min(s0 + q, S - 1);
+    t[q] = partial[((size_t)s * M + m) * RPAD + j];
   }
+  int b, i;
+  if (!row_resolve(idx, n, B, L, m, n0, i0, b, i)) return;
+  const size_t row = (size_t)b * L + i;
   double v = 0.0;
 #pragma unroll
   for (int q = 0; q < PER; ++q)

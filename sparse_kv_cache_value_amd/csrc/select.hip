@@ -54,15 +54,15 @@ __device__ __forceinline__ uint64_t score_key(double s) {
 }
 
 // The selection of one sequence by a workgroup of NT threads.  s and fr are
-// the sequence's scores and forced flags (fr may be null); all_rows takes
-// every row.  Thread t owns rows [i0, i0 + E), E = ceil(L / NT) <= EM.  On
+// the sequence's scores and forced flags (fr may be null); a set *full_flag
+// (full_flag may be null) takes every row.  Thread t owns rows [i0, i0 + E), E = ceil(L / NT) <= EM.  On
 // return sel[e] marks its selected rows, pos is the compact position of its
 // first selected row and total the size of the set.  With m_exit >= 0 it
 // returns false (uniformly, before any radix pass) when the set has at most
 // m_exit rows.
 template <int NT, int EM>
 __device__ __forceinline__ bool select_rows(int L, int k, const double* __restrict__ s,
-                                            const uint8_t* __restrict__ fr, bool all_rows, int m_exit,
+                                            const uint8_t* __restrict__ fr, const uint8_t* __restrict__ full_flag, int m_exit,
                                             int* hist, int* wsum, int* pick, int& i0, bool (&sel)[EM],
                                             int& pos, int& total) {
   constexpr int NW = NT / 64;
@@ -73,14 +73,31 @@ __device__ __forceinline__ bool select_rows(int L, int k, const double* __restri
   uint64_t key[EM];
   int cls[EM];  // 0 = candidate, 1 = forced, 2 = past the end
   int nf = 0, nz = 0;
+  // every score and forced flag loaded unconditionally (index clamped), so
+  // the loads are issued together rather than one round trip each
+  // (without a forced list the flags are read from the scores' bytes, in
+  // bounds, and ignored)
+  const bool has_fr = fr != nullptr;
+  const uint8_t* frp = has_fr ? fr : reinterpret_cast<const uint8_t*>(s);
+  double sv[EM];
+  uint8_t fv[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    const int ii = min(i0 + e, L - 1);
+    sv[e] = s[ii];
+    fv[e] = frp[ii];
+  }
+  // the full-pass flag (null: none), read with the scores
+  const bool has_full = full_flag != nullptr;
+  const uint8_t fullv = (has_full ? full_flag : frp)[0];
 #pragma unroll
   for (int e = 0; e < EM; ++e) {
     const int i = i0 + e;
     key[e] = 0;
     cls[e] = 2;
     if (e < E && i < L) {
-      cls[e] = (fr && fr[i]) ? 1 : 0;
-      key[e] = score_key(s[i]);
+      cls[e] = (has_fr && fv[e]) ? 1 : 0;
+      key[e] = score_key(sv[e]);
       nf += cls[e] == 1;
       nz += cls[e] == 0 && key[e] != 0;
     }
@@ -90,6 +107,7 @@ __device__ __forceinline__ bool select_rows(int L, int k, const double* __restri
   int packed;
   (void)block_excl_scan<NW>(nf | (nz << 16), wsum, &packed);
   const int nF = packed & 0xFFFF, nnz = packed >> 16;
+  const bool all_rows = has_full && fullv != 0;
   const int keff = all_rows ? L : min(max(k, nF), L);
   if (m_exit >= 0 && m_exit >= keff) return false;  // the set is keff rows
   const int need = keff - nF;       // rows to take by score
@@ -212,7 +230,7 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(int L, int k, const doubl
   int i0, pos, total;
   bool sel[EM];
   (void)select_rows<SEL_T, EM>(L, k, score + (size_t)b * L, forced ? forced + (size_t)b * L : nullptr,
-                               full && full[b], -1, hist, wsum, pick, i0, sel, pos, total);
+                               full ? full + b : nullptr, -1, hist, wsum, pick, i0, sel, pos, total);
   int32_t* out = idx + (size_t)b * L;
 #pragma unroll
   for (int e = 0; e < EM; ++e)
@@ -240,7 +258,7 @@ __global__ __launch_bounds__(RT) void select_gather_kernel(int L, int d, float e
   const int m = blockIdx.x;
   int i0, pos, total;
   bool sel[EM];
-  if (!select_rows<RT, EM>(L, k, score, forced, full && full[0], m == 0 ? -1 : m, hist, wsum, pick, i0, sel, pos,
+  if (!select_rows<RT, EM>(L, k, score, forced, full, m == 0 ? -1 : m, hist, wsum, pick, i0, sel, pos,
                            total))
     return;
   int p = pos;
