@@ -485,10 +485,18 @@ __global__ __launch_bounds__(256) void ps_codes_kernel(int L, int d, int blk, in
   for (int g = threadIdx.x; g < d / 16; g += blockDim.x) {
     double r[16];
     double amax = 0.0;
+    // the row's and the centroid's values loaded unconditionally (issued
+    // together), then the unit row (zero for a zero row)
+    double xv[16], cv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const double xh = n > 0.0 ? (double)io<T>::ld(x + 16 * g + e) / n : 0.0;
-      r[e] = xh - c[16 * g + e];
+      xv[e] = (double)io<T>::ld(x + 16 * g + e);
+      cv[e] = c[16 * g + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const double xh = n > 0.0 ? xv[e] / n : 0.0;
+      r[e] = xh - cv[e];
       amax = fmax(amax, fabs(r[e]));
     }
     const int scode = e4m3_code(amax / 6.0);
@@ -592,13 +600,16 @@ __global__ __launch_bounds__(256) void ps_attn_kl_kernel(int L, int blk, int W, 
       ld8d(qrow + c, xa[u]);
       ld8d(kb + kc_off(ws + wc, slot * kq + c, dh), xb[u]);
     }
+    // chunks past kq are zeroed rather than skipped (a skip let the loads
+    // sink into per-chunk branches, each with its own wait); their products
+    // add exact zeros
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (u * 8 >= kq) break;
+      const bool live = u * 8 < kq;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (r >= K) xa[u][e] = 0.0;
-        if (w >= W) xb[u][e] = 0.0;
+        if (r >= K || !live) xa[u][e] = 0.0;
+        if (w >= W || !live) xb[u][e] = 0.0;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[u][e], xb[u][e], acc, 0, 0, 0);
