@@ -78,6 +78,13 @@ __global__ __launch_bounds__(64) void attn_ref_kernel(int B, int L, int Hq, int 
 constexpr int ATT_NW = 8;
 constexpr int ATT_ONE_ROUND = 256;  // (query tile, head) workgroups of 8 waves that fit one round (one per CU)
 constexpr int ATT_HALF_MAX_KEYS = 1024;  // longest cache the 4-wave variant takes
+// The running maximum of a query's scores (log2 units) moves only when a key
+// tile's maximum passes it by more than this.  Softmax is shift-invariant, so
+// any value at or below the true maximum gives the same result; a stale one
+// only lets the probabilities grow up to 2^ATT_M_SLACK (far inside bf16 and
+// fp32 range), and a tile that moves no lane's maximum skips the rescale of
+// the output accumulators, which is most of a tile's vector work.
+constexpr float ATT_M_SLACK = 8.0f;
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -225,8 +232,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_mfma_kernel(int
 #pragma unroll
     for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2e;
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_new = mt > m_run + ATT_M_SLACK ? mt : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where m_run stays
     // probabilities packed to bf16 as they are made (P^T operands of the two
     // 16-key halves); the row sum in element order
     u32x4 pf[2];
@@ -244,7 +251,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_mfma_kernel(int
     rs += __shfl_xor(rs, 32, 64);
     l_run = l_run * alpha + rs;
     m_run = m_new;
-    if (rescale) {  // o is still zero on a wave's first tile
+    // o is still zero on a wave's first tile; a multiply by 1 is skipped
+    if (rescale && __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -487,8 +495,8 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_gqa_kernel(int B, int L, int
 #pragma unroll
     for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2e;
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_new = mt > m_run + ATT_M_SLACK ? mt : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where m_run stays
     u32x4 pf[2];
     float rs = 0.f;
 #pragma unroll
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void attn_gqa_kernel(int B, int L, int
     rs += __shfl_xor(rs, 32, 64);
     l_run = l_run * alpha + rs;
     m_run = m_new;
-    if (kt > 0) {
+    if (kt > 0 && __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
