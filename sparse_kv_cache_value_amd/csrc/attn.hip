@@ -359,8 +359,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_mfma_kernel(int
 constexpr int GQ_TPB = 1;           // key tiles per barrier (2 measured no faster)
 constexpr int GQ_NB = 4 * GQ_TPB;  // ring slots (key tiles)
 
+// Four waves per SIMD (at most 128 VGPRs; a few dwords spill): two
+// workgroups share a CU, so more (query tile, KV head) pairs than CUs run in
+// one round instead of two.
 template <int DH>
-__global__ __launch_bounds__(ATT_NW * 64) void attn_gqa_kernel(int B, int L, int Hq, int Hkv, int ntq, float sl2e, int cap,
+__global__ __launch_bounds__(ATT_NW * 64, 4) void attn_gqa_kernel(int B, int L, int Hq, int Hkv, int ntq, float sl2e, int cap,
                                                                const int32_t* __restrict__ n,
                                                                const bf16* __restrict__ q,
                                                                const bf16* __restrict__ Kc,
