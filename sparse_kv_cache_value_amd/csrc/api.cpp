@@ -289,7 +289,7 @@ dllm_status gemm(dllm_model* m, hipStream_t st, int max_rows, int B, int K, int 
     while (sp > 1 && (size_t)sp * max_rows * N > out_floats) sp /= 2;
     if (!act && (size_t)sp * max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
     HIPCHK(launch_gemm_bf16(st, max_rows, B, K, N, (const uint16_t*)A, MTt, (const uint16_t*)W, n_sel, out, sp,
-                            (uint16_t*)act, m->MTt, prof.ev));
+                            (uint16_t*)act, m->MTt, gemm_bf16_pick_cols(max_rows, K, N, m->n_cu, sp), prof.ev));
     *splits = sp;
   } else {
     if ((size_t)max_rows * N > out_floats) return fail(DLLM_E_SHAPE, "GEMM partial buffer too small");
@@ -433,7 +433,8 @@ dllm_status do_lm_head(dllm_model* m, const dllm_state* s, hipStream_t st, int n
                                 (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0, prof.ev));
     else
       HIPCHK(launch_gemm_bf16(st, B * blk, 1, d.d_model, d.vocab, (const uint16_t*)m->A_lm, m->lm_MTt,
-                              (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0, prof.ev));
+                              (const uint16_t*)m->lm_head, m->lm_rows, m->logits, 1, nullptr, 0,
+                              gemm_bf16_pick_cols(B * blk, d.d_model, d.vocab, m->n_cu, 1), prof.ev));
     prof.done();
   } else {
     CHK(gemm(m, st, B * blk, 1, d.d_model, d.vocab, m->A_lm, m->lm_head, m->lm_rows, m->logits, cap, &sp,

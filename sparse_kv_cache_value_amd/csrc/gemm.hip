@@ -88,18 +88,21 @@ hipError_t launch_pack_f32(hipStream_t st, int K, int Nsrc, const float* src, in
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM.
 //
-// Workgroup = 4 waves, a 128-column slab (4 column tiles of 32) and a row
-// block of 4*MTW row tiles; wave w owns row tiles w, w+4, ... of the block and
-// all 4 column tiles, so each A fragment it loads (straight from the packed
-// activations, 16 B per lane) feeds 4 MFMAs.  The slab's weight fragments are
-// loaded once per workgroup (wave w loads column tile w) and shared through a
-// double-buffered LDS stage.  Both operands are prefetched two chunks ahead in
+// Workgroup = 4 waves, a slab of COLS column tiles of 32 (128 or 96 columns)
+// and a row block of 4*MTW row tiles; wave w owns row tiles w, w+4, ... of the
+// block and all the slab's column tiles, so each A fragment it loads (straight
+// from the packed activations, 16 B per lane) feeds COLS MFMAs.  The slab's
+// weight fragments are loaded once per workgroup (wave w loads column tile w;
+// with 3 columns wave 3 repeats wave 2's loads, which hit in L2, and its LDS
+// slot is not read) and shared through a double-buffered LDS stage.  96-column
+// slabs serve shapes whose 128-column workgroups leave much of the last round
+// of the chip empty.  Both operands are prefetched two chunks ahead in
 // registers, so the HBM weight stream overlaps the MFMAs of earlier chunks.
 // EPI 0 writes fp32 split-K partials out[split][m][n] ([S][cap][N]); EPI 1 (one split)
 // applies SwiGLU to the gate/up pairs inside each 32-column tile (16 gate then
 // 16 up columns) and writes the packed bf16 activation of the next GEMM.
 // ---------------------------------------------------------------------------
-template <int MTW, int KS, int EPI>
+template <int MTW, int KS, int EPI, int COLS>
 __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel(const u32x4* __restrict__ Ap, int MTt,
                                                            const u32x4* __restrict__ Wp, float* __restrict__ out,
                                                            uint16_t* __restrict__ act, int MTt_out,
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
   if (mt_base * 32 >= M) return;
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int NT = N >> 5;
-  const int nt0 = slab * 4;
+  const int nt0 = slab * COLS;
   const int KT = K >> 4;
   const int kt0 = (split * kps) >> 4;
   const int nchunks = kps / (16 * KS);
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
   // the prefetched chunks in flight: invalid tiles are clamped to a valid one
   // and the (at most three) chunks read past the end of a range land in the
   // padding that every weight and activation buffer carries.
-  const int ntw = min(nt0 + wv, NT - 1);
+  const int ntw = min(nt0 + min(wv, COLS - 1), NT - 1);
   const u32x4* wsrc = Wp + ((size_t)ntw * KT + kt0) * 64 + lane;
   const u32x4* asrc[MTW];
 #pragma unroll
@@ -139,11 +142,11 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
     asrc[j] = Ap + (size_t)kt0 * MTt * 64 + (size_t)min(mt_base + wv + 4 * j, m_tiles - 1) * 64 + lane;
   const size_t astep = (size_t)KS * MTt * 64;  // one chunk of A, in 16-byte units
 
-  f32x16_t acc[MTW][4];
+  f32x16_t acc[MTW][COLS];
 #pragma unroll
   for (int j = 0; j < MTW; ++j)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < COLS; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[j][nt][i] = 0.f;
 
@@ -169,11 +172,11 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
   // tile
   auto compute = [&](int buf, u32x4 (*a)[KS], auto nv) {
     // all B fragments of the chunk first, so one LDS latency covers them all
-    u32x4 b[KS][4];
+    u32x4 b[KS][COLS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) b[ks][nt] = wl[buf * WBUF + (ks * 4 + nt) * 64 + lane];
+      for (int nt = 0; nt < COLS; ++nt) b[ks][nt] = wl[buf * WBUF + (ks * 4 + nt) * 64 + lane];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
         }
         const bf16x8_t aa = __builtin_bit_cast(bf16x8_t, a[j][ks]);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < COLS; ++nt)
           acc[j][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, __builtin_bit_cast(bf16x8_t, b[ks][nt]),
                                                                acc[j][nt], 0, 0, 0);
       }
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
       if (!tv[j]) continue;
       const int mrow = (mt_base + wv + 4 * j) * 32 + (lane >> 5) * 4;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < COLS; ++nt) {
         if (nt0 + nt >= NT) continue;
         const int ncol = (nt0 + nt) * 32 + (lane & 31);
 #pragma unroll
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(256, (MTW * KS <= 4) ? 2 : 1) void gemm_bf16_kernel
       if (!tv[j]) continue;
       const int mrow = (mt_base + wv + 4 * j) * 32 + (lane >> 5) * 4;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < COLS; ++nt) {
         if (nt0 + nt >= NT) continue;
         const int f = (nt0 + nt) * 16 + (lane & 15);
 #pragma unroll
@@ -286,23 +289,23 @@ static int mtw_for_rows(int max_rows) {
 // waves per SIMD), else 4.
 static int ks_for(int mtw) { return mtw == 2 ? 2 : 4; }
 
-template <int MTW, int KS, int EPI>
+template <int MTW, int KS, int EPI, int COLS>
 static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, const void* Wp, float* out,
                              uint16_t* act, int MTt_out, const int32_t* n_sel, int B, int K, int N, int kps,
                              int row_blocks, int n_slabs, int total, int cap, LaunchEvents ev) {
   static std::atomic<unsigned long long> attr_set{0};
   const size_t lds = (size_t)2 * KS * 4 * 64 * 16;
   hipError_t ea = once_per_device(attr_set, [&] {
-    return hipFuncSetAttribute((const void*)gemm_bf16_kernel<MTW, KS, EPI>,
+    return hipFuncSetAttribute((const void*)gemm_bf16_kernel<MTW, KS, EPI, COLS>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   });
   if (ea != hipSuccess) return ea;
   if (ev.start)
-    hipExtLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI>), dim3(grid), dim3(256), lds, st, ev.start, ev.stop, 0,
-                          (const u32x4*)A, MTt, (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks,
-                          n_slabs, total, cap);
+    hipExtLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI, COLS>), dim3(grid), dim3(256), lds, st, ev.start, ev.stop,
+                          0, (const u32x4*)A, MTt, (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps,
+                          row_blocks, n_slabs, total, cap);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
+    hipLaunchKernelGGL((gemm_bf16_kernel<MTW, KS, EPI, COLS>), dim3(grid), dim3(256), lds, st, (const u32x4*)A, MTt,
                        (const u32x4*)Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, cap);
   return hipGetLastError();
 }
@@ -311,22 +314,42 @@ static hipError_t launch_cfg(hipStream_t st, int grid, const void* A, int MTt, c
 // end: the pipeline reads up to three 64-wide k chunks beyond a range.
 size_t gemm_pad_elems(int rows_tiles) { return (size_t)3 * 4 * (size_t)(rows_tiles > 0 ? rows_tiles : 1) * 512; }
 
-int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
+// Relative cost of a 96-column slab per unit of work (each activation
+// fragment feeds 3 MFMAs instead of 4), fitted to measurements: at 3 row
+// tiles per wave, 11 rounds of 96-column workgroups ran 5 % slower than 9
+// rounds of 128-column ones (2624 rows, 37888 columns), and one round of
+// 96-column workgroups (256 of them) 7 % faster than 192 128-column ones
+// (about 380 rows, 24576 and 12288 columns).  At 2 row tiles per wave two
+// workgroups share a CU and fill the idle SIMDs of a partial round by
+// themselves: there 96-column slabs were 9 % slower (1024 rows), so they
+// are not used.
+constexpr double BF16_COLS3_COST = 1.2;
+
+// Cost of a (column tiles per workgroup, K splits) choice: the weight stream
+// at the occupancy its rounds of workgroups achieve, plus the split partials'
+// round trip; infinite where the split does not divide K in whole chunk pairs.
+static double bf16_cost(int max_rows, int K, int N, int n_cu, int cols, int s) {
   const int mtw = mtw_for_rows(max_rows);
   const int ks = ks_for(mtw);
+  if (K % (s * 32 * ks) != 0) return 1e300;  // an even number of chunks per split
   const int row_blocks = (max_rows + 128 * mtw - 1) / (128 * mtw);
-  const int n_slabs = (N + 127) / 128;
+  const int n_slabs = ((N >> 5) + cols - 1) / cols;
   const int base = n_slabs * row_blocks;
+  const int slots = mtw * ks <= 4 ? 2 * n_cu : n_cu;  // workgroups resident at once (two when they fit)
+  const int rounds = (base * s + slots - 1) / slots;
+  const double eff = (double)base * s / ((double)rounds * slots);
   const double wbytes = (double)K * N * 2.0;
+  return wbytes / eff * (cols == 3 ? BF16_COLS3_COST : 1.0) +
+         (s > 1 ? 2.0 * 4.0 * s * (double)max_rows * N : 0.0);
+}
+
+int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
   double best = 1e300;
   int best_s = 1;
   for (int s = 1; s <= 32; s *= 2) {
-    if (K % (s * 32 * ks) != 0) break;  // an even number of chunks per split
-    const int slots = mtw * ks <= 4 ? 2 * n_cu : n_cu;  // workgroups resident at once (two when they fit)
-    const int waves = (base * s + slots - 1) / slots;
-    const double eff = (double)base * s / ((double)waves * slots);
-    // weight stream at the achieved occupancy + split partial round trip
-    const double cost = wbytes / eff + (s > 1 ? 2.0 * 4.0 * s * (double)max_rows * N : 0.0);
+    if (K % (s * 32 * ks_for(mtw_for_rows(max_rows))) != 0) break;
+    const double c3 = mtw_for_rows(max_rows) != 3 ? 1e300 : bf16_cost(max_rows, K, N, n_cu, 3, s);
+    const double cost = std::min(bf16_cost(max_rows, K, N, n_cu, 4, s), c3);
     if (cost < best * 0.999) {
       best = cost;
       best_s = s;
@@ -335,29 +358,37 @@ int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu) {
   return best_s;
 }
 
+int gemm_bf16_pick_cols(int max_rows, int K, int N, int n_cu, int splits) {
+  if (mtw_for_rows(max_rows) != 3) return 4;  // 96-column slabs pay off at 3 row tiles per wave only
+  return bf16_cost(max_rows, K, N, n_cu, 3, splits) < bf16_cost(max_rows, K, N, n_cu, 4, splits) ? 3 : 4;
+}
+
 hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                             const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
-                            int MTt_out, LaunchEvents ev) {
+                            int MTt_out, int cols, LaunchEvents ev) {
   if (max_rows <= 0) return hipSuccess;
+  if (cols != 3 && cols != 4) return hipErrorInvalidValue;
   const int mtw = mtw_for_rows(max_rows);
   const int ks = ks_for(mtw);
   const int row_blocks = (max_rows + 128 * mtw - 1) / (128 * mtw);
-  const int n_slabs = (N + 127) / 128;
+  const int n_slabs = ((N >> 5) + cols - 1) / cols;
   const int kps = K / splits;
   if (kps * splits != K || kps % (32 * ks) != 0) return hipErrorInvalidValue;
   if (act != nullptr && (splits != 1 || N % 64 != 0)) return hipErrorInvalidValue;
   const int total = n_slabs * row_blocks * splits;
   const int grid = (total + 7) / 8 * 8;
-#define GL(MTW, KS, EPI) \
-  launch_cfg<MTW, KS, EPI>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, total, max_rows, ev)
+#define GL(MTW, KS, EPI, C)                                                                                   \
+  launch_cfg<MTW, KS, EPI, C>(st, grid, A, MTt, Wp, out, act, MTt_out, n_sel, B, K, N, kps, row_blocks, n_slabs, \
+                              total, max_rows, ev)
+  if (cols == 3 && mtw != 3) return hipErrorInvalidValue;
   if (act == nullptr) {
-    if (mtw == 1) return GL(1, 4, 0);
-    if (mtw == 2) return GL(2, 2, 0);
-    return GL(3, 4, 0);
+    if (mtw == 1) return GL(1, 4, 0, 4);
+    if (mtw == 2) return GL(2, 2, 0, 4);
+    return cols == 3 ? GL(3, 4, 0, 3) : GL(3, 4, 0, 4);
   }
-  if (mtw == 1) return GL(1, 4, 1);
-  if (mtw == 2) return GL(2, 2, 1);
-  return GL(3, 4, 1);
+  if (mtw == 1) return GL(1, 4, 1, 4);
+  if (mtw == 2) return GL(2, 2, 1, 4);
+  return cols == 3 ? GL(3, 4, 1, 3) : GL(3, 4, 1, 4);
 #undef GL
 }
 

@@ -76,15 +76,17 @@ struct LaunchEvents {
 // out[s][m][n] = sum_{k in split s} A[m][k] W[k][n] for m < sum(n_sel).
 hipError_t launch_gemm_f32(hipStream_t st, int max_rows, int B, int K, int N, const float* A,
                            const float* W, const int32_t* n_sel, float* out, LaunchEvents ev = {});
-// bf16 weights pre-packed by launch_pack_bf16; `splits` from gemm_bf16_pick_splits.
+// bf16 weights pre-packed by launch_pack_bf16; `splits` from gemm_bf16_pick_splits,
+// `cols` (column tiles per workgroup: 4, or 3 at 384-row blocks) from gemm_bf16_pick_cols.
 // A is packed (apack_off) with MTt row tiles.  act != NULL (one split, N a
 // multiple of 64, each 32-column tile holding 16 gate then the matching 16 up
 // columns) writes SwiGLU(gate, up) as a packed bf16 [M][N/2] activation with
 // MTt_out row tiles instead of out.
 hipError_t launch_gemm_bf16(hipStream_t st, int max_rows, int B, int K, int N, const uint16_t* A, int MTt,
                             const uint16_t* Wp, const int32_t* n_sel, float* out, int splits, uint16_t* act,
-                            int MTt_out, LaunchEvents ev = {});
+                            int MTt_out, int cols, LaunchEvents ev = {});
 int gemm_bf16_pick_splits(int max_rows, int K, int N, int n_cu);
+int gemm_bf16_pick_cols(int max_rows, int K, int N, int n_cu, int splits);
 // Streaming variant for up to 288 rows (N % 128 == 0, K % 256 == 0); `splits`
 // from gemm_stream_pick_splits (0 there = use launch_gemm_bf16).
 int gemm_stream_pick_splits(int max_rows, int K, int N, int n_cu, bool fused, int MTt);
