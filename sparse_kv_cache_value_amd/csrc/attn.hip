@@ -359,7 +359,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_mfma_kernel(int
 constexpr int GQ_TPB = 1;           // key tiles per barrier (2 measured no faster)
 constexpr int GQ_NB = 4 * GQ_TPB;  // ring slots (key tiles)
 
-// Four waves per SIMD (at most 128 VGPRs; a few dwords spill): two
+// Four waves per SIMD (at most 128 VGPRs; 10 spill, 28 bytes of scratch): two
 // workgroups share a CU, so more (query tile, KV head) pairs than CUs run in
 // one round instead of two.
 template <int DH>
