@@ -29,7 +29,7 @@ CASES = [(1, 0, 0), (17, 16, 0), (50, 40, 0), (40, 57, 5), (70, 65, 0), (100, 91
          (128, 128, 0), (140, 131, 0), (150, 133, 9), (190, 162, 0), (200, 184, 0), (240, 145, 0), (256, 256, 0)]
 
 
-def _run_cases(cfg, cases):
+def _run_cases(cfg, cases, prep=None):
     torch.manual_seed(0)
     spec = spec_of(cfg)
     tol = TOL[cfg.dtype]
@@ -37,6 +37,8 @@ def _run_cases(cfg, cases):
     st = runtime.State(cfg)
     Bn, L = cfg.batch, cfg.seq_len
     runtime.step(model, st, mode=B.DLLM_MODE_FULL)
+    if prep is not None:
+        prep(st)
     rng = np.random.default_rng(7)
     dev = "cuda"
     for case in cases:
@@ -80,6 +82,29 @@ def test_attention_long_cache(heads, dh):
     cfg = medium_cfg(name=f"split-h{heads}-d{dh}", n_layers=1, batch=1, seq_len=1024, prompt_len=512,
                      n_q_heads=heads, n_kv_heads=heads // 2, head_dim=dh, seed=33, n_steps=1)
     _run_cases(cfg, [(1, 0), (37, 3), (200, 0), (700, 0), (1024, 0)])
+
+
+def _scale_key_tiles(st):
+    """Layer-0 keys of 32-key tile t scaled by 2^(t % 3), tile 5 by 2^3 more
+    (powers of two: exact in bf16).  Each query's score maximum then grows by
+    far more than 8 (log2 units) inside a wave's key range and stays put over
+    other tiles, so the attention kernels' running-maximum update, their
+    output rescale and its skip all run on sharply peaked softmaxes."""
+    k = st.k_cache[0]  # [B][G][T][KS][64][8], fragment order
+    T = k.shape[2]
+    f = torch.tensor([2.0 ** (t % 3) for t in range(T)], dtype=torch.float32)
+    f[min(5, T - 1)] *= 8.0
+    k.mul_(f.view(1, 1, T, 1, 1, 1).to(device=k.device, dtype=k.dtype))
+
+
+@pytest.mark.parametrize("heads,kv,dh", [(4, 2, 128), (8, 4, 64), (8, 2, 64)])
+def test_attention_score_range(heads, kv, dh):
+    """L = 1024 keys whose tiles are scaled 1x to 32x: the multi-head kernel
+    (2 query heads per KV head) and the grouped-query kernel (4 per KV head)
+    against the oracle's sparse layer on the same scaled cache."""
+    cfg = medium_cfg(name=f"range-h{heads}-kv{kv}-d{dh}", n_layers=1, batch=1, seq_len=1024, prompt_len=512,
+                     n_q_heads=heads, n_kv_heads=kv, head_dim=dh, seed=39, n_steps=1)
+    _run_cases(cfg, [(37, 0), (200, 0), (700, 0)], prep=_scale_key_tiles)
 
 
 def test_wide_layer_shapes():
