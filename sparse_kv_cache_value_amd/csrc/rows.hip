@@ -156,10 +156,79 @@ __global__ __launch_bounds__(RT) void gather_norm_kernel(int B, int L, int d, fl
   norm_row_store<T>(H + ((size_t)b * L + i) * d, d, eps, g, A, m, MTt, red);
 }
 
+// The same rows, one per wave (8 rows per workgroup), for launches of many
+// rows: no workgroup barrier and an eighth of the workgroups.  Each lane
+// stands in for the 8 threads l + 64 w of gather_norm_kernel's workgroup
+// and keeps their partial sums apart, so that the sum of squares is added
+// in the same order (each virtual wave's shuffle tree, then the 8 wave
+// totals in wave order) and the result is bit-identical.
+constexpr int GN_ROWS = 8;             // rows (waves) per workgroup
+constexpr int GN_WAVE_MIN_ROWS = 1024;  // launches from this many rows use it
+
+template <typename T>
+__global__ __launch_bounds__(GN_ROWS * 64) void gather_norm_rows_kernel(int B, int L, int d, float eps, int MTt,
+                                                                       const int32_t* __restrict__ idx,
+                                                                       const int32_t* __restrict__ n,
+                                                                       const T* __restrict__ H,
+                                                                       const float* __restrict__ g,
+                                                                       T* __restrict__ A) {
+  constexpr int VW = RT / 64;  // virtual waves of gather_norm_kernel's workgroup
+  const int lane = threadIdx.x & 63;
+  const int m = __builtin_amdgcn_readfirstlane(blockIdx.x * GN_ROWS + (threadIdx.x >> 6));
+  int b, i;
+  if (!row_of(idx, n, B, L, m, b, i)) return;
+  const T* x = H + ((size_t)b * L + i) * d;
+  float v[VW][RV][8];
+  float part[VW];
+#pragma unroll
+  for (int w = 0; w < VW; ++w) {
+    part[w] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const int c8 = (lane + 64 * w + r * RT) * 8;
+      if (c8 < d) {
+        load8<T>(x + c8, v[w][r]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[w] += v[w][r][e] * v[w][r][e];
+      }
+    }
+  }
+  // virtual wave w's total as its lane 0 would have it, then the totals in order
+  float ss = 0.f;
+#pragma unroll
+  for (int w = 0; w < VW; ++w) {
+    const float t = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wave_sum(part[w]))));
+    ss = w == 0 ? t : ss + t;
+  }
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int w = 0; w < VW; ++w)
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const int c8 = (lane + 64 * w + r * RT) * 8;
+      if (c8 < d) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = v[w][r][e] * inv * g[c8 + e];
+        store_a8(A, m, c8, MTt, d, o);
+      }
+    }
+}
+
 hipError_t launch_gather_norm(hipStream_t st, bool bf16m, int max_rows, int B, int L, int d, float eps, int MTt,
                               const int32_t* idx, const int32_t* n, const void* H, const float* g,
                               void* A) {
   if (max_rows <= 0) return hipSuccess;
+  if (max_rows >= GN_WAVE_MIN_ROWS) {
+    const dim3 grid((max_rows + GN_ROWS - 1) / GN_ROWS);
+    if (bf16m)
+      hipLaunchKernelGGL(gather_norm_rows_kernel<bf16>, grid, dim3(GN_ROWS * 64), 0, st, B, L, d, eps, MTt, idx, n,
+                         (const bf16*)H, g, (bf16*)A);
+    else
+      hipLaunchKernelGGL(gather_norm_rows_kernel<float>, grid, dim3(GN_ROWS * 64), 0, st, B, L, d, eps, MTt, idx, n,
+                         (const float*)H, g, (float*)A);
+    return hipGetLastError();
+  }
   if (bf16m)
     hipLaunchKernelGGL(gather_norm_kernel<bf16>, dim3(max_rows), dim3(RT), 0, st, B, L, d, eps, MTt, idx, n,
                        (const bf16*)H, g, (bf16*)A);
