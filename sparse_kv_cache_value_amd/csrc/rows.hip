@@ -156,16 +156,16 @@ __global__ __launch_bounds__(RT) void gather_norm_kernel(int B, int L, int d, fl
   norm_row_store<T>(H + ((size_t)b * L + i) * d, d, eps, g, A, m, MTt, red);
 }
 
-// The same rows, one per wave (8 rows per workgroup), for launches of many
+// The same rows, one per wave (4 rows per workgroup), for launches of many
 // rows: no workgroup barrier and an eighth of the workgroups.  Each lane
 // stands in for the 8 threads l + 64 w of gather_norm_kernel's workgroup
 // and keeps their partial sums apart, so that the sum of squares is added
 // in the same order (each virtual wave's shuffle tree, then the 8 wave
 // totals in wave order) and the result is bit-identical.
-constexpr int GN_ROWS = 8;             // rows (waves) per workgroup
+constexpr int GN_ROWS = 4;             // rows (waves) per workgroup
 constexpr int GN_WAVE_MIN_ROWS = 1024;  // launches from this many rows use it
 
-template <typename T>
+template <typename T, int RVN>  // RVN: the groups of 8 per virtual thread that d needs (1 up to d = RT * 8)
 __global__ __launch_bounds__(GN_ROWS * 64) void gather_norm_rows_kernel(int B, int L, int d, float eps, int MTt,
                                                                        const int32_t* __restrict__ idx,
                                                                        const int32_t* __restrict__ n,
@@ -178,13 +178,13 @@ __global__ __launch_bounds__(GN_ROWS * 64) void gather_norm_rows_kernel(int B, i
   int b, i;
   if (!row_of(idx, n, B, L, m, b, i)) return;
   const T* x = H + ((size_t)b * L + i) * d;
-  float v[VW][RV][8];
+  float v[VW][RVN][8];
   float part[VW];
 #pragma unroll
   for (int w = 0; w < VW; ++w) {
     part[w] = 0.f;
 #pragma unroll
-    for (int r = 0; r < RV; ++r) {
+    for (int r = 0; r < RVN; ++r) {
       const int c8 = (lane + 64 * w + r * RT) * 8;
       if (c8 < d) {
         load8<T>(x + c8, v[w][r]);
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(GN_ROWS * 64) void gather_norm_rows_kernel(int B, i
 #pragma unroll
   for (int w = 0; w < VW; ++w)
 #pragma unroll
-    for (int r = 0; r < RV; ++r) {
+    for (int r = 0; r < RVN; ++r) {
       const int c8 = (lane + 64 * w + r * RT) * 8;
       if (c8 < d) {
         float o[8];
@@ -221,12 +221,15 @@ hipError_t launch_gather_norm(hipStream_t st, bool bf16m, int max_rows, int B, i
   if (max_rows <= 0) return hipSuccess;
   if (max_rows >= GN_WAVE_MIN_ROWS) {
     const dim3 grid((max_rows + GN_ROWS - 1) / GN_ROWS);
-    if (bf16m)
-      hipLaunchKernelGGL(gather_norm_rows_kernel<bf16>, grid, dim3(GN_ROWS * 64), 0, st, B, L, d, eps, MTt, idx, n,
-                         (const bf16*)H, g, (bf16*)A);
-    else
-      hipLaunchKernelGGL(gather_norm_rows_kernel<float>, grid, dim3(GN_ROWS * 64), 0, st, B, L, d, eps, MTt, idx, n,
-                         (const float*)H, g, (float*)A);
+#define GNR(TT, RR)                                                                                        \
+  hipLaunchKernelGGL((gather_norm_rows_kernel<TT, RR>), grid, dim3(GN_ROWS * 64), 0, st, B, L, d, eps, MTt, idx, n, \
+                     (const TT*)H, g, (TT*)A)
+    if (bf16m) {
+      if (d <= RT * 8) GNR(bf16, 1); else GNR(bf16, RV);
+    } else {
+      if (d <= RT * 8) GNR(float, 1); else GNR(float, RV);
+    }
+#undef GNR
     return hipGetLastError();
   }
   if (bf16m)
