@@ -430,10 +430,97 @@ __global__ __launch_bounds__(RT) void o_epilogue_kernel(int B, int L, int d, int
   }
 }
 
+// The same rows, one per wave (GN_ROWS per workgroup), for launches of many
+// rows and a split count fixed at compile time: each lane stands in for the
+// 8 threads l + 64 w of o_epilogue_kernel's workgroup, so every value and the
+// order of the sum of squares are the same and the outputs bit-identical.
+template <typename T, int S, int RVN>
+__global__ __launch_bounds__(GN_ROWS * 64) void o_epilogue_rows_kernel(int B, int L, int d, int cap, float eps,
+                                                                      int MTt, const int32_t* __restrict__ idx,
+                                                                      const int32_t* __restrict__ n,
+                                                                      const float* __restrict__ part,
+                                                                      const T* __restrict__ H,
+                                                                      const float* __restrict__ g2,
+                                                                      float* __restrict__ hprime,
+                                                                      T* __restrict__ A2) {
+  constexpr int VW = RT / 64;
+  const int lane = threadIdx.x & 63;
+  const int m = __builtin_amdgcn_readfirstlane(blockIdx.x * GN_ROWS + (threadIdx.x >> 6));
+  if (m >= cap) return;
+  const int n0 = n[0];
+  const int i0 = idx[m < L ? m : L - 1];
+  const size_t sstride = (size_t)cap * d;
+  const float* p0 = part + (size_t)m * d;
+  // the partials, before the row's position is known (clamped, unconditional)
+  float4 t[VW][RVN][2][S];
+#pragma unroll
+  for (int w = 0; w < VW; ++w)
+#pragma unroll
+    for (int r = 0; r < RVN; ++r) {
+      const int c8 = (lane + 64 * w + r * RT) * 8;
+      const int cc = c8 < d ? c8 : 0;
+      load_splits4<S>(p0 + cc, sstride, t[w][r][0]);
+      load_splits4<S>(p0 + cc + 4, sstride, t[w][r][1]);
+    }
+  int b, i;
+  if (!row_resolve(idx, n, B, L, m, n0, i0, b, i)) return;
+  const T* x = H + ((size_t)b * L + i) * d;
+  float* hp = hprime + (size_t)m * d;
+  float v[VW][RVN][8];
+  float pt[VW];
+#pragma unroll
+  for (int w = 0; w < VW; ++w) {
+    pt[w] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RVN; ++r) {
+      const int c8 = (lane + 64 * w + r * RT) * 8;
+      if (c8 < d) {
+        load8<T>(x + c8, v[w][r]);
+        const float4 a = add_splits4<S>(t[w][r][0]), c = add_splits4<S>(t[w][r][1]);
+        v[w][r][0] += a.x; v[w][r][1] += a.y; v[w][r][2] += a.z; v[w][r][3] += a.w;
+        v[w][r][4] += c.x; v[w][r][5] += c.y; v[w][r][6] += c.z; v[w][r][7] += c.w;
+        *reinterpret_cast<float4*>(hp + c8) = make_float4(v[w][r][0], v[w][r][1], v[w][r][2], v[w][r][3]);
+        *reinterpret_cast<float4*>(hp + c8 + 4) = make_float4(v[w][r][4], v[w][r][5], v[w][r][6], v[w][r][7]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pt[w] += v[w][r][e] * v[w][r][e];
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int w = 0; w < VW; ++w) {
+    const float tw = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wave_sum(pt[w]))));
+    ss = w == 0 ? tw : ss + tw;
+  }
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int w = 0; w < VW; ++w)
+#pragma unroll
+    for (int r = 0; r < RVN; ++r) {
+      const int c8 = (lane + 64 * w + r * RT) * 8;
+      if (c8 < d) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = v[w][r][e] * inv * g2[c8 + e];
+        store_a8(A2, m, c8, MTt, d, o);
+      }
+    }
+}
+
 template <typename T>
 static hipError_t o_epi_cfg(hipStream_t st, int max_rows, int B, int L, int d, int S, float eps, int MTt,
                             const int32_t* idx, const int32_t* n, const float* part, const T* H, const float* g2,
                             float* hprime, T* A2) {
+  // (one or two splits: with four the partials alone take 128 registers)
+  if (max_rows >= GN_WAVE_MIN_ROWS && d <= RT * 8 && (S == 1 || S == 2)) {
+    const dim3 grid((max_rows + GN_ROWS - 1) / GN_ROWS);
+#define OR(SS)                                                                                                   \
+  hipLaunchKernelGGL((o_epilogue_rows_kernel<T, SS, 1>), grid, dim3(GN_ROWS * 64), 0, st, B, L, d, max_rows, eps, MTt, \
+                     idx, n, part, H, g2, hprime, A2)
+    if (S == 1) OR(1); else OR(2);
+#undef OR
+    return hipGetLastError();
+  }
 #define OE(SS) hipLaunchKernelGGL((o_epilogue_kernel<T, SS>), dim3(max_rows), dim3(RT), 0, st, B, L, d, S, max_rows, \
                                   eps, MTt, idx, n, part, H, g2, hprime, A2)
   switch (S) {
